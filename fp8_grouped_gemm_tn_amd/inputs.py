@@ -1,0 +1,249 @@
+"""Seeded synthetic inputs for the K-grouped weight-gradient GEMM.
+
+This module makes inputs only: per-expert token counts (routing), fp32 values,
+and their quantisation to fp8 e4m3fn with per-(block, channel) scales or to
+bf16. It contains none of the GEMM's arithmetic, and both the GPU path's tests
+and the CPU oracle's tests draw their inputs from it.
+
+Workloads (named by what they are):
+  worked       - the how-to page's worked shape: ks = [32, 45, 27], M = 64, N = 128,
+                 fp8 with fp32 scales per 128 tokens, no C.
+  bf16         - G = 4, M = 1024, N = 2048, 16384 tokens routed uniformly over three
+                 experts (the second expert gets none), bf16 N(0,1)*0.1, C ~ N(0,1).
+  zipf_fp8     - G = 32, M = 7168, N = 4096, 65536 tokens with Zipf(1.2) routing, A
+                 N(0,1) with 1% of entries x50, B N(0,1)*1e-3, fp8 + fp32 scales per
+                 128 tokens, C ~ N(0,1).
+  ue8m0_many   - G = 256, M = 2048, N = 7168, 16384 tokens each routed to 8 distinct
+                 experts among 205 active ones (51 experts empty), A, B ~ N(0,1), fp8 +
+                 power-of-two scales per 32 tokens, no C.
+  local_share  - G = 8, M = 7168, N = 4096, 262144 tokens with per-expert counts drawn
+                 from N(32768, 8192), clipped at 0 and rescaled, values as zipf_fp8.
+
+Quantiser (input preparation, not part of the measured path): for each run of
+gran_k tokens of one expert (runs restart at each expert's first token) and each
+channel, amax = max |x|; fp32 scale = amax / 448 (1 if amax == 0) and
+q = e4m3fn(RNE(clamp(x / scale, +-448))); power-of-two scales use
+e = ceil(log2(amax / 448)) + 127 clamped to [0, 254] (127 if amax == 0), scale
+2^(e-127).
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+E4M3_F32SCALE, E4M3_UE8M0, BF16 = 0, 1, 2
+DTYPE_NAMES = {E4M3_F32SCALE: "e4m3+f32scale", E4M3_UE8M0: "e4m3+ue8m0", BF16: "bf16"}
+FP8_MAX = 448.0
+
+
+@dataclass
+class Case:
+    name: str
+    G: int
+    M: int
+    N: int
+    ks: np.ndarray          # int32 [G]
+    dtype: int
+    gran_k: int
+    A: torch.Tensor         # uint8 [K_total, M] (fp8 bytes) or bfloat16 [K_total, M]
+    B: torch.Tensor         # uint8 [K_total, N] or bfloat16 [K_total, N]
+    sa: Optional[torch.Tensor]  # float32 or uint8 [nblocks, M]; None for bf16
+    sb: Optional[torch.Tensor]  # float32 or uint8 [nblocks, N]; None for bf16
+    C: Optional[torch.Tensor]   # float32 [G, M, N] or None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def K_total(self) -> int:
+        return int(self.ks.astype(np.int64).sum())
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.K_total * self.M * self.N
+
+    def host(self):
+        """numpy copies in the layouts the oracle reads (fp8 / bf16 as raw bits)."""
+        def bits(t):
+            if t is None:
+                return None
+            t = t.detach().cpu()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16)
+            return t.numpy()
+        return dict(A=bits(self.A), B=bits(self.B), sa=bits(self.sa), sb=bits(self.sb),
+                    C=bits(self.C), ks=self.ks.copy())
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the method must move once: A, B, scales, C (if given) and D."""
+        elt = 2 if self.dtype == BF16 else 1
+        nbytes = self.K_total * (self.M + self.N) * elt
+        if self.sa is not None:
+            nbytes += self.sa.numel() * self.sa.element_size()
+            nbytes += self.sb.numel() * self.sb.element_size()
+        out = self.G * self.M * self.N * 4
+        nbytes += out + (out if self.C is not None else 0)
+        return nbytes
+
+
+# ----------------------------------------------------------------- routing
+
+def ks_worked():
+    return np.array([32, 45, 27], np.int32)
+
+
+def ks_uniform_with_empty(total, G, empty, seed):
+    rng = np.random.default_rng(seed)
+    live = [g for g in range(G) if g not in set(empty)]
+    counts = rng.multinomial(total, [1.0 / len(live)] * len(live))
+    ks = np.zeros(G, np.int64)
+    ks[live] = counts
+    return ks.astype(np.int32)
+
+
+def ks_zipf(total, G, s, seed):
+    rng = np.random.default_rng(seed)
+    ranks = rng.permutation(G) + 1
+    p = ranks.astype(np.float64) ** (-s)
+    p /= p.sum()
+    return rng.multinomial(total, p).astype(np.int32)
+
+
+def ks_topk(tokens, G, topk, n_empty, seed):
+    rng = np.random.default_rng(seed)
+    empty = rng.choice(G, n_empty, replace=False)
+    active = np.setdiff1d(np.arange(G), empty)
+    picks = np.argsort(rng.random((tokens, active.size)), axis=1)[:, :topk]
+    counts = np.bincount(picks.ravel(), minlength=active.size)
+    ks = np.zeros(G, np.int64)
+    ks[active] = counts
+    return ks.astype(np.int32)
+
+
+def ks_normal(total, G, mean, std, seed):
+    rng = np.random.default_rng(seed)
+    x = np.clip(rng.normal(mean, std, G), 0.0, None)
+    if x.sum() == 0:
+        x[:] = 1.0
+    x = x * (total / x.sum())
+    base = np.floor(x).astype(np.int64)
+    rem = total - int(base.sum())
+    order = np.argsort(-(x - base), kind="stable")
+    base[order[:rem]] += 1
+    return base.astype(np.int32)
+
+
+# ----------------------------------------------------------------- quantiser
+
+def _block_rows(ks, gran):
+    return int(sum((int(k) + gran - 1) // gran for k in ks))
+
+
+def quantize_fp8(x: torch.Tensor, ks, gran: int, pow2: bool):
+    """x fp32 [K_total, W] -> (uint8 [K_total, W], scales [nblocks, W])."""
+    K_total, W = x.shape
+    q = torch.empty((K_total, W), dtype=torch.uint8, device=x.device)
+    nb = _block_rows(ks, gran)
+    s = torch.empty((nb, W), dtype=torch.uint8 if pow2 else torch.float32, device=x.device)
+    t0 = 0
+    r0 = 0
+    for k in ks:
+        k = int(k)
+        if k == 0:
+            continue
+        nbk = (k + gran - 1) // gran
+        xg = x[t0:t0 + k]
+        pad = nbk * gran - k
+        if pad:
+            xg = torch.cat([xg, torch.zeros((pad, W), dtype=x.dtype, device=x.device)])
+        xb = xg.view(nbk, gran, W)
+        amax = xb.abs().amax(dim=1)                      # [nbk, W]
+        if pow2:
+            v = amax / FP8_MAX
+            mant, ex = torch.frexp(v)                    # v = mant * 2^ex, mant in [0.5, 1)
+            e = torch.where(mant == 0.5, ex - 1, ex)     # ceil(log2 v)
+            e = torch.clamp(e + 127, 0, 254)
+            e = torch.where(amax == 0, torch.full_like(e, 127), e)
+            scale = torch.ldexp(torch.ones_like(amax), (e - 127).to(torch.int32))
+            s[r0:r0 + nbk] = e.to(torch.uint8)
+        else:
+            scale = torch.where(amax == 0, torch.ones_like(amax), amax / FP8_MAX)
+            s[r0:r0 + nbk] = scale
+        y = torch.clamp(xb / scale[:, None, :], -FP8_MAX, FP8_MAX)
+        y = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(nbk * gran, W)
+        q[t0:t0 + k] = y[:k]
+        t0 += k
+        r0 += nbk
+    return q, s
+
+
+# ----------------------------------------------------------------- cases
+
+def _normal(gen, shape, device, std=1.0):
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std
+
+
+def make_case(name, ks, M, N, dtype, gran_k=128, with_c=True, seed=0, device="cpu",
+              a_std=1.0, b_std=1.0, a_outlier_p=0.0, a_outlier_mul=50.0, scale_values=None):
+    """Seeded inputs of one problem. Draw order: A, outlier mask, B, C."""
+    ks = np.asarray(ks, dtype=np.int32)
+    G = ks.size
+    K_total = int(ks.astype(np.int64).sum())
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    a = _normal(gen, (K_total, M), dev, a_std)
+    if a_outlier_p > 0:
+        mask = torch.rand((K_total, M), generator=gen, device=dev) < a_outlier_p
+        a = torch.where(mask, a * a_outlier_mul, a)
+        del mask
+    b = _normal(gen, (K_total, N), dev, b_std)
+    C = _normal(gen, (G, M, N), dev) if with_c else None
+    if dtype == BF16:
+        A, B, sa, sb = a.to(torch.bfloat16), b.to(torch.bfloat16), None, None
+    else:
+        pow2 = dtype == E4M3_UE8M0
+        A, sa = quantize_fp8(a, ks, gran_k, pow2)
+        del a
+        B, sb = quantize_fp8(b, ks, gran_k, pow2)
+        del b
+    return Case(name=name, G=G, M=M, N=N, ks=ks, dtype=dtype, gran_k=gran_k,
+                A=A.contiguous(), B=B.contiguous(), sa=sa, sb=sb, C=C,
+                meta=dict(seed=seed, device=str(dev)))
+
+
+WORKLOADS = ("worked", "bf16", "zipf_fp8", "ue8m0_many", "local_share")
+
+
+def workload(name, device="cpu", seed=0):
+    """The five named workloads (see the module docstring)."""
+    if name == "worked":
+        return make_case(name, ks_worked(), 64, 128, E4M3_F32SCALE, 128, with_c=False,
+                         seed=seed, device=device)
+    if name == "bf16":
+        ks = ks_uniform_with_empty(16384, 4, [1], seed)
+        return make_case(name, ks, 1024, 2048, BF16, 128, with_c=True, seed=seed,
+                         device=device, a_std=0.1, b_std=0.1)
+    if name == "zipf_fp8":
+        ks = ks_zipf(65536, 32, 1.2, seed)
+        return make_case(name, ks, 7168, 4096, E4M3_F32SCALE, 128, with_c=True, seed=seed,
+                         device=device, b_std=1e-3, a_outlier_p=0.01)
+    if name == "ue8m0_many":
+        ks = ks_topk(16384, 256, 8, 51, seed)
+        return make_case(name, ks, 2048, 7168, E4M3_UE8M0, 32, with_c=False, seed=seed,
+                         device=device)
+    if name == "local_share":
+        ks = ks_normal(262144, 8, 32768.0, 8192.0, seed)
+        return make_case(name, ks, 7168, 4096, E4M3_F32SCALE, 128, with_c=True, seed=seed,
+                         device=device, b_std=1e-3, a_outlier_p=0.01)
+    raise KeyError(name)
+
+
+def workload_ks(name, seed=0):
+    """Routing of a named workload without generating its values."""
+    return {
+        "worked": lambda: ks_worked(),
+        "bf16": lambda: ks_uniform_with_empty(16384, 4, [1], seed),
+        "zipf_fp8": lambda: ks_zipf(65536, 32, 1.2, seed),
+        "ue8m0_many": lambda: ks_topk(16384, 256, 8, 51, seed),
+        "local_share": lambda: ks_normal(262144, 8, 32768.0, 8192.0, seed),
+    }[name]()

@@ -1,0 +1,380 @@
+/*
+ * kgref.c -- CPU oracle for the K-grouped weight-gradient GEMM.
+ *
+ * TEST INFRASTRUCTURE, not the product: only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load this library. It shares no code with
+ * the GPU library. Plain C11 + pthreads, fp64 throughout.
+ *
+ * Method (the pages' wording restated):
+ *  - Page "How to Use DeepGEMM Weight Gradient Kernels for Training Backward
+ *    Passes", "Understanding K-Grouped Weight Gradient Kernels": every expert keeps
+ *    the two output dimensions fixed and owns a variable number of tokens; the
+ *    tokens of expert g are a contiguous slice of A [sum K, M] and B [sum K, N]
+ *    ("FP8 Implementation Example"). The weight gradient of expert g is the
+ *    contraction of its two slices over the token axis.
+ *  - GitHub issue "Is DeepGEMM directly applicable to backward in training?",
+ *    comments by qijiaxing (2025-03-26, 2025-05-12) and hxdtest (2025-05-09): the
+ *    token axis is the accumulation axis; each run of gran_k tokens shares one scale
+ *    per channel, and the scale is applied to the block's partial sum after that
+ *    block has been accumulated.
+ *  - Same how-to page, "Dispatch and Tensor-Map Handling": the group sizes must add
+ *    up to the rows of A and B; zero-size groups are skipped. The recipe text under
+ *    the FP8 example restricts gran_k to 32 or 128.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - Scale blocks restart at each group start; group g's blocks occupy scale rows
+ *    [boff[g], boff[g+1]) with boff[g+1] = boff[g] + ceil(K_g / gran_k). The last
+ *    block of a group may be partial and uses its own scale row.
+ *  - sa is [nblocks][M], sb is [nblocks][N], row-major.
+ *  - The output is fp32 [G][M][N] on the GPU; here it is fp64. An empty group
+ *    yields C[g] unchanged, or +0.0 without C.
+ *
+ * Exactness: every e4m3fn value is an integer multiple of 2^-9 below 2^9 in
+ * magnitude, so each product is a multiple of 2^-18 below 2^18 and a sum of at
+ * most 128 of them is below 2^25 with 2^-18 resolution: 43 bits, exact in fp64.
+ * The block partial is therefore exact; the only roundings are the multiply by the
+ * scale product and the fp64 accumulation over blocks.
+ */
+#include "kgref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdatomic.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---------------------------------------------------------------- decoders */
+
+static double g_e4m3[256];
+static pthread_once_t g_once = PTHREAD_ONCE_INIT;
+
+/* OCP e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0
+ * is subnormal (m/8 * 2^-6); no infinities; 0x7F and 0xFF are NaN; max 448. */
+static void build_tables(void) {
+  for (int x = 0; x < 256; ++x) {
+    int s = (x >> 7) & 1, e = (x >> 3) & 15, m = x & 7;
+    double mag;
+    if (e == 15 && m == 7)
+      mag = NAN;
+    else if (e == 0)
+      mag = ldexp((double)m, -9); /* (m/8) * 2^-6 */
+    else
+      mag = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    g_e4m3[x] = s ? -mag : mag;
+  }
+}
+
+double kgref_e4m3(uint8_t byte) {
+  pthread_once(&g_once, build_tables);
+  return g_e4m3[byte];
+}
+
+/* UE8M0: an unsigned biased exponent, value 2^(e-127); 255 is NaN. */
+double kgref_e8m0(uint8_t byte) { return byte == 255 ? NAN : ldexp(1.0, (int)byte - 127); }
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double kgref_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* ---------------------------------------------------------------- checks */
+
+int kgref_validate(const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k, int dtype) {
+  if (G < 0 || M < 0 || N < 0 || K_total < 0) return KGREF_ERR_SHAPE;
+  if (dtype != KGREF_E4M3_F32SCALE && dtype != KGREF_E4M3_UE8M0 && dtype != KGREF_BF16)
+    return KGREF_ERR_DTYPE;
+  if (dtype != KGREF_BF16 && gran_k != 32 && gran_k != 128) return KGREF_ERR_GRAN;
+  if (G > 0 && ks == NULL) return KGREF_ERR_NULL;
+  int64_t sum = 0;
+  for (int g = 0; g < G; ++g) {
+    if (ks[g] < 0) return KGREF_ERR_KSUM;
+    sum += ks[g];
+  }
+  if (sum != K_total) return KGREF_ERR_KSUM;
+  return KGREF_OK;
+}
+
+int kgref_offsets(const int32_t* ks, int G, int gran_k, int64_t* off, int32_t* boff) {
+  if (G < 0 || gran_k <= 0) return KGREF_ERR_SHAPE;
+  off[0] = 0;
+  boff[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    if (ks[g] < 0) return KGREF_ERR_KSUM;
+    off[g + 1] = off[g] + ks[g];
+    boff[g + 1] = boff[g] + (ks[g] + gran_k - 1) / gran_k;
+  }
+  return KGREF_OK;
+}
+
+/* ---------------------------------------------------------------- element access */
+
+typedef struct {
+  const void *A, *sa, *B, *sb;
+  const float* C;
+  const int64_t* off;
+  const int32_t* boff;
+  int M, N, gran_k, dtype;
+} problem_t;
+
+static inline double dec_a(const problem_t* p, int64_t t, int m) {
+  if (p->dtype == KGREF_BF16) return kgref_bf16(((const uint16_t*)p->A)[t * p->M + m]);
+  return g_e4m3[((const uint8_t*)p->A)[t * p->M + m]];
+}
+
+static inline double dec_b(const problem_t* p, int64_t t, int n) {
+  if (p->dtype == KGREF_BF16) return kgref_bf16(((const uint16_t*)p->B)[t * p->N + n]);
+  return g_e4m3[((const uint8_t*)p->B)[t * p->N + n]];
+}
+
+/* Scale of scale-row r for channel c of an operand with `width` channels. */
+static inline double scale_of(const problem_t* p, const void* s, int64_t r, int c, int width) {
+  if (p->dtype == KGREF_BF16) return 1.0;
+  if (p->dtype == KGREF_E4M3_F32SCALE) return (double)((const float*)s)[r * width + c];
+  return kgref_e8m0(((const uint8_t*)s)[r * width + c]);
+}
+
+static inline int block_len(const problem_t* p) {
+  /* bf16 carries no scales: the whole group is one accumulation. */
+  return p->gran_k;
+}
+
+/* ---------------------------------------------------------------- one row of D */
+
+/* D[g][m][:] and its bound, using caller-provided scratch of 4*N doubles. */
+static void row_of_d(const problem_t* p, int g, int m, double* d_row, double* bnd_row,
+                     double* scratch) {
+  const int N = p->N;
+  double* part = scratch;           /* block partial, exact for fp8 */
+  double* part_abs = scratch + N;   /* block partial of |a||b|      */
+  double* acc = scratch + 2 * N;
+  double* acc_abs = scratch + 3 * N;
+  for (int n = 0; n < N; ++n) acc[n] = acc_abs[n] = 0.0;
+
+  const int64_t t_begin = p->off[g], t_end = p->off[g + 1];
+  if (t_end > t_begin) {
+    const int L = block_len(p);
+    int64_t kb = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += L, ++kb) {
+      const int64_t t1 = (t0 + L < t_end) ? t0 + L : t_end;
+      for (int n = 0; n < N; ++n) part[n] = part_abs[n] = 0.0;
+      for (int64_t t = t0; t < t1; ++t) {
+        const double a = dec_a(p, t, m);
+        const double aa = fabs(a);
+        for (int n = 0; n < N; ++n) {
+          const double b = dec_b(p, t, n);
+          part[n] += a * b;
+          part_abs[n] += aa * fabs(b);
+        }
+      }
+      /* scales are applied to the finished block partial */
+      const int64_t srow = (int64_t)p->boff[g] + kb;
+      const double s_a = scale_of(p, p->sa, srow, m, p->M);
+      for (int n = 0; n < N; ++n) {
+        const double s = s_a * scale_of(p, p->sb, srow, n, p->N);
+        acc[n] += s * part[n];
+        acc_abs[n] += fabs(s) * part_abs[n];
+      }
+    }
+  }
+  for (int n = 0; n < N; ++n) {
+    const double c = p->C ? (double)p->C[((int64_t)g * p->M + m) * N + n] : 0.0;
+    /* empty group: D = C exactly (or +0.0) */
+    d_row[n] = (t_end > t_begin) ? c + acc[n] : c;
+    bnd_row[n] = acc_abs[n];
+  }
+}
+
+/* One element, same arithmetic as row_of_d. */
+static void elem_of_d(const problem_t* p, int g, int m, int n, double* d, double* bnd) {
+  double acc = 0.0, acc_abs = 0.0;
+  const int64_t t_begin = p->off[g], t_end = p->off[g + 1];
+  const int L = block_len(p);
+  int64_t kb = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += L, ++kb) {
+    const int64_t t1 = (t0 + L < t_end) ? t0 + L : t_end;
+    double part = 0.0, part_abs = 0.0;
+    for (int64_t t = t0; t < t1; ++t) {
+      const double a = dec_a(p, t, m), b = dec_b(p, t, n);
+      part += a * b;
+      part_abs += fabs(a) * fabs(b);
+    }
+    const int64_t srow = (int64_t)p->boff[g] + kb;
+    const double s = scale_of(p, p->sa, srow, m, p->M) * scale_of(p, p->sb, srow, n, p->N);
+    acc += s * part;
+    acc_abs += fabs(s) * part_abs;
+  }
+  const double c = p->C ? (double)p->C[((int64_t)g * p->M + m) * p->N + n] : 0.0;
+  *d = (t_end > t_begin) ? c + acc : c;
+  *bnd = acc_abs;
+}
+
+/* ---------------------------------------------------------------- threading */
+
+static int g_last_threads = 0;
+int kgref_last_threads(void) { return g_last_threads; }
+
+static int pick_threads(int requested) {
+  if (requested > 0) return requested;
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+typedef struct {
+  const problem_t* p;
+  int g_lo, g_hi, m_lo, m_hi;
+  double *D, *bound;
+  atomic_long next;
+  long nitems;
+  /* sampled mode */
+  int64_t ns;
+  const int32_t *sg, *sm, *sn;
+  int err;
+} job_t;
+
+static void* full_worker(void* arg) {
+  job_t* j = (job_t*)arg;
+  const int N = j->p->N, rows = j->m_hi - j->m_lo;
+  double* scratch = (double*)malloc(sizeof(double) * 4 * (size_t)(N > 0 ? N : 1));
+  if (!scratch) {
+    j->err = 1;
+    return NULL;
+  }
+  for (;;) {
+    long it = atomic_fetch_add(&j->next, 1);
+    if (it >= j->nitems) break;
+    int g = j->g_lo + (int)(it / rows), mm = (int)(it % rows);
+    size_t o = ((size_t)(g - j->g_lo) * rows + mm) * N;
+    row_of_d(j->p, g, j->m_lo + mm, j->D + o, j->bound + o, scratch);
+  }
+  free(scratch);
+  return NULL;
+}
+
+static void* sampled_worker(void* arg) {
+  job_t* j = (job_t*)arg;
+  for (;;) {
+    long it = atomic_fetch_add(&j->next, 1);
+    if (it >= j->ns) break;
+    elem_of_d(j->p, j->sg[it], j->sm[it], j->sn[it], j->D + it, j->bound + it);
+  }
+  return NULL;
+}
+
+static int run_threads(job_t* job, void* (*fn)(void*), int nthreads) {
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!th) return KGREF_ERR_SHAPE;
+  int started = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    if (pthread_create(&th[i], NULL, fn, job) != 0) break;
+    ++started;
+  }
+  if (started == 0) fn(job);
+  for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  free(th);
+  g_last_threads = started > 0 ? started : 1;
+  return job->err ? KGREF_ERR_SHAPE : KGREF_OK;
+}
+
+/* ---------------------------------------------------------------- entry points */
+
+static int setup(problem_t* p, int64_t** off, int32_t** boff, const void* A, const void* sa,
+                 const void* B, const void* sb, const float* C, const int32_t* ks, int G, int M,
+                 int N, int64_t K_total, int gran_k, int dtype) {
+  pthread_once(&g_once, build_tables);
+  int rc = kgref_validate(ks, G, M, N, K_total, gran_k, dtype);
+  if (rc != KGREF_OK) return rc;
+  if (K_total > 0 && (A == NULL || B == NULL)) return KGREF_ERR_NULL;
+  if (dtype != KGREF_BF16 && K_total > 0 && (sa == NULL || sb == NULL)) return KGREF_ERR_NULL;
+  *off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(G + 1));
+  *boff = (int32_t*)malloc(sizeof(int32_t) * (size_t)(G + 1));
+  if (!*off || !*boff) return KGREF_ERR_SHAPE;
+  /* bf16 has no scale blocks: one accumulation per group (gran_k only sizes the
+   * summation runs, which does not change the exact-product sum beyond rounding). */
+  int gk = (dtype == KGREF_BF16) ? (gran_k > 0 ? gran_k : 128) : gran_k;
+  kgref_offsets(ks, G, gk, *off, *boff);
+  p->A = A;
+  p->sa = sa;
+  p->B = B;
+  p->sb = sb;
+  p->C = C;
+  p->off = *off;
+  p->boff = *boff;
+  p->M = M;
+  p->N = N;
+  p->gran_k = gk;
+  p->dtype = dtype;
+  return KGREF_OK;
+}
+
+int kgref_wgrad(const void* A, const void* sa, const void* B, const void* sb, const float* C,
+                const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k, int dtype,
+                int g_lo, int g_hi, int m_lo, int m_hi, double* D_out, double* bound_out,
+                int nthreads) {
+  problem_t p;
+  int64_t* off = NULL;
+  int32_t* boff = NULL;
+  int rc = setup(&p, &off, &boff, A, sa, B, sb, C, ks, G, M, N, K_total, gran_k, dtype);
+  if (rc == KGREF_OK && (g_lo < 0 || g_hi > G || g_lo > g_hi || m_lo < 0 || m_hi > M || m_lo > m_hi))
+    rc = KGREF_ERR_SHAPE;
+  if (rc == KGREF_OK && (long)(g_hi - g_lo) * (m_hi - m_lo) > 0 && N > 0) {
+    if (!D_out || !bound_out) {
+      rc = KGREF_ERR_NULL;
+    } else {
+      job_t job;
+      memset(&job, 0, sizeof job);
+      job.p = &p;
+      job.g_lo = g_lo;
+      job.g_hi = g_hi;
+      job.m_lo = m_lo;
+      job.m_hi = m_hi;
+      job.D = D_out;
+      job.bound = bound_out;
+      atomic_init(&job.next, 0);
+      job.nitems = (long)(g_hi - g_lo) * (m_hi - m_lo);
+      int nt = pick_threads(nthreads);
+      if (nt > job.nitems) nt = (int)job.nitems;
+      rc = run_threads(&job, full_worker, nt);
+    }
+  }
+  free(off);
+  free(boff);
+  return rc;
+}
+
+int kgref_wgrad_sampled(const void* A, const void* sa, const void* B, const void* sb,
+                        const float* C, const int32_t* ks, int G, int M, int N, int64_t K_total,
+                        int gran_k, int dtype, int64_t ns, const int32_t* sg, const int32_t* sm,
+                        const int32_t* sn, double* out, double* bound_out, int nthreads) {
+  problem_t p;
+  int64_t* off = NULL;
+  int32_t* boff = NULL;
+  int rc = setup(&p, &off, &boff, A, sa, B, sb, C, ks, G, M, N, K_total, gran_k, dtype);
+  if (rc == KGREF_OK && ns > 0) {
+    if (!sg || !sm || !sn || !out || !bound_out) rc = KGREF_ERR_NULL;
+    for (int64_t i = 0; rc == KGREF_OK && i < ns; ++i)
+      if (sg[i] < 0 || sg[i] >= G || sm[i] < 0 || sm[i] >= M || sn[i] < 0 || sn[i] >= N)
+        rc = KGREF_ERR_SHAPE;
+    if (rc == KGREF_OK) {
+      job_t job;
+      memset(&job, 0, sizeof job);
+      job.p = &p;
+      job.D = out;
+      job.bound = bound_out;
+      atomic_init(&job.next, 0);
+      job.ns = ns;
+      job.sg = sg;
+      job.sm = sm;
+      job.sn = sn;
+      int nt = pick_threads(nthreads);
+      if (nt > ns) nt = (int)ns;
+      rc = run_threads(&job, sampled_worker, nt);
+    }
+  }
+  free(off);
+  free(boff);
+  return rc;
+}

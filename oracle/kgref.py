@@ -1,0 +1,152 @@
+"""ctypes binding of the CPU oracle (oracle/libkgref.so).
+
+TEST INFRASTRUCTURE: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module. Argument marshalling only; all the
+arithmetic is in kgref.c (fp64, see its header for the method and the readings
+of the pages it follows).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+OK, ERR_NULL, ERR_SHAPE, ERR_GRAN, ERR_DTYPE, ERR_KSUM = 0, -1, -2, -3, -4, -9
+E4M3_F32SCALE, E4M3_UE8M0, BF16 = 0, 1, 2
+
+_lib = None
+
+
+def lib():
+    """Load the oracle library, compiling it first only if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.kgref_e4m3.restype = ctypes.c_double
+        L.kgref_e4m3.argtypes = [ctypes.c_uint8]
+        L.kgref_e8m0.restype = ctypes.c_double
+        L.kgref_e8m0.argtypes = [ctypes.c_uint8]
+        L.kgref_bf16.restype = ctypes.c_double
+        L.kgref_bf16.argtypes = [ctypes.c_uint16]
+        L.kgref_validate.restype = ctypes.c_int
+        L.kgref_validate.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64,
+                                     ctypes.c_int, ctypes.c_int]
+        L.kgref_offsets.restype = ctypes.c_int
+        L.kgref_offsets.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.kgref_wgrad.restype = ctypes.c_int
+        L.kgref_wgrad.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, i64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  vp, vp, ctypes.c_int]
+        L.kgref_wgrad_sampled.restype = ctypes.c_int
+        L.kgref_wgrad_sampled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, i64, ctypes.c_int, ctypes.c_int,
+                                          i64, vp, vp, vp, vp, vp, ctypes.c_int]
+        L.kgref_last_threads.restype = ctypes.c_int
+        L.kgref_last_threads.argtypes = []
+        _lib = L
+        del i32
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {a.dtype}")
+    return a
+
+
+def _inputs(A, sa, B, sb, C, ks, dtype):
+    ks = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    adt = np.uint16 if dtype == BF16 else np.uint8
+    A = _c(A, adt)
+    B = _c(B, adt)
+    if dtype == E4M3_F32SCALE:
+        sa, sb = _c(sa, np.float32), _c(sb, np.float32)
+    elif dtype == E4M3_UE8M0:
+        sa, sb = _c(sa, np.uint8), _c(sb, np.uint8)
+    C = _c(C, np.float32)
+    return A, sa, B, sb, C, ks
+
+
+def e4m3(byte):
+    return lib().kgref_e4m3(int(byte))
+
+
+def e8m0(byte):
+    return lib().kgref_e8m0(int(byte))
+
+
+def bf16(bits):
+    return lib().kgref_bf16(int(bits))
+
+
+def validate(ks, G, M, N, K_total, gran_k, dtype):
+    ks = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    return lib().kgref_validate(_ptr(ks) if G > 0 else None, G, M, N, K_total, gran_k, dtype)
+
+
+def offsets(ks, gran_k):
+    ks = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    G = ks.size
+    off = np.zeros(G + 1, np.int64)
+    boff = np.zeros(G + 1, np.int32)
+    rc = lib().kgref_offsets(_ptr(ks), G, gran_k, _ptr(off), _ptr(boff))
+    if rc != OK:
+        raise ValueError(f"kgref_offsets failed: {rc}")
+    return off, boff
+
+
+def wgrad(A, sa, B, sb, C, ks, M, N, gran_k, dtype, g_range=None, m_range=None,
+          threads=0, K_total=None):
+    """Reference D and bound (fp64) for groups g_range and rows m_range.
+
+    Returns (rc, D, bound); D and bound have shape [g_hi-g_lo, m_hi-m_lo, N].
+    """
+    A, sa, B, sb, C, ks = _inputs(A, sa, B, sb, C, ks, dtype)
+    G = ks.size
+    if K_total is None:
+        K_total = int(ks.astype(np.int64).sum())
+    g_lo, g_hi = g_range if g_range is not None else (0, G)
+    m_lo, m_hi = m_range if m_range is not None else (0, M)
+    shape = (max(g_hi - g_lo, 0), max(m_hi - m_lo, 0), N)
+    D = np.zeros(shape, np.float64)
+    bound = np.zeros(shape, np.float64)
+    rc = lib().kgref_wgrad(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C),
+                           _ptr(ks) if G > 0 else None, G, M, N, K_total, gran_k, dtype,
+                           g_lo, g_hi, m_lo, m_hi, _ptr(D), _ptr(bound), threads)
+    return rc, D, bound
+
+
+def wgrad_sampled(A, sa, B, sb, C, ks, M, N, gran_k, dtype, sg, sm, sn, threads=0,
+                  K_total=None):
+    """Reference value and bound for the elements (sg[i], sm[i], sn[i])."""
+    A, sa, B, sb, C, ks = _inputs(A, sa, B, sb, C, ks, dtype)
+    G = ks.size
+    if K_total is None:
+        K_total = int(ks.astype(np.int64).sum())
+    sg = np.ascontiguousarray(sg, dtype=np.int32)
+    sm = np.ascontiguousarray(sm, dtype=np.int32)
+    sn = np.ascontiguousarray(sn, dtype=np.int32)
+    ns = sg.size
+    out = np.zeros(ns, np.float64)
+    bound = np.zeros(ns, np.float64)
+    rc = lib().kgref_wgrad_sampled(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C),
+                                   _ptr(ks) if G > 0 else None, G, M, N, K_total, gran_k,
+                                   dtype, ns, _ptr(sg), _ptr(sm), _ptr(sn), _ptr(out),
+                                   _ptr(bound), threads)
+    return rc, out, bound
+
+
+def last_threads():
+    return lib().kgref_last_threads()
