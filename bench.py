@@ -1,0 +1,201 @@
+"""Benchmark of the K-grouped weight-gradient GEMM (libkgwgrad) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--fast]
+
+A step is one kg_wgrad call over one batch of synthetic inputs (the whole hot
+path: device scan of the expert sizes, schedule, grouped contraction with the
+block rescale, epilogue with C, empty-expert fill). Inputs are resident in HBM
+before the timed region. Prints one JSON line.
+
+Default workload: bf16, G = 4 experts, M = 1024, N = 2048, 16384 tokens routed
+uniformly over three experts (the second expert gets none), D accumulated onto
+C. The other workloads (worked, zipf_fp8, ue8m0_many, local_share) are
+selectable with --workload.
+
+The JSON line carries:
+  value / ms_per_step     TFLOP/s of useful work 2*sum(K_g)*M*N over the timed steps
+  roofline                the kernel's average launch time (HIP events on its
+                          stream) against its bound: MFMA peak for its dtype or
+                          8 TB/s of HBM, whichever the algorithmic work hits first;
+                          `traffic` is the measured HBM bytes per launch from
+                          rocprofv3 counters (profiles/*.json) if those were taken
+                          for the current kernel source, else null
+  cpu_baseline            the CPU oracle (fp64, all host cores) timed on a bounded
+                          sample of the same workload, scaled to TFLOP/s
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp8": 5000.0}  # dense MFMA TFLOP/s, MI355X
+HBM_GBS = 8000.0
+METRIC = "K-grouped wgrad TFLOP/s (2*sum(K)*M*N) + % of FP8 MFMA / HBM roofline, 1 GPU"
+
+DESCR = {
+    "worked": "worked shape: G=3, ks=[32,45,27], M=64, N=128, fp8 e4m3 + fp32 scales per 128 tokens, no C",
+    "bf16": "bf16: G=4, M=1024, N=2048, 16384 tokens uniform over 3 experts (1 empty), D += C",
+    "zipf_fp8": "zipf fp8: G=32, M=7168, N=4096, 65536 tokens Zipf(1.2), fp8 e4m3 + fp32 scales per 128, D += C",
+    "ue8m0_many": "many experts UE8M0: G=256 (51 empty), M=2048, N=7168, 131072 tokens top-8, fp8 e4m3 + E8M0 per 32, no C",
+    "local_share": "local expert share: G=8, M=7168, N=4096, 262144 tokens ~N(32768,8192), fp8 e4m3 + fp32 scales per 128, D += C",
+}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_grouped_gemm_tn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_for(workload, fast):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"kg_wgrad_{workload}{'_fast' if fast else ''}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The oracle as it is, on a bounded sample of the workload's rows."""
+    from oracle import kgref
+    h = case.host()
+    G, M, N = case.G, case.M, case.N
+    live = [g for g in range(G) if case.ks[g] > 0]
+    g_lo, g_hi = min(live), max(live) + 1
+    tokens = int(case.ks[g_lo:g_hi].astype("int64").sum())
+
+    def run(rows):
+        t0 = time.perf_counter()
+        rc, _, _ = kgref.wgrad(h["A"], h["sa"], h["B"], h["sb"], h["C"], h["ks"], M, N,
+                               case.gran_k, case.dtype, g_range=(g_lo, g_hi), m_range=(0, rows))
+        assert rc == kgref.OK
+        return time.perf_counter() - t0
+
+    rows = 8
+    t = run(rows)
+    if t < budget_s / 4:
+        rows = int(min(M, max(rows, rows * budget_s / max(t, 1e-3) / 2)))
+        rows = max(8, rows - rows % 8)
+        t = run(rows)
+    flops = 2.0 * tokens * rows * N
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": kgref.last_threads(),
+            "kind": "oracle",
+            "sample": f"experts {g_lo}..{g_hi - 1}, rows 0..{rows - 1} of M={M}, all N={N}: "
+                      f"{flops / 1e9:.2f} GFLOP in {t:.2f} s (fp64)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16", choices=list(DESCR))
+    ap.add_argument("--fast", action="store_true", help="fp8 kinds: contract with the fp8 MFMA")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_grouped_gemm_tn_amd as kg
+    from fp8_grouped_gemm_tn_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    case = inputs.workload(args.workload, device="cuda", seed=args.seed)
+    A, B = case.A, case.B
+    sa, sb, C = case.sa, case.sb, case.C
+    ks = torch.from_numpy(case.ks).to(dev)
+    D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev)
+    flags = kg.KG_FLAG_FP8_MFMA if (args.fast and case.dtype != kg.KG_BF16) else 0
+    dtype = case.dtype | flags
+
+    def step():
+        kg.kg_wgrad(A, sa, B, sb, C, D, ks, case.gran_k, dtype, K_total=case.K_total)
+
+    for _ in range(args.warmup):
+        step()
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert kg.kg_status() == kg.KG_OK
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    total_ms = ev[0][0].elapsed_time(ev[-1][1])
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    flops = case.flops
+    nbytes = case.algorithmic_bytes()
+    is_bf16 = case.dtype == kg.KG_BF16
+    mfma_peak = PEAK["bf16"] if is_bf16 else PEAK["fp8"]
+    t_mfma = flops / (mfma_peak * 1e12)
+    t_hbm = nbytes / (HBM_GBS * 1e9)
+    secs = avg_launch_ms / 1e3
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(flops / secs / 1e12, 3), "peak": mfma_peak,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = counters_for(args.workload, bool(flags))
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+    roof["roofline_ms"] = round(max(t_mfma, t_hbm) * 1e3, 4)
+
+    value = flops / (ms_per_step / 1e3) / 1e12
+    dname = "bf16" if is_bf16 else ("fp8 e4m3 (fp8 MFMA)" if flags else "fp8 e4m3 (bf16 MFMA)")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dname,
+        "data": "synthetic (seeded generators, fp8 values quantised per 128/32-token block)",
+        "config": {"workload": DESCR[args.workload], "G": case.G, "M": case.M, "N": case.N,
+                   "tokens": case.K_total, "gran_k": case.gran_k if not is_bf16 else None,
+                   "fp8_mfma": bool(flags)},
+        "roofline": roof,
+        "pct_fp8_peak": round(100.0 * value / PEAK["fp8"], 2),
+        "hbm_gbs": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),
+        "wall_s": round(wall, 4),
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

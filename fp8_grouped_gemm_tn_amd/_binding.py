@@ -1,0 +1,99 @@
+"""ctypes binding of libkgwgrad.so (the C ABI in include/kgwgrad.h).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels. There is no fallback: if the library is missing or cannot be
+loaded, the calls raise.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkgwgrad.so")
+
+KG_E4M3_F32SCALE, KG_E4M3_UE8M0, KG_BF16 = 0, 1, 2
+KG_FLAG_FP8_MFMA = 0x100
+KG_OK = 0
+KG_ERR_NULL, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_DTYPE = -1, -2, -3, -4
+KG_ERR_ALIGN, KG_ERR_ALIAS, KG_ERR_UNSUPPORTED, KG_ERR_HIP, KG_ERR_KSUM = -5, -6, -7, -8, -9
+ERROR_NAMES = {0: "KG_OK", -1: "KG_ERR_NULL", -2: "KG_ERR_SHAPE", -3: "KG_ERR_GRAN",
+               -4: "KG_ERR_DTYPE", -5: "KG_ERR_ALIGN", -6: "KG_ERR_ALIAS",
+               -7: "KG_ERR_UNSUPPORTED", -8: "KG_ERR_HIP", -9: "KG_ERR_KSUM"}
+
+# name -> (restype, argtypes): the symbols include/kgwgrad.h declares
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+SIGNATURES = {
+    "kg_wgrad": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32,
+                        _vp]),
+    "kg_status": (_i32, [_vp]),
+    "kg_debug_offsets": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "kg_max_groups": (_i32, []),
+}
+
+_lib = None
+
+
+class KgError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what} failed: {ERROR_NAMES.get(code, code)}")
+        self.code = code
+
+
+def lib():
+    """The loaded library. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m fp8_grouped_gemm_tn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream=None):
+    """Call kg_wgrad with torch device tensors (or None); returns the status code."""
+    return lib().kg_wgrad(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D), _ptr(ks),
+                          int(G), int(M), int(N), int(K_total), int(gran_k), int(dtype),
+                          _stream(stream))
+
+
+def kg_wgrad(A, sa, B, sb, C, D, ks, gran_k, dtype, K_total=None, stream=None):
+    """D = C + K-grouped A^T B. Shapes are read from the tensors:
+    A [K_total, M], B [K_total, N], D [G, M, N], ks [G] int32 (all on the GPU)."""
+    G, M, N = D.shape
+    if K_total is None:
+        K_total = A.shape[0]
+    rc = kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream)
+    if rc != KG_OK:
+        raise KgError(rc, "kg_wgrad")
+    return D
+
+
+def kg_status(stream=None):
+    return lib().kg_status(_stream(stream))
+
+
+def kg_debug_offsets(ks, gran_k, off, boff, stream=None):
+    rc = lib().kg_debug_offsets(_ptr(ks), int(ks.numel()), int(gran_k), _ptr(off), _ptr(boff),
+                                _stream(stream))
+    if rc != KG_OK:
+        raise KgError(rc, "kg_debug_offsets")
+
+
+def kg_max_groups():
+    return lib().kg_max_groups()

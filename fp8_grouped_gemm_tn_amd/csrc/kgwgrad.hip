@@ -1,0 +1,752 @@
+// kgwgrad.hip -- K-grouped weight-gradient GEMM on MI355X (gfx950), C ABI.
+//
+// For every expert g, D[g] = C[g] (or 0) + sum over the expert's token blocks of
+// (sa_kb outer sb_kb) * (A_kb^T . B_kb), where expert g owns token rows
+// [off[g], off[g+1]) of A [K_total, M] and B [K_total, N] (page "How to Use
+// DeepGEMM Weight Gradient Kernels for Training Backward Passes", sections
+// "Understanding K-Grouped Weight Gradient Kernels" and "FP8 Implementation
+// Example"). Scales are shared by each gran_k-token run of one expert and are
+// applied to the run's partial sum after it is accumulated (GitHub issue "Is
+// DeepGEMM directly applicable to backward in training?", qijiaxing 2025-03-26).
+//
+// Design (MI355X-first, not the pages' TMA design):
+//  * One persistent launch. Every workgroup rebuilds the schedule in LDS
+//    (kg_sched.h) and walks work items (expert, m-tile, n-tile), longest experts
+//    first. Items are dealt so that the workgroups of one XCD take neighbouring
+//    tiles of one expert and share their operand rows in that XCD's L2.
+//  * Empty experts become copy/fill items (D = C, or 0).
+//  * Operands move global -> LDS with buffer loads that write LDS directly; token
+//    rows past the expert's end are outside the buffer's range and read as zero,
+//    which masks ragged tails in both operands.
+//  * The contraction runs over tokens, the leading (strided) dimension of both
+//    operands: LDS holds token-major rows, and transposing LDS reads
+//    (ds_read_b64_tr_b8 / _tr_b16) hand every lane token-contiguous fragments.
+//  * Math policies:
+//      bf16              16x16x32 bf16 MFMA, fp32 accumulation.
+//      fp8, precise      fragments are widened to bf16 in registers (exact for
+//                        e4m3; an E8M0 scale is folded into the widening, also
+//                        exact) and contracted with the bf16 MFMA, whose fp32
+//                        accumulation is exact to rounding. fp32 scales: the
+//                        block's four chained MFMAs give its partial sum, which is
+//                        rescaled by sa (x) sb on the VALU and accumulated.
+//      fp8, fast         the 16x16x128 fp8 MFMA (the scaled form applies E8M0
+//                        scales per 32 tokens). gfx950 sums each group of 8 fp8
+//                        products aligned to the largest with about 13 bits, so
+//                        this policy trades accuracy (~1e-4 of sum|ab|) for twice
+//                        the MFMA rate. Selected by KG_FLAG_FP8_MFMA.
+//  * 8 waves per workgroup (2 per SIMD); two LDS stages (block kb+1 loads while
+//    block kb computes); an LDS-staged epilogue with float4 C loads and
+//    non-temporal float4 D stores.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "kg_device.h"
+#include "kg_sched.h"
+#include "kgwgrad.h"
+
+// Per-device status word (KG_OK or KG_ERR_KSUM); read and cleared by kg_status.
+__device__ int kgwgrad_status_word;
+
+namespace kg {
+
+enum Kind { F32S = 0, E8M0 = 1, BF16 = 2 };
+
+struct Params {
+  const unsigned char* A;
+  const unsigned char* sa;
+  const unsigned char* B;
+  const unsigned char* sb;
+  const float* C;
+  float* D;
+  const int32_t* ks;
+  int G, M, N;
+  int64_t K_total;
+  int gran;  // tokens per scale row
+  int tiles_m, tiles_n;
+};
+
+// Tile configuration: BM x BN per workgroup, 8 waves as WAVES_M x WAVES_N, TK tokens
+// per LDS stage, ELT bytes per operand element, SCALE_BYTES of scale tile per operand.
+template <int BM_, int BN_, int WAVES_M_, int TK_, int ELT_, int SCALE_BYTES_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, TK = TK_, ELT = ELT_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = kWaves / WAVES_M_;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int NI = WM / 16, NJ = WN / 16;
+  // LDS rows: one token each, BM (BN) elements + 16 bytes of padding
+  static constexpr int ROWA = BM * ELT + 16, ROWB = BN * ELT + 16;
+  static constexpr int CHA = ROWA / 16, CHB = ROWB / 16;
+  static constexpr int LOADS_A = TK * CHA / 64, LOADS_B = TK * CHB / 64;
+  static constexpr int OPA = TK * ROWA, OPB = TK * ROWB;
+  static constexpr int SCALE_BYTES = SCALE_BYTES_;
+  static constexpr int SA_OFF = OPA + OPB, SB_OFF = SA_OFF + SCALE_BYTES;
+  static constexpr int STAGE = SB_OFF + SCALE_BYTES;
+  // epilogue: passes over pairs of 16-column sub-tiles
+  static constexpr int EPI_COLS = WAVES_N * 32;
+  static constexpr int EPI_STRIDE = EPI_COLS + 4;
+  static constexpr int EPI_BYTES = BM * EPI_STRIDE * 4;
+  static constexpr int EPI_PER = BM * (EPI_COLS / 4) / kThreads;
+  static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile must be whole sub-tile pairs");
+  static_assert(TK * CHA % 64 == 0 && TK * CHB % 64 == 0, "stage must be whole wave loads");
+  static_assert(EPI_BYTES <= 2 * STAGE, "epilogue must fit the stages");
+  static_assert(BM * (EPI_COLS / 4) % kThreads == 0, "epilogue work must split evenly");
+  static_assert(SCALE_BYTES <= 1024, "one wave load per scale tile");
+};
+
+// fp8, 256 x 256 per workgroup, 64 x 128 per wave, 128 tokens per stage
+using CfgF8 = Cfg<256, 256, 4, 128, 1, 1024>;
+// bf16, same tile, 64 tokens per stage
+using CfgB16 = Cfg<256, 256, 4, 64, 2, 0>;
+
+// ---------------------------------------------------------------- fill
+
+// D tile = C tile (or 0) for an empty expert.
+template <class CF>
+__device__ void fill_tile(const Params& p, int g, int m0, int n0) {
+  if (p.C == p.D) return;  // in place: D already holds C
+  const int t = threadIdx.x;
+  constexpr int kCols4 = CF::BN / 4;
+  constexpr int kPer = CF::BM * kCols4 / kThreads;
+  constexpr int kBatch = kPer < 16 ? kPer : 16;
+  static_assert(kPer % kBatch == 0, "fill batches");
+  const size_t base = (size_t)g * p.M * p.N;
+#pragma unroll
+  for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+    v4f v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int e = t + kThreads * (b0 + k);
+      const int r = e / kCols4, c4 = e - r * kCols4;
+      const int m = m0 + r, n = n0 + 4 * c4;
+      v[k] = v4f{0.f, 0.f, 0.f, 0.f};
+      if (p.C && m < p.M && n < p.N)
+        v[k] = __builtin_nontemporal_load((const v4f*)(p.C + base + (size_t)m * p.N + n));
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int e = t + kThreads * (b0 + k);
+      const int r = e / kCols4, c4 = e - r * kCols4;
+      const int m = m0 + r, n = n0 + 4 * c4;
+      if (m < p.M && n < p.N)
+        __builtin_nontemporal_store(v[k], (v4f*)(p.D + base + (size_t)m * p.N + n));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- epilogue
+
+// Pass `pass` takes sub-tile columns jn = 2*pass, 2*pass+1 of every wave: WAVES_N
+// strips of 32 columns x BM rows. Thread element idx -> LDS (row, col), global (m, n).
+template <class CF>
+__device__ inline void epi_coords(int idx, int pass, int m0, int n0, int& row, int& lcol, int& m,
+                                  int& n) {
+  constexpr int kRow4 = CF::EPI_COLS / 4;  // float4 per LDS row
+  row = idx / kRow4;
+  const int c4 = idx - row * kRow4;
+  const int strip = c4 >> 3;
+  lcol = 4 * c4;
+  m = m0 + row;
+  n = n0 + strip * CF::WN + 32 * pass + 4 * (c4 & 7);
+}
+
+template <class CF>
+__device__ inline void epi_load_c(const Params& p, size_t base, int pass, int m0, int n0,
+                                  v4f (&c)[CF::EPI_PER]) {
+#pragma unroll
+  for (int k = 0; k < CF::EPI_PER; ++k) {
+    int row, lcol, m, n;
+    epi_coords<CF>(threadIdx.x + kThreads * k, pass, m0, n0, row, lcol, m, n);
+    c[k] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (p.C && m < p.M && n < p.N)
+      c[k] = __builtin_nontemporal_load((const v4f*)(p.C + base + (size_t)m * p.N + n));
+  }
+}
+
+// acc (this lane's 4 rows x 1 column of each 16x16 sub-tile) + C -> D through LDS.
+template <class CF>
+__device__ inline void store_tile(const Params& p, unsigned char* lds, int g, int m0, int n0,
+                                  const v4f (&acc)[CF::NI][CF::NJ]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  float* e = (float*)lds;
+  const size_t base = (size_t)g * p.M * p.N;
+  v4f cnext[CF::EPI_PER];
+  epi_load_c<CF>(p, base, 0, m0, n0, cnext);
+#pragma unroll
+  for (int pass = 0; pass < CF::NJ / 2; ++pass) {
+    __syncthreads();  // stage buffers / previous pass no longer read
+#pragma unroll
+    for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * CF::WM + 16 * i + 4 * q + r;
+          const int col = wn * 32 + 16 * jj + j;
+          e[row * CF::EPI_STRIDE + col] = acc[i][2 * pass + jj][r];
+        }
+    v4f c[CF::EPI_PER];
+#pragma unroll
+    for (int k = 0; k < CF::EPI_PER; ++k) c[k] = cnext[k];
+    if (pass + 1 < CF::NJ / 2) epi_load_c<CF>(p, base, pass + 1, m0, n0, cnext);
+    __syncthreads();  // this pass's accumulators are in LDS
+#pragma unroll
+    for (int k = 0; k < CF::EPI_PER; ++k) {
+      int row, lcol, m, n;
+      epi_coords<CF>(threadIdx.x + kThreads * k, pass, m0, n0, row, lcol, m, n);
+      if (m < p.M && n < p.N) {
+        const v4f v = *(const v4f*)(e + row * CF::EPI_STRIDE + lcol) + c[k];
+        __builtin_nontemporal_store(v, (v4f*)(p.D + base + (size_t)m * p.N + n));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stage loads
+
+// Stage kb of an item: token rows [TK*kb, TK*kb + TK) of the expert's A and B
+// slices (rows past the expert's end read as zero), plus the scale rows that
+// cover them.
+template <int KIND, class CF>
+__device__ inline void load_stage(const Params& p, unsigned char* st, int64_t t_begin, int Kg,
+                                  int boff_g, int kb, int m0, int n0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rows = uniform(min(CF::TK, Kg - CF::TK * kb));
+  const int64_t t0 = t_begin + (int64_t)CF::TK * kb;
+  const int eM = p.M * CF::ELT, eN = p.N * CF::ELT;
+  const v4i ra = make_rsrc(p.A + t0 * eM, (uint32_t)(rows * eM));
+  const v4i rb = make_rsrc(p.B + t0 * eN, (uint32_t)(rows * eN));
+  const uint32_t sA = lds_addr(st), sB = sA + CF::OPA;
+  for (int k = w; k < CF::LOADS_A; k += kWaves) {
+    const int idx = 64 * k + lane;
+    const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
+    const uint32_t v =
+        ch == CF::CHA - 1 ? kOobOffset : (uint32_t)(row * eM + m0 * CF::ELT + 16 * ch);
+    load16_lds(ra, sA + 1024 * k, v);
+  }
+  for (int k = w; k < CF::LOADS_B; k += kWaves) {
+    const int idx = 64 * k + lane;
+    const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
+    const uint32_t v =
+        ch == CF::CHB - 1 ? kOobOffset : (uint32_t)(row * eN + n0 * CF::ELT + 16 * ch);
+    load16_lds(rb, sB + 1024 * k, v);
+  }
+  if constexpr (KIND != BF16) {
+    // scale tiles: fp32 -> one row of BM (BN) floats; E8M0 -> TK/gran rows of BM (BN) bytes
+    constexpr int esz = KIND == F32S ? 4 : 1;
+    const int per = KIND == F32S ? 1 : CF::TK / p.gran;  // scale rows per stage
+    const int nb_g = (Kg + p.gran - 1) / p.gran;
+    const int r0 = per * kb;
+    const int nrows = uniform(min(per, nb_g - r0));
+    const int64_t r = (int64_t)boff_g + r0;
+    if (w == 0) {
+      constexpr int cpr = CF::BM * esz / 16;  // 16-byte chunks per scale row
+      const int sr = lane / cpr, c = lane - sr * cpr;
+      const v4i rs = make_rsrc(p.sa + r * p.M * esz, (uint32_t)(nrows * p.M * esz));
+      load16_lds(rs, sA + CF::SA_OFF,
+                 sr < per ? (uint32_t)(sr * p.M * esz + m0 * esz + 16 * c) : kOobOffset);
+    } else if (w == 1) {
+      constexpr int cpr = CF::BN * esz / 16;
+      const int sr = lane / cpr, c = lane - sr * cpr;
+      const v4i rs = make_rsrc(p.sb + r * p.N * esz, (uint32_t)(nrows * p.N * esz));
+      load16_lds(rs, sA + CF::SB_OFF,
+                 sr < per ? (uint32_t)(sr * p.N * esz + n0 * esz + 16 * c) : kOobOffset);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fragments
+
+// fast fp8: 32 contraction bytes per lane for the 16x16x128 MFMA: tokens 16q..16q+15
+// then 64+16q..64+16q+15. `p` is the lane's base (row 16q + j/2, byte 8*(j&1)).
+template <int ROW>
+__device__ inline v8i frag_f8(const unsigned char* p) {
+  const v2i x0 = tr8(p + 0 * ROW);
+  const v2i x1 = tr8(p + 8 * ROW);
+  const v2i x2 = tr8(p + 64 * ROW);
+  const v2i x3 = tr8(p + 72 * ROW);
+  return v8i{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+}
+
+// precise fp8: 8 tokens widened to bf16 (times a power-of-two scale, exact).
+__device__ inline v8bf widen8(v2i x, float scale) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.x, scale, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.x, scale, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.y, scale, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x.y, scale, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// E8M0 byte -> fp32 scale 2^(e-127); 255 is NaN.
+__device__ inline float e8m0_scale(int e) {
+  return e == 255 ? __builtin_nanf("") : __builtin_ldexpf(1.0f, e - 127);
+}
+
+// ---------------------------------------------------------------- compute policies
+
+// All policies: wave (wm, wn) owns rows [wm*WM, +WM) and cols [wn*WN, +WN) of the
+// tile; acc[i][jn] is the 16x16 sub-tile (i, jn), this lane holding rows 4q..4q+3,
+// column j.
+
+// fast fp8 + fp32 scales: one fp8 MFMA per sub-tile gives the block partial; the
+// rescale of sub-tile s-1 is issued after the MFMA of sub-tile s so they overlap.
+template <class CF>
+__device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  const int lrow = 16 * q + (j >> 1);
+  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const float* sSa = (const float*)(st + CF::SA_OFF);
+  const float* sSb = (const float*)(st + CF::SB_OFF);
+  v8i af[CF::NI];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i) af[i] = frag_f8<CF::ROWA>(aBase + 16 * i);
+  v4f sa[CF::NI];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i) sa[i] = *(const v4f*)(sSa + wm * CF::WM + 16 * i + 4 * q);
+  float sbv[CF::NJ];
+#pragma unroll
+  for (int jn = 0; jn < CF::NJ; ++jn) sbv[jn] = sSb[wn * CF::WN + 16 * jn + j];
+  constexpr int S = CF::NI * CF::NJ;
+  v8i bcur = frag_f8<CF::ROWB>(bBase), bnext = bcur;
+  v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int jn = s / CF::NI, i = s % CF::NI;
+    if (i == 0 && jn + 1 < CF::NJ) bnext = frag_f8<CF::ROWB>(bBase + 16 * (jn + 1));
+    const v4f part = mfma_fp8(af[i], bcur, v4f{0.f, 0.f, 0.f, 0.f});
+    if (s > 0) {
+      const int pj = (s - 1) / CF::NI, pi = (s - 1) % CF::NI;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[pi][r] * sbv[pj], prev[r], acc[pi][pj][r]);
+    }
+    prev = part;
+    if (i == CF::NI - 1) bcur = bnext;
+  }
+  constexpr int li = CF::NI - 1, lj = CF::NJ - 1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[li][lj][r] = fmaf(sa[li][r] * sbv[lj], prev[r], acc[li][lj][r]);
+}
+
+// fast fp8 + E8M0: the scaled MFMA takes lane 16b+i's exponent for (row i, 32-token
+// block b) and accumulates directly.
+template <class CF>
+__device__ inline void compute_fast_e8m0(const unsigned char* st, int gran,
+                                         v4f (&acc)[CF::NI][CF::NJ]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  const int lrow = 16 * q + (j >> 1);
+  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const unsigned char* sSa = st + CF::SA_OFF;
+  const unsigned char* sSb = st + CF::SB_OFF;
+  const int srow = gran == 32 ? q : 0;
+  v8i af[CF::NI];
+  int ea[CF::NI];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i) {
+    af[i] = frag_f8<CF::ROWA>(aBase + 16 * i);
+    ea[i] = sSa[srow * CF::BM + wm * CF::WM + 16 * i + j];
+  }
+  v8i bcur = frag_f8<CF::ROWB>(bBase);
+#pragma unroll
+  for (int jn = 0; jn < CF::NJ; ++jn) {
+    const v8i bnext = jn + 1 < CF::NJ ? frag_f8<CF::ROWB>(bBase + 16 * (jn + 1)) : bcur;
+    const int eb = sSb[srow * CF::BN + wn * CF::WN + 16 * jn + j];
+#pragma unroll
+    for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_fp8_e8m0(af[i], bcur, acc[i][jn], ea[i], eb);
+    bcur = bnext;
+  }
+}
+
+// precise fp8: lane base row 8q + j/2; MFMA kk (tokens 32kk..32kk+31) takes this
+// lane's 8 tokens 32kk+8q..32kk+8q+7 for its row (A) or column (B).
+
+// precise fp8 + fp32 scales: per block, four chained bf16 MFMAs (K = 32 each) give
+// the partial sum of sub-tile (i, jn), which is rescaled on the VALU one sub-tile
+// behind the MFMAs.
+template <class CF>
+__device__ inline void compute_precise_f32s(const unsigned char* st,
+                                            v4f (&acc)[CF::NI][CF::NJ]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  const int lrow = 8 * q + (j >> 1);
+  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const float* sSa = (const float*)(st + CF::SA_OFF);
+  const float* sSb = (const float*)(st + CF::SB_OFF);
+  v8bf af[CF::NI][4];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) af[i][kk] = widen8(tr8(aBase + 32 * kk * CF::ROWA + 16 * i), 1.0f);
+  constexpr int S = CF::NI * CF::NJ;
+  v2i rnext[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+  v8bf bf[4];
+  v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int jn = s / CF::NI, i = s % CF::NI;
+    if (i == 0) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
+      if (jn + 1 < CF::NJ) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+      }
+    }
+    v4f part = mfma_bf16(af[i][0], bf[0], v4f{0.f, 0.f, 0.f, 0.f});
+    part = mfma_bf16(af[i][1], bf[1], part);
+    part = mfma_bf16(af[i][2], bf[2], part);
+    part = mfma_bf16(af[i][3], bf[3], part);
+    if (s > 0) {
+      const int pj = (s - 1) / CF::NI, pi = (s - 1) % CF::NI;
+      const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * pi + 4 * q);
+      const float sb = sSb[wn * CF::WN + 16 * pj + j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[r] * sb, prev[r], acc[pi][pj][r]);
+    }
+    prev = part;
+  }
+  constexpr int li = CF::NI - 1, lj = CF::NJ - 1;
+  const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * li + 4 * q);
+  const float sb = sSb[wn * CF::WN + 16 * lj + j];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[li][lj][r] = fmaf(sa[r] * sb, prev[r], acc[li][lj][r]);
+}
+
+// precise fp8 + E8M0: every fragment is widened with its power-of-two scale
+// (exact), then the bf16 MFMAs accumulate straight into acc.
+template <class CF>
+__device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
+                                            v4f (&acc)[CF::NI][CF::NJ]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  const int lrow = 8 * q + (j >> 1);
+  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const unsigned char* sSa = st + CF::SA_OFF;
+  const unsigned char* sSb = st + CF::SB_OFF;
+  // 32-token block kk uses scale row kk (gran 32) or row 0 (gran 128)
+  const int g32 = gran == 32 ? 1 : 0;
+  v8bf af[CF::NI][4];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float s = e8m0_scale(sSa[g32 * kk * CF::BM + wm * CF::WM + 16 * i + j]);
+      af[i][kk] = widen8(tr8(aBase + 32 * kk * CF::ROWA + 16 * i), s);
+    }
+  v2i rnext[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+#pragma unroll
+  for (int jn = 0; jn < CF::NJ; ++jn) {
+    v8bf bf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float s = e8m0_scale(sSb[g32 * kk * CF::BN + wn * CF::WN + 16 * jn + j]);
+      bf[kk] = widen8(rnext[kk], s);
+    }
+    if (jn + 1 < CF::NJ) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i][kk], bf[kk], acc[i][jn]);
+  }
+}
+
+// bf16: lane 4r+c of a 16-lane group names token row r, halfwords 4c..4c+3; lane
+// base row 8q + j/4. MFMA kk takes tokens 32kk+8q..32kk+8q+7.
+template <class CF>
+__device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  const int lrow = 8 * q + (j >> 2);
+  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 3) + 2 * (wm * CF::WM);
+  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 3) + 2 * (wn * CF::WN);
+#pragma unroll
+  for (int kk = 0; kk < CF::TK / 32; ++kk) {
+    v8bf af[CF::NI];
+#pragma unroll
+    for (int i = 0; i < CF::NI; ++i) {
+      const v4bf x0 = tr16(aBase + (32 * kk + 0) * CF::ROWA + 32 * i);
+      const v4bf x1 = tr16(aBase + (32 * kk + 4) * CF::ROWA + 32 * i);
+      af[i] = v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
+#pragma unroll
+    for (int jn = 0; jn < CF::NJ; ++jn) {
+      const v4bf y0 = tr16(bBase + (32 * kk + 0) * CF::ROWB + 32 * jn);
+      const v4bf y1 = tr16(bBase + (32 * kk + 4) * CF::ROWB + 32 * jn);
+      const v8bf b = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+#pragma unroll
+      for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i], b, acc[i][jn]);
+    }
+  }
+}
+
+template <int KIND, bool FAST, class CF>
+__device__ inline void compute_stage(const unsigned char* st, int gran,
+                                     v4f (&acc)[CF::NI][CF::NJ]) {
+  if constexpr (KIND == BF16)
+    compute_bf16<CF>(st, acc);
+  else if constexpr (KIND == F32S && FAST)
+    compute_fast_f32s<CF>(st, acc);
+  else if constexpr (KIND == F32S)
+    compute_precise_f32s<CF>(st, acc);
+  else if constexpr (FAST)
+    compute_fast_e8m0<CF>(st, gran, acc);
+  else
+    compute_precise_e8m0<CF>(st, gran, acc);
+}
+
+// ---------------------------------------------------------------- the kernel
+
+template <int KIND, bool FAST, class CF>
+__global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int64_t wsum_k[kWaves];
+  __shared__ int32_t wsum_b[kWaves];
+  Sched s = sched_carve(smem + 2 * CF::STAGE, p.G);
+  const int gran = KIND == BF16 ? CF::TK : p.gran;
+  if (sched_build(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
+    return;
+  }
+  const int T = p.tiles_m * p.tiles_n;
+  const int total = p.G * T;
+  const int grid = gridDim.x;
+  // XCD-aware deal: workgroup b runs on XCD b % 8; give each XCD a contiguous run
+  // of items per round so its workgroups share operand rows in its L2.
+  const int b = blockIdx.x;
+  const int slot = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
+
+  for (int base = 0; base < total; base += grid) {
+    const int idx = base + slot;
+    if (idx >= total) break;
+    const Item it = decode_item(idx, T, p.tiles_m, p.tiles_n, s.order);
+    const int g = it.g;
+    const int m0 = it.tm * CF::BM, n0 = it.tn * CF::BN;
+    const int64_t t_begin = s.off[g];
+    const int Kg = uniform((int)(s.off[g + 1] - t_begin));
+    __syncthreads();  // the previous item is done with the stage buffers
+    if (Kg == 0) {
+      fill_tile<CF>(p, g, m0, n0);
+      continue;
+    }
+    const int boff_g = uniform(s.boff[g]);
+    const int nk = (Kg + CF::TK - 1) / CF::TK;
+    v4f acc[CF::NI][CF::NJ];
+#pragma unroll
+    for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+      for (int jn = 0; jn < CF::NJ; ++jn) acc[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    load_stage<KIND, CF>(p, smem, t_begin, Kg, boff_g, 0, m0, n0);
+    for (int kb = 0; kb < nk; ++kb) {
+      wait_all_and_barrier();  // block kb has landed; everyone is done with block kb-1
+      if (kb + 1 < nk)
+        load_stage<KIND, CF>(p, smem + ((kb + 1) & 1) * CF::STAGE, t_begin, Kg, boff_g, kb + 1,
+                             m0, n0);
+      compute_stage<KIND, FAST, CF>(smem + (kb & 1) * CF::STAGE, p.gran, acc);
+    }
+    store_tile<CF>(p, smem, g, m0, n0, acc);
+  }
+}
+
+// Same scan as the main kernel, written out for tests.
+__global__ __launch_bounds__(kThreads, 1) void kg_offsets_kernel(const int32_t* ks, int G, int gran,
+                                                                 int64_t* off, int32_t* boff) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int64_t wsum_k[kWaves];
+  __shared__ int32_t wsum_b[kWaves];
+  Sched s = sched_carve(smem, G);
+  // K_total is not known here: the sum check fails, the scans are still written
+  sched_build(ks, G, gran, -1, s, wsum_k, wsum_b);
+  for (int g = threadIdx.x; g <= G; g += kThreads) {
+    off[g] = s.off[g];
+    boff[g] = s.boff[g];
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+// KG_VERBOSE=1 in the environment prints HIP errors to stderr.
+static int hip_fail(hipError_t e, const char* what) {
+  static const bool verbose = getenv("KG_VERBOSE") != nullptr;
+  if (verbose) fprintf(stderr, "kgwgrad: %s: %s\n", what, hipGetErrorString(e));
+  return KG_ERR_HIP;
+}
+
+struct Launch {
+  const void* fn;
+  int stage_bytes;  // both stages
+  int bm, bn;
+};
+
+template <int KIND, bool FAST, class CF>
+static Launch launch_of() {
+  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF>, 2 * CF::STAGE, CF::BM, CF::BN};
+}
+
+static Launch pick(int kind, bool fast) {
+  if (kind == BF16) return launch_of<BF16, false, CfgB16>();
+  if (kind == F32S) return fast ? launch_of<F32S, true, CfgF8>() : launch_of<F32S, false, CfgF8>();
+  return fast ? launch_of<E8M0, true, CfgF8>() : launch_of<E8M0, false, CfgF8>();
+}
+
+struct DeviceInfo {
+  int cus = 0;
+  bool ready = false;
+};
+static std::mutex g_mu;
+static DeviceInfo g_dev[64];
+
+static int device_setup(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (dev < 0 || dev >= 64) return KG_ERR_HIP;
+  DeviceInfo& d = g_dev[dev];
+  if (!d.ready) {
+    int cus = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    const Launch all[5] = {pick(BF16, false), pick(F32S, false), pick(F32S, true),
+                           pick(E8M0, false), pick(E8M0, true)};
+    for (const Launch& l : all) {
+      e = hipFuncSetAttribute(l.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              l.stage_bytes + sched_bytes(kMaxGroups));
+      if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    }
+    d.cus = cus;
+    d.ready = true;
+  }
+  return KG_OK;
+}
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15) != 0; }
+
+}  // namespace kg
+
+using namespace kg;
+
+extern "C" int kg_max_groups(void) { return kMaxGroups; }
+
+extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb,
+                        const float* C, float* D, const int32_t* ks, int G, int M, int N,
+                        int64_t K_total, int gran_k, int dtype_flags, void* stream) {
+  const int dtype = dtype_flags & 0xFF;
+  const int flags = dtype_flags & ~0xFF;
+  if (dtype != KG_E4M3_F32SCALE && dtype != KG_E4M3_UE8M0 && dtype != KG_BF16)
+    return KG_ERR_DTYPE;
+  if (flags & ~KG_FLAG_FP8_MFMA) return KG_ERR_DTYPE;
+  const bool fast = (flags & KG_FLAG_FP8_MFMA) != 0;
+  if (fast && dtype == KG_BF16) return KG_ERR_DTYPE;
+  if (G < 0 || M < 0 || N < 0 || K_total < 0) return KG_ERR_SHAPE;
+  if (dtype != KG_BF16 && gran_k != 32 && gran_k != 128) return KG_ERR_GRAN;
+  if (dtype == KG_E4M3_F32SCALE && gran_k != 128) return KG_ERR_UNSUPPORTED;
+  if (G > kMaxGroups) return KG_ERR_UNSUPPORTED;
+  if (M > (1 << 24) || N > (1 << 24) || K_total > INT32_MAX) return KG_ERR_UNSUPPORTED;
+  if (G == 0 || M == 0 || N == 0) return KG_OK;
+  if (D == nullptr || ks == nullptr) return KG_ERR_NULL;
+  if (K_total > 0 && (A == nullptr || B == nullptr)) return KG_ERR_NULL;
+  if (dtype == KG_BF16) {
+    if (sa != nullptr || sb != nullptr) return KG_ERR_NULL;
+  } else if (K_total > 0 && (sa == nullptr || sb == nullptr)) {
+    return KG_ERR_NULL;
+  }
+  if (M % 16 != 0 || N % 16 != 0) return KG_ERR_ALIGN;
+  if (misaligned(A) || misaligned(B) || misaligned(sa) || misaligned(sb) || misaligned(C) ||
+      misaligned(D) || ((uintptr_t)ks & 3) != 0)
+    return KG_ERR_ALIGN;
+  const int elt = dtype == KG_BF16 ? 2 : 1;
+  const size_t dbytes = (size_t)G * M * N * 4;
+  if (C != nullptr && C != D && overlap(C, dbytes, D, dbytes)) return KG_ERR_ALIAS;
+  if (overlap(A, (size_t)K_total * M * elt, D, dbytes) ||
+      overlap(B, (size_t)K_total * N * elt, D, dbytes) || overlap(ks, (size_t)G * 4, D, dbytes))
+    return KG_ERR_ALIAS;
+
+  const int kind = dtype == KG_E4M3_F32SCALE ? F32S : dtype == KG_E4M3_UE8M0 ? E8M0 : BF16;
+  const Launch L = pick(kind, fast);
+  const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
+  const int64_t total = (int64_t)G * tiles_m * tiles_n;
+  if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;
+
+  int dev = 0;
+  const hipError_t eg = hipGetDevice(&dev);
+  if (eg != hipSuccess) return hip_fail(eg, "hipGetDevice");
+  const int rc = device_setup(dev);
+  if (rc != KG_OK) return rc;
+
+  Params p;
+  p.A = (const unsigned char*)A;
+  p.sa = (const unsigned char*)sa;
+  p.B = (const unsigned char*)B;
+  p.sb = (const unsigned char*)sb;
+  p.C = C;
+  p.D = D;
+  p.ks = ks;
+  p.G = G;
+  p.M = M;
+  p.N = N;
+  p.K_total = K_total;
+  p.gran = dtype == KG_BF16 ? 0 : gran_k;
+  p.tiles_m = tiles_m;
+  p.tiles_n = tiles_n;
+  const int cus = g_dev[dev].cus > 0 ? g_dev[dev].cus : 256;
+  const int grid = (int)(total < cus ? total : cus);
+  void* args[] = {&p};
+  const hipError_t e = hipLaunchKernel(L.fn, dim3(grid), dim3(kThreads), args,
+                                       L.stage_bytes + sched_bytes(G), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return KG_OK;
+}
+
+extern "C" int kg_status(void* stream) {
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int v = 0;
+  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(kgwgrad_status_word), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyFromSymbol");
+  if (v != 0) {
+    const int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(kgwgrad_status_word), &zero, sizeof zero, 0,
+                          hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyToSymbol");
+  }
+  return v;
+}
+
+extern "C" int kg_debug_offsets(const int32_t* ks, int G, int gran_k, int64_t* off, int32_t* boff,
+                                void* stream) {
+  if (G < 0 || G > kMaxGroups) return KG_ERR_SHAPE;
+  if (gran_k <= 0) return KG_ERR_GRAN;
+  if (off == nullptr || boff == nullptr || (G > 0 && ks == nullptr)) return KG_ERR_NULL;
+  hipLaunchKernelGGL(kg_offsets_kernel, dim3(1), dim3(kThreads), sched_bytes(G),
+                     (hipStream_t)stream, ks, G, gran_k, off, boff);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return KG_OK;
+}

@@ -1,0 +1,119 @@
+/*
+ * kgwgrad.h -- K-grouped weight-gradient GEMM for Mixture-of-Experts training on
+ * AMD Instinct MI355X (gfx950). C ABI of libkgwgrad.so.
+ *
+ * Operation (page "How to Use DeepGEMM Weight Gradient Kernels for Training
+ * Backward Passes": lede, "Understanding K-Grouped Weight Gradient Kernels",
+ * "FP8 Implementation Example", "BF16 Alternative"; GitHub issue "Is DeepGEMM
+ * directly applicable to backward in training?", qijiaxing's comment of
+ * 2025-03-26 on per-128-token scales along the accumulation axis applied after
+ * accumulation):
+ *
+ *   Expert g owns the contiguous token rows [off[g], off[g+1]) of
+ *     A [K_total, M]  (activations, row-major, M contiguous) and
+ *     B [K_total, N]  (output gradients, row-major, N contiguous),
+ *   where off[0] = 0 and off[g+1] = off[g] + ks[g]. For every g:
+ *
+ *     D[g] = C[g] (or 0) + sum over token blocks kb of expert g of
+ *            (sa[boff[g]+kb, :] outer sb[boff[g]+kb, :]) * (A_kb^T . B_kb)
+ *
+ *   with blocks of gran_k tokens that restart at each expert's first token (the
+ *   last block of an expert may be partial) and boff[g+1] = boff[g] +
+ *   ceil(ks[g] / gran_k). Empty experts (ks[g] == 0) are skipped: D[g] = C[g]
+ *   bit for bit, or +0.0 without C ("Dispatch and Tensor-Map Handling").
+ *
+ * Memory: every pointer is a device pointer; the caller owns every buffer. The
+ * library allocates no memory per call and never synchronises inside kg_wgrad.
+ *
+ * Thread safety: calls on different streams may run concurrently; they share
+ * one per-device status word (see kg_status).
+ */
+#ifndef KGWGRAD_H
+#define KGWGRAD_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input kinds (argument `dtype`). */
+typedef enum {
+  KG_E4M3_F32SCALE = 0, /* A, B: fp8 e4m3fn bytes; sa, sb: fp32 per (block, channel)      */
+  KG_E4M3_UE8M0 = 1,    /* A, B: fp8 e4m3fn bytes; sa, sb: uint8 exponent e, scale 2^(e-127) */
+  KG_BF16 = 2           /* A, B: bf16; sa, sb must be NULL; gran_k is ignored              */
+} kg_dtype;
+
+/*
+ * Flag OR-ed into `dtype` for the fp8 kinds: contract with the fp8 MFMA instead of
+ * widening the fp8 values to bf16 first. Twice the MFMA rate, but gfx950's fp8 MFMA
+ * adds each group of 8 products aligned to the largest of them with about 13
+ * bits, so the result is accurate to roughly 1e-4 of sum|a*b| rather than to
+ * fp32 rounding (the default). Invalid with KG_BF16.
+ */
+#define KG_FLAG_FP8_MFMA 0x100
+
+/* Return codes. */
+typedef enum {
+  KG_OK = 0,
+  KG_ERR_NULL = -1,        /* a required pointer is NULL, or sa/sb given for bf16          */
+  KG_ERR_SHAPE = -2,       /* G, M, N or K_total negative                                  */
+  KG_ERR_GRAN = -3,        /* fp8 with gran_k not in {32, 128}                             */
+  KG_ERR_DTYPE = -4,       /* unknown dtype, or an invalid flag                            */
+  KG_ERR_ALIGN = -5,       /* M or N not a multiple of 16, or a pointer not 16-byte aligned */
+  KG_ERR_ALIAS = -6,       /* C and D overlap without being the same buffer                */
+  KG_ERR_UNSUPPORTED = -7, /* a combination this build does not implement (see kg_wgrad)   */
+  KG_ERR_HIP = -8,         /* the HIP runtime reported an error                            */
+  KG_ERR_KSUM = -9         /* some ks[g] < 0, or sum(ks) != K_total (reported by kg_status) */
+} kg_status_code;
+
+/*
+ * kg_wgrad -- enqueue D = C + K-grouped A^T B on `stream`.
+ *
+ *   A      [K_total, M]   fp8 e4m3fn bytes, or bf16
+ *   sa     [nblk, M]      fp32 (KG_E4M3_F32SCALE) or uint8 E8M0 (KG_E4M3_UE8M0); NULL for bf16
+ *   B      [K_total, N]   same element type as A
+ *   sb     [nblk, N]      same type as sa; NULL for bf16
+ *   C      [G, M, N] fp32, may be NULL (treated as 0) or equal to D (in-place accumulate)
+ *   D      [G, M, N] fp32, output
+ *   ks     [G] int32, device memory: tokens per expert, in expert order
+ *   nblk   = sum_g ceil(ks[g] / gran_k)
+ *   gran_k tokens per scale block: 128 or 32 (fp8); ignored for bf16
+ *   stream a hipStream_t (NULL: the default stream)
+ *
+ * Implemented combinations: (KG_E4M3_F32SCALE, 128), (KG_E4M3_UE8M0, 32),
+ * (KG_E4M3_UE8M0, 128) and KG_BF16. (KG_E4M3_F32SCALE, 32) returns
+ * KG_ERR_UNSUPPORTED. G is limited to 1024 (kg_max_groups).
+ *
+ * Returns KG_OK after enqueueing, or an error code before enqueueing anything (D
+ * untouched). G == 0, M == 0 or N == 0 return KG_OK without a launch. A ks that
+ * does not add up to K_total or holds a negative count is detected on the device:
+ * the kernel then writes nothing and records KG_ERR_KSUM for kg_status.
+ */
+int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb, const float* C,
+             float* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
+             int dtype, void* stream);
+
+/*
+ * kg_status -- synchronise `stream`, then return and clear the device status
+ * word of the current device (KG_OK, or KG_ERR_KSUM if a kg_wgrad call since the
+ * last kg_status found an inconsistent ks). Returns KG_ERR_HIP if the stream
+ * reports an error.
+ */
+int kg_status(void* stream);
+
+/*
+ * kg_debug_offsets -- run the device prefix scan that kg_wgrad's kernels use and
+ * write off[G+1] (int64 token offsets) and boff[G+1] (int32 scale-row offsets)
+ * to device memory. Test hook. Errors: KG_ERR_NULL, KG_ERR_SHAPE (G < 0 or
+ * G > 1024), KG_ERR_GRAN (gran_k <= 0), KG_ERR_HIP.
+ */
+int kg_debug_offsets(const int32_t* ks, int G, int gran_k, int64_t* off, int32_t* boff,
+                     void* stream);
+
+/* Largest G accepted by kg_wgrad and kg_debug_offsets. */
+int kg_max_groups(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

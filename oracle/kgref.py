@@ -139,6 +139,8 @@ def wgrad_sampled(A, sa, B, sb, C, ks, M, N, gran_k, dtype, sg, sm, sn, threads=
     sm = np.ascontiguousarray(sm, dtype=np.int32)
     sn = np.ascontiguousarray(sn, dtype=np.int32)
     ns = sg.size
+    if sm.size != ns or sn.size != ns:
+        raise ValueError("sample index arrays differ in length")
     out = np.zeros(ns, np.float64)
     bound = np.zeros(ns, np.float64)
     rc = lib().kgref_wgrad_sampled(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C),

@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching any GPU (all the
+argument sets below fail validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp8_grouped_gemm_tn_amd as kg
+from fp8_grouped_gemm_tn_amd import _binding as B
+from fp8_grouped_gemm_tn_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kgwgrad.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*int\s+(kg_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert names == sorted(B.SIGNATURES)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_enums_match_binding():
+    text = open(HEADER).read()
+    for name, val in re.findall(r"(KG_\w+)\s*=\s*(-?\d+)", text):
+        assert getattr(B, name) == int(val), name
+    for name, val in re.findall(r"#define\s+(KG_\w+)\s+(0x[0-9a-fA-F]+|\d+)", text):
+        assert getattr(B, name) == int(val, 0), name
+
+
+def test_max_groups():
+    assert kg.kg_max_groups() == 1024
+
+
+FAKE = 0x100000  # an aligned, never dereferenced address
+
+
+def call(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE + (1 << 31),
+         G=3, M=64, N=128, K=104, gran=128, dtype=kg.KG_E4M3_F32SCALE):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.lib().kg_wgrad(v(A), v(sa), v(Bp), v(sb), v(C), v(D), v(ks), G, M, N, K, gran,
+                            dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), B.KG_ERR_DTYPE),
+    (dict(dtype=kg.KG_BF16 | kg.KG_FLAG_FP8_MFMA, sa=None, sb=None), B.KG_ERR_DTYPE),
+    (dict(dtype=kg.KG_E4M3_F32SCALE | 0x200), B.KG_ERR_DTYPE),
+    (dict(G=-1), B.KG_ERR_SHAPE),
+    (dict(M=-16), B.KG_ERR_SHAPE),
+    (dict(K=-1), B.KG_ERR_SHAPE),
+    (dict(gran=64), B.KG_ERR_GRAN),
+    (dict(gran=32), B.KG_ERR_UNSUPPORTED),  # fp32 scales at 32 tokens: not built
+    (dict(G=1025), B.KG_ERR_UNSUPPORTED),
+    (dict(D=None), B.KG_ERR_NULL),
+    (dict(ks=None), B.KG_ERR_NULL),
+    (dict(A=None), B.KG_ERR_NULL),
+    (dict(sb=None), B.KG_ERR_NULL),
+    (dict(dtype=kg.KG_BF16), B.KG_ERR_NULL),  # scales given for bf16
+    (dict(M=72), B.KG_ERR_ALIGN),
+    (dict(N=8), B.KG_ERR_ALIGN),
+    (dict(A=FAKE + 4), B.KG_ERR_ALIGN),
+    (dict(D=FAKE + (1 << 30) + 8), B.KG_ERR_ALIGN),
+    (dict(C=FAKE + (1 << 30) + 64), B.KG_ERR_ALIAS),  # partial overlap of C and D
+    (dict(D=FAKE + 4096), B.KG_ERR_ALIAS),  # D overlaps A
+])
+def test_synchronous_errors(kw, code):
+    assert call(**kw) == code
+
+
+def test_empty_shapes_are_ok_without_launch():
+    assert call(G=0) == B.KG_OK
+    assert call(M=0) == B.KG_OK
+    assert call(N=0) == B.KG_OK
+
+
+def test_debug_offsets_errors():
+    L = B.lib()
+    v = ctypes.c_void_p
+    assert L.kg_debug_offsets(v(FAKE), -1, 128, v(FAKE), v(FAKE), None) == B.KG_ERR_SHAPE
+    assert L.kg_debug_offsets(v(FAKE), 1025, 128, v(FAKE), v(FAKE), None) == B.KG_ERR_SHAPE
+    assert L.kg_debug_offsets(v(FAKE), 3, 0, v(FAKE), v(FAKE), None) == B.KG_ERR_GRAN
+    assert L.kg_debug_offsets(None, 3, 128, v(FAKE), v(FAKE), None) == B.KG_ERR_NULL
+
+
+# ---------------------------------------------------------------- generators
+
+def test_routing_generators():
+    for name in inputs.WORKLOADS:
+        ks = inputs.workload_ks(name)
+        assert ks.dtype == np.int32 and (ks >= 0).all()
+    assert inputs.workload_ks("worked").tolist() == [32, 45, 27]
+    ks = inputs.workload_ks("bf16")
+    assert ks.size == 4 and ks[1] == 0 and ks.sum() == 16384
+    ks = inputs.workload_ks("zipf_fp8")
+    assert ks.size == 32 and ks.sum() == 65536 and ks.max() > 10 * max(ks.min(), 1)
+    ks = inputs.workload_ks("ue8m0_many")
+    assert ks.size == 256 and ks.sum() == 131072 and (ks == 0).sum() == 51
+    ks = inputs.workload_ks("local_share")
+    assert ks.size == 8 and ks.sum() == 262144
+
+
+def test_quantizer_blocks_restart_per_group_and_fit_e4m3():
+    import torch
+    ks = np.array([130, 0, 5], np.int32)
+    x = torch.randn(135, 16) * 3
+    q, s = inputs.quantize_fp8(x, ks, 128, pow2=False)
+    assert s.shape == (2 + 1, 16)  # ceil(130/128) + ceil(5/128)
+    deq = q.view(torch.float8_e4m3fn).float()
+    rows = torch.tensor([0] * 128 + [1] * 2 + [2] * 5)
+    err = (deq * s[rows] - x).abs()
+    assert (err <= x.abs() * 2 ** -3 + s[rows] * 2 ** -9).all()
+    q2, e = inputs.quantize_fp8(x, ks, 32, pow2=True)
+    assert e.dtype == torch.uint8 and e.shape == (5 + 1, 16)
+    sc = torch.ldexp(torch.ones(e.shape), e.to(torch.int32) - 127)
+    rows = torch.tensor([0] * 32 + [1] * 32 + [2] * 32 + [3] * 32 + [4] * 2 + [5] * 5)
+    assert (q2.view(torch.float8_e4m3fn).float().abs() <= 448).all()
+    assert ((q2.view(torch.float8_e4m3fn).float() * sc[rows] - x).abs() <= x.abs() * 2 ** -3 + sc[rows] * 2 ** -9).all()

@@ -1,0 +1,325 @@
+"""GPU parity: libkgwgrad (through its C ABI) against the CPU oracle.
+
+Default (precise) paths, from the fp32 accumulation of exact fp8 or bf16 products:
+|D - D_ref| <= 1e-5 * sum_t |a(t,m) b(t,n)| + 1e-6 and ||D - D_ref||_F <=
+1e-5 ||D_ref||_F. Offsets and empty experts are bit-exact.
+
+Fast fp8-MFMA mode (KG_FLAG_FP8_MFMA): gfx950's fp8 MFMA adds each group of 8
+products aligned to the largest with about 13 bits, so a group loses less than
+8 * 2^-13 of its largest product, i.e. at most 2^-10 of its sum of |products|:
+|D - D_ref| <= 2^-10 * sum|ab| + 1e-6, and ||D - D_ref||_F <= 1e-4 ||D_ref||_F.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_grouped_gemm_tn_amd as kg
+from fp8_grouped_gemm_tn_amd import inputs
+from oracle import kgref
+
+pytestmark = pytest.mark.gpu
+
+F32, UE8, BF = kg.KG_E4M3_F32SCALE, kg.KG_E4M3_UE8M0, kg.KG_BF16
+FAST = kg.KG_FLAG_FP8_MFMA
+RTOL, ATOL, FROB = 1e-5, 1e-6, 1e-5
+FAST_RTOL, FAST_FROB = 2.0 ** -10, 1e-4
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def to_dev(case):
+    d = dev()
+    mv = lambda t: None if t is None else t.to(d)
+    return dict(A=mv(case.A), B=mv(case.B), sa=mv(case.sa), sb=mv(case.sb), C=mv(case.C),
+                ks=torch.from_numpy(case.ks).to(d))
+
+
+def run_gpu(case, t, D=None, C="default", check_status=True, flags=0):
+    if D is None:
+        D = torch.full((case.G, case.M, case.N), float("nan"), dtype=torch.float32, device=dev())
+    Cp = t["C"] if C == "default" else C
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], Cp, D, t["ks"], case.gran_k,
+                case.dtype | flags, K_total=case.K_total)
+    if check_status:
+        assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    return D
+
+
+def oracle_full(case, C="default"):
+    h = case.host()
+    Ch = h["C"] if C == "default" else C
+    rc, D, bound = kgref.wgrad(h["A"], h["sa"], h["B"], h["sb"], Ch, h["ks"], case.M, case.N,
+                               case.gran_k, case.dtype)
+    assert rc == kgref.OK
+    return D, bound
+
+
+def check_close(D_gpu, D_ref, bound, what="", fast=False):
+    D = D_gpu.detach().cpu().numpy().astype(np.float64)
+    assert np.isfinite(D).all(), f"{what}: non-finite output"
+    err = np.abs(D - D_ref)
+    lim = (FAST_RTOL if fast else RTOL) * bound + ATOL
+    bad = err > lim
+    assert not bad.any(), (f"{what}: {bad.sum()} elements out of tolerance, worst "
+                           f"{(err - lim).max():.3e} at {np.unravel_index(np.argmax(err - lim), err.shape)}")
+    ref_norm = np.linalg.norm(D_ref)
+    if ref_norm > 0:
+        rel = np.linalg.norm(D - D_ref) / ref_norm
+        assert rel <= (FAST_FROB if fast else FROB), f"{what}: Frobenius {rel:.3e}"
+
+
+def small_case(dtype, gran, ks, M, N, with_c=True, seed=1, **kw):
+    return inputs.make_case("small", ks, M, N, dtype, gran, with_c=with_c, seed=seed, **kw)
+
+
+# ---------------------------------------------------------------- offsets
+
+def test_device_offsets_bit_exact():
+    for ks, gran in [([32, 45, 27], 128), ([32, 45, 27], 32), ([0, 5, 0, 300, 1, 0, 4096], 128),
+                     (list(np.random.default_rng(0).integers(0, 3000, 1024)), 32), ([], 128)]:
+        say("offsets", len(ks), gran)
+        ks_np = np.asarray(ks, np.int32)
+        G = ks_np.size
+        off = torch.full((G + 1,), -7, dtype=torch.int64, device=dev())
+        boff = torch.full((G + 1,), -7, dtype=torch.int32, device=dev())
+        kg.kg_debug_offsets(torch.from_numpy(ks_np).to(dev()), gran, off, boff)
+        torch.cuda.synchronize()
+        if G == 0:
+            assert off.cpu().tolist() == [0] and boff.cpu().tolist() == [0]
+            continue
+        r_off, r_boff = kgref.offsets(ks_np, gran)
+        assert off.cpu().numpy().tolist() == r_off.tolist()
+        assert boff.cpu().numpy().tolist() == r_boff.tolist()
+
+
+# ---------------------------------------------------------------- worked shape
+
+def test_worked_shape_full():
+    say("worked shape")
+    case = inputs.workload("worked")
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "worked")
+
+
+# ---------------------------------------------------------------- multi-tile ragged
+
+RAGGED = [300, 0, 129, 1, 513, 64]
+PATHS = [(F32, 128), (UE8, 32), (UE8, 128), (BF, 128)]
+
+
+@pytest.mark.parametrize("dtype,gran", PATHS)
+@pytest.mark.parametrize("with_c", [True, False])
+def test_ragged_multi_tile(dtype, gran, with_c):
+    say("ragged", dtype, gran, with_c)
+    # M spans two m-tiles (the second partial), N spans two n-tiles (partial)
+    case = small_case(dtype, gran, RAGGED, 320, 272, with_c=with_c, seed=3)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, f"ragged {dtype} {gran}")
+    # empty expert: bit-exact passthrough of C, or +0.0
+    g = RAGGED.index(0)
+    Dg = D[g].cpu()
+    if with_c:
+        assert torch.equal(Dg.view(torch.int32), case.C[g].view(torch.int32))
+    else:
+        assert torch.equal(Dg.view(torch.int32), torch.zeros_like(Dg).view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype,gran", PATHS)
+def test_outliers_and_small_gradients(dtype, gran):
+    say("outliers", dtype, gran)
+    case = small_case(dtype, gran, [700, 77, 1000], 256, 512, seed=4, b_std=1e-3,
+                      a_outlier_p=0.01)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "outliers")
+
+
+FAST_PATHS = [(F32, 128), (UE8, 32), (UE8, 128)]
+
+
+@pytest.mark.parametrize("dtype,gran", FAST_PATHS)
+@pytest.mark.parametrize("with_c", [True, False])
+def test_fast_fp8_mfma_mode(dtype, gran, with_c):
+    say("fast", dtype, gran, with_c)
+    case = small_case(dtype, gran, RAGGED, 320, 272, with_c=with_c, seed=13, b_std=1e-3,
+                      a_outlier_p=0.01)
+    t = to_dev(case)
+    D = run_gpu(case, t, flags=FAST)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, f"fast {dtype} {gran}", fast=True)
+    g = RAGGED.index(0)
+    if with_c:
+        assert torch.equal(D[g].cpu().view(torch.int32), case.C[g].view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype,gran", [(F32, 128), (BF, 128)])
+def test_in_place_accumulate(dtype, gran):
+    say("in place", dtype)
+    case = small_case(dtype, gran, [200, 0, 57], 64, 128, seed=5)
+    t = to_dev(case)
+    D = t["C"].clone()
+    run_gpu(case, t, D=D, C=D)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "in place")
+
+
+def test_guard_canaries_and_determinism():
+    say("canaries")
+    case = small_case(F32, 128, [129, 0, 400], 128, 256, seed=6)
+    t = to_dev(case)
+    n = case.G * case.M * case.N
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 12345.0, dtype=torch.float32, device=dev())
+    D = buf[pad:pad + n].view(case.G, case.M, case.N)
+    run_gpu(case, t, D=D)
+    assert (buf[:pad] == 12345.0).all() and (buf[pad + n:] == 12345.0).all()
+    D2 = run_gpu(case, t)
+    assert torch.equal(D.view(torch.int32), D2.view(torch.int32)), "run-to-run bits differ"
+
+
+def test_power_of_two_scales_bit_exact_on_gpu():
+    say("power of two")
+    case = small_case(F32, 128, [300, 45], 128, 128, with_c=False, seed=7)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    t2 = dict(t, sa=t["sa"] * 8.0)
+    D8 = run_gpu(case, t2)
+    assert torch.equal(D8, D * 8.0)
+    case = small_case(UE8, 32, [300, 45], 128, 128, with_c=False, seed=7)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    t2 = dict(t, sb=(t["sb"].to(torch.int32) - 3).to(torch.uint8))
+    Dm = run_gpu(case, t2)
+    assert torch.equal(Dm, D / 8.0)
+
+
+def test_k_split_invariant_on_gpu():
+    say("k split")
+    case = small_case(F32, 128, [50, 3 * 128 + 17, 9], 128, 256, seed=8)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    ks2 = torch.tensor([50, 256, 128 + 17, 9], dtype=torch.int32, device=dev())
+    C2 = torch.cat([t["C"][:2], torch.zeros_like(t["C"][:1]), t["C"][2:]])
+    D2 = torch.empty((4, case.M, case.N), dtype=torch.float32, device=dev())
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], C2, D2, ks2, 128, F32, K_total=case.K_total)
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    # D2[1] + D2[2] must equal D[1] to the tolerance, measured against sum|ab|
+    _, bound = oracle_full(case)
+    s = (D2[1] + D2[2]).double().cpu().numpy()
+    ref = D[1].double().cpu().numpy()
+    assert (np.abs(s - ref) <= 2e-5 * bound[1] + 2e-6).all()
+    assert torch.equal(D2[0], D[0]) and torch.equal(D2[3], D[2])
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_all_groups_empty_and_single_group():
+    say("all empty")
+    case = small_case(F32, 128, [0, 0, 0], 64, 64, seed=9)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    assert torch.equal(D.cpu().view(torch.int32), case.C.view(torch.int32))
+    say("single group, minimal 16x16")
+    case = small_case(BF, 128, [1], 16, 16, seed=10)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "16x16")
+
+
+def test_max_groups():
+    say("G = 1024")
+    rng = np.random.default_rng(11)
+    ks = rng.integers(0, 40, 1024).astype(np.int32)
+    ks[rng.choice(1024, 100, replace=False)] = 0
+    case = small_case(UE8, 32, ks, 16, 32, seed=11)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "G=1024")
+
+
+def test_ksum_mismatch_is_reported_and_writes_nothing():
+    say("ksum mismatch")
+    case = small_case(F32, 128, [100, 28], 64, 64, seed=12)
+    t = to_dev(case)
+    D = torch.full((2, 64, 64), float("nan"), device=dev())
+    rc = kg.kg_wgrad_raw(t["A"], t["sa"], t["B"], t["sb"], t["C"], D, t["ks"], 2, 64, 64,
+                         case.K_total - 1, 128, F32)
+    assert rc == kg.KG_OK
+    assert kg.kg_status() == kg.KG_ERR_KSUM
+    assert torch.isnan(D).all()
+    assert kg.kg_status() == kg.KG_OK  # cleared
+    bad = torch.tensor([130, -2], dtype=torch.int32, device=dev())
+    rc = kg.kg_wgrad_raw(t["A"], t["sa"], t["B"], t["sb"], t["C"], D, bad, 2, 64, 64,
+                         case.K_total, 128, F32)
+    assert rc == kg.KG_OK and kg.kg_status() == kg.KG_ERR_KSUM
+    assert torch.isnan(D).all()
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def sampled_check(case, t, D, n=1500, seed=0, fast=False):
+    rng = np.random.default_rng(seed)
+    G, M, N = case.G, case.M, case.N
+    live = np.nonzero(case.ks > 0)[0]
+    sg = rng.choice(live, n)
+    sm = rng.integers(0, M, n)
+    sn = rng.integers(0, N, n)
+    # corners of tiles and the last row / column of a few experts
+    corners = [(0, 0), (M - 1, N - 1), (min(255, M - 1), min(256, N - 1)),
+               (min(256, M - 1), min(255, N - 1))]
+    cg = [g for g in live[:4] for _ in corners]
+    cm = [m for _ in live[:4] for m, _n in corners]
+    cn = [n for _ in live[:4] for _m, n in corners]
+    sg = np.concatenate([sg, cg]).astype(np.int64)
+    sm = np.concatenate([sm, cm]).astype(np.int64)
+    sn = np.concatenate([sn, cn]).astype(np.int64)
+    assert sg.size == sm.size == sn.size
+    h = case.host()
+    rc, ref, bound = kgref.wgrad_sampled(h["A"], h["sa"], h["B"], h["sb"], h["C"], h["ks"], M,
+                                         N, case.gran_k, case.dtype, sg, sm, sn)
+    assert rc == kgref.OK
+    got = D[torch.from_numpy(sg).to(D.device), torch.from_numpy(sm).to(D.device),
+            torch.from_numpy(sn).to(D.device)].double().cpu().numpy()
+    err = np.abs(got - ref)
+    lim = (FAST_RTOL if fast else RTOL) * bound + ATOL
+    assert (err <= lim).all(), f"{(err > lim).sum()} sampled elements out of tolerance"
+    assert np.linalg.norm(got - ref) <= (FAST_FROB if fast else FROB) * np.linalg.norm(ref)
+    # every empty expert is bit-exact C (or +0.0)
+    for g in np.nonzero(case.ks == 0)[0]:
+        if case.C is not None:
+            assert torch.equal(D[g].view(torch.int32), t["C"][g].view(torch.int32))
+        else:
+            assert (D[g].view(torch.int32) == 0).all()
+
+
+@pytest.mark.parametrize("name", ["bf16", "zipf_fp8", "ue8m0_many", "local_share"])
+def test_full_size_workloads_sampled(name):
+    say("full size", name)
+    case = inputs.workload(name, device="cuda")
+    t = to_dev(case)
+    D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev())
+    run_gpu(case, t, D=D)
+    assert torch.isfinite(D).all()
+    sampled_check(case, t, D)
+    if case.dtype != BF:
+        say("full size fast", name)
+        run_gpu(case, t, D=D, flags=FAST)
+        sampled_check(case, t, D, fast=True)
+    del D, t, case
+    torch.cuda.empty_cache()
