@@ -67,6 +67,46 @@ def counters_for(workload, fast):
     return rec.get("traffic_bytes")
 
 
+COPY_BYTES = 1 << 30
+
+
+def _counter_rows(path):
+    """(kernel name, counter name, value) per dispatch from a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            key = (row.get("Dispatch_Id") or row.get("Correlation_Id"), row["Kernel_Name"])
+            out.setdefault(key, {})[row["Counter_Name"]] = float(row["Counter_Value"])
+    return out
+
+
+def ingest_counters(fetch_csv, write_csv, name):
+    """HBM bytes per launch of kg_wgrad from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a 1 GiB plain copy
+    recorded in the same CSV (bench.py --copy-calib in the same profiled run)."""
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path)
+        mine = [v[counter] for (d, k), v in rows.items() if "kg_wgrad_kernel" in k]
+        copy = [v[counter] for (d, k), v in rows.items()
+                if "copy" in k.lower() and "kg_" not in k and v[counter] > COPY_BYTES / 1024 / 4]
+        assert mine, f"no kg_wgrad dispatch in {path}"
+        assert copy, f"no 1 GiB copy dispatch in {path}"
+        factor = (COPY_BYTES / 1024) / max(copy)   # true KiB per counted KiB
+        per_launch = sorted(mine)[len(mine) // 2] * factor * 1024
+        res[counter] = {"raw_kib_median": sorted(mine)[len(mine) // 2], "copy_kib": max(copy),
+                        "scale": factor, "bytes_per_launch": per_launch}
+    rec = {"workload": name, "kernel_source": kernel_source_hash(),
+           "traffic_bytes": int(res["FETCH_SIZE"]["bytes_per_launch"] +
+                                res["WRITE_SIZE"]["bytes_per_launch"]),
+           "counters": res}
+    path = os.path.join(ROOT, "profiles", f"kg_wgrad_{name}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The oracle as it is, on a bounded sample of the workload's rows."""
     from oracle import kgref
@@ -105,7 +145,15 @@ def main():
     ap.add_argument("--fast", action="store_true", help="fp8 kinds: contract with the fp8 MFMA")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "NAME"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) into "
+                         "profiles/kg_wgrad_NAME_traffic.json")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
               f"--gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
@@ -117,6 +165,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calib:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
+        return
     case = inputs.workload(args.workload, device="cuda", seed=args.seed)
     A, B = case.A, case.B
     sa, sb, C = case.sa, case.sb, case.C

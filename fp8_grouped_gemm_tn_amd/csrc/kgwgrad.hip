@@ -78,30 +78,81 @@ struct Cfg {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = kWaves / WAVES_M_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int NI = WM / 16, NJ = WN / 16;
-  // LDS rows: one token each, BM (BN) elements + 16 bytes of padding
-  static constexpr int ROWA = BM * ELT + 16, ROWB = BN * ELT + 16;
-  static constexpr int CHA = ROWA / 16, CHB = ROWB / 16;
+  // LDS rows: one token each, BM (BN) elements + PAD bytes. With the lane-to-row
+  // maps of the compute policies, the rows one half-wave reads then start in
+  // distinct bank windows (fp8: 16-byte reads, row stride = 17 x 16 B; bf16: 32-byte
+  // reads, row stride = 34 x 16 B).
+  static constexpr int PAD = ELT == 2 ? 32 : 16;
+  static constexpr int ROWA = BM * ELT + PAD, ROWB = BN * ELT + PAD;
+  static constexpr int CHA = ROWA / 16, CHB = ROWB / 16;        // 16-byte chunks per row
+  static constexpr int DCA = BM * ELT / 16, DCB = BN * ELT / 16;  // of which data
   static constexpr int LOADS_A = TK * CHA / 64, LOADS_B = TK * CHB / 64;
+  static constexpr int SLOTS_A = (LOADS_A + kWaves - 1) / kWaves;  // per wave
+  static constexpr int SLOTS_B = (LOADS_B + kWaves - 1) / kWaves;
   static constexpr int OPA = TK * ROWA, OPB = TK * ROWB;
   static constexpr int SCALE_BYTES = SCALE_BYTES_;
   static constexpr int SA_OFF = OPA + OPB, SB_OFF = SA_OFF + SCALE_BYTES;
   static constexpr int STAGE = SB_OFF + SCALE_BYTES;
-  // epilogue: passes over pairs of 16-column sub-tiles
+  // epilogue passes: column pair pc (sub-tile columns 2pc, 2pc+1 of every wave) x
+  // row block ph of EPI_ROWS rows; LDS holds the pass's accumulators (padded rows)
+  // and its C tile (dense rows of EPI_COLS floats)
   static constexpr int EPI_COLS = WAVES_N * 32;
   static constexpr int EPI_STRIDE = EPI_COLS + 4;
-  static constexpr int EPI_BYTES = BM * EPI_STRIDE * 4;
-  static constexpr int EPI_PER = BM * (EPI_COLS / 4) / kThreads;
+  static constexpr int EPI_ROWS =
+      BM * (EPI_STRIDE + EPI_COLS) * 4 <= 2 * STAGE ? BM
+      : (BM / 2) * (EPI_STRIDE + EPI_COLS) * 4 <= 2 * STAGE ? BM / 2 : BM / 4;
+  static constexpr int EPI_C_OFF = EPI_ROWS * EPI_STRIDE * 4;
+  static constexpr int EPI_BYTES = EPI_C_OFF + EPI_ROWS * EPI_COLS * 4;
+  static constexpr int EPI_CPR = EPI_COLS / 4;                    // float4 per row
+  static constexpr int EPI_PER = EPI_ROWS * EPI_CPR / kThreads;   // float4 per thread
+  static constexpr int EPI_LOADS = EPI_ROWS * EPI_CPR / 64;       // wave loads of C
   static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile must be whole sub-tile pairs");
   static_assert(TK * CHA % 64 == 0 && TK * CHB % 64 == 0, "stage must be whole wave loads");
   static_assert(EPI_BYTES <= 2 * STAGE, "epilogue must fit the stages");
-  static_assert(BM * (EPI_COLS / 4) % kThreads == 0, "epilogue work must split evenly");
+  static_assert(EPI_ROWS * EPI_CPR % kThreads == 0, "epilogue work must split evenly");
+  static_assert(EPI_ROWS % WM == 0, "epilogue row blocks hold whole wave rows");
   static_assert(SCALE_BYTES <= 1024, "one wave load per scale tile");
 };
 
-// fp8, 256 x 256 per workgroup, 64 x 128 per wave, 128 tokens per stage
+// fp8 with the fp8 MFMA: 256 x 256 per workgroup, 64 x 128 per wave, 128 tokens per stage
 using CfgF8 = Cfg<256, 256, 4, 128, 1, 1024>;
+// fp8 widened to bf16: 256 x 128 per workgroup, 64 x 64 per wave (the widened
+// fragments need the registers a wider wave tile would take)
+using CfgF8h = Cfg<256, 128, 4, 128, 1, 1024>;
 // bf16, same tile, 64 tokens per stage
 using CfgB16 = Cfg<256, 256, 4, 64, 2, 0>;
+// bf16, 128 x 256 per workgroup (64 x 64 per wave) for problems with few tiles
+using CfgB16s = Cfg<128, 256, 2, 64, 2, 0>;
+
+// This lane's global byte offsets for its share of a stage's operand loads,
+// relative to the first loaded byte of the stage (row 0, column m0 or n0); the
+// same for every stage and item of a launch. Padding chunks get an offset past
+// any buffer range, so they load zeros.
+template <class CF>
+struct LoadOffsets {
+  uint32_t a[CF::SLOTS_A];
+  uint32_t b[CF::SLOTS_B];
+};
+
+template <class CF>
+__device__ inline LoadOffsets<CF> load_offsets(const Params& p) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t eM = p.M * CF::ELT, eN = p.N * CF::ELT;
+  LoadOffsets<CF> o;
+#pragma unroll
+  for (int s = 0; s < CF::SLOTS_A; ++s) {
+    const int idx = 64 * (w + kWaves * s) + lane;
+    const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
+    o.a[s] = ch >= CF::DCA ? kOobOffset : row * eM + 16 * ch;
+  }
+#pragma unroll
+  for (int s = 0; s < CF::SLOTS_B; ++s) {
+    const int idx = 64 * (w + kWaves * s) + lane;
+    const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
+    o.b[s] = ch >= CF::DCB ? kOobOffset : row * eN + 16 * ch;
+  }
+  return o;
+}
 
 // ---------------------------------------------------------------- fill
 
@@ -140,34 +191,22 @@ __device__ void fill_tile(const Params& p, int g, int m0, int n0) {
 
 // ---------------------------------------------------------------- epilogue
 
-// Pass `pass` takes sub-tile columns jn = 2*pass, 2*pass+1 of every wave: WAVES_N
-// strips of 32 columns x BM rows. Thread element idx -> LDS (row, col), global (m, n).
+// Thread element idx of a pass -> LDS row / float column and global (m, n).
 template <class CF>
-__device__ inline void epi_coords(int idx, int pass, int m0, int n0, int& row, int& lcol, int& m,
-                                  int& n) {
-  constexpr int kRow4 = CF::EPI_COLS / 4;  // float4 per LDS row
-  row = idx / kRow4;
-  const int c4 = idx - row * kRow4;
-  const int strip = c4 >> 3;
+__device__ inline void epi_coords(int idx, int ph, int pc, int m0, int n0, int& row, int& lcol,
+                                  int& m, int& n) {
+  row = idx / CF::EPI_CPR;
+  const int c4 = idx - row * CF::EPI_CPR;
+  const int strip = c4 >> 3;  // wave column
   lcol = 4 * c4;
-  m = m0 + row;
-  n = n0 + strip * CF::WN + 32 * pass + 4 * (c4 & 7);
+  m = m0 + ph * CF::EPI_ROWS + row;
+  n = n0 + strip * CF::WN + 32 * pc + 4 * (c4 & 7);
 }
 
-template <class CF>
-__device__ inline void epi_load_c(const Params& p, size_t base, int pass, int m0, int n0,
-                                  v4f (&c)[CF::EPI_PER]) {
-#pragma unroll
-  for (int k = 0; k < CF::EPI_PER; ++k) {
-    int row, lcol, m, n;
-    epi_coords<CF>(threadIdx.x + kThreads * k, pass, m0, n0, row, lcol, m, n);
-    c[k] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (p.C && m < p.M && n < p.N)
-      c[k] = __builtin_nontemporal_load((const v4f*)(p.C + base + (size_t)m * p.N + n));
-  }
-}
-
-// acc (this lane's 4 rows x 1 column of each 16x16 sub-tile) + C -> D through LDS.
+// acc (this lane's 4 rows x 1 column of each 16x16 sub-tile) + C -> D. Per pass:
+// the C tile goes global -> LDS by buffer loads (rows past M read as zero) while
+// the waves owning the pass's rows write their accumulators to LDS; then every
+// thread adds and stores whole float4 runs along N, non-temporally.
 template <class CF>
 __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, int m0, int n0,
                                   const v4f (&acc)[CF::NI][CF::NJ]) {
@@ -175,34 +214,48 @@ __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, in
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   float* e = (float*)lds;
-  const size_t base = (size_t)g * p.M * p.N;
-  v4f cnext[CF::EPI_PER];
-  epi_load_c<CF>(p, base, 0, m0, n0, cnext);
+  const float* cl = (const float*)(lds + CF::EPI_C_OFF);
+  const size_t gbase = (size_t)g * p.M * p.N;
+  // C of this expert, from (m0, 0) to the expert's end
+  const v4i rc = make_rsrc(p.C + gbase + (size_t)m0 * p.N,
+                           (uint32_t)((size_t)(p.M - m0) * p.N * 4));
+  constexpr int kPH = CF::BM / CF::EPI_ROWS;
 #pragma unroll
-  for (int pass = 0; pass < CF::NJ / 2; ++pass) {
-    __syncthreads();  // stage buffers / previous pass no longer read
+  for (int ph = 0; ph < kPH; ++ph) {
 #pragma unroll
-    for (int i = 0; i < CF::NI; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wm * CF::WM + 16 * i + 4 * q + r;
-          const int col = wn * 32 + 16 * jj + j;
-          e[row * CF::EPI_STRIDE + col] = acc[i][2 * pass + jj][r];
+    for (int pc = 0; pc < CF::NJ / 2; ++pc) {
+      __syncthreads();  // stage buffers / previous pass no longer read
+      if (p.C) {
+        for (int k = w; k < CF::EPI_LOADS; k += kWaves) {
+          int row, lcol, m, n;
+          epi_coords<CF>(64 * k + lane, ph, pc, m0, n0, row, lcol, m, n);
+          load16_lds(rc, lds_addr(lds + CF::EPI_C_OFF) + 1024 * k,
+                     (uint32_t)(((m - m0) * p.N + n) * 4));
         }
-    v4f c[CF::EPI_PER];
+      }
+      const int wrow0 = wm * CF::WM - ph * CF::EPI_ROWS;  // this wave's first row in the pass
+      if (wrow0 >= 0 && wrow0 < CF::EPI_ROWS) {
 #pragma unroll
-    for (int k = 0; k < CF::EPI_PER; ++k) c[k] = cnext[k];
-    if (pass + 1 < CF::NJ / 2) epi_load_c<CF>(p, base, pass + 1, m0, n0, cnext);
-    __syncthreads();  // this pass's accumulators are in LDS
+        for (int i = 0; i < CF::NI; ++i)
 #pragma unroll
-    for (int k = 0; k < CF::EPI_PER; ++k) {
-      int row, lcol, m, n;
-      epi_coords<CF>(threadIdx.x + kThreads * k, pass, m0, n0, row, lcol, m, n);
-      if (m < p.M && n < p.N) {
-        const v4f v = *(const v4f*)(e + row * CF::EPI_STRIDE + lcol) + c[k];
-        __builtin_nontemporal_store(v, (v4f*)(p.D + base + (size_t)m * p.N + n));
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = wrow0 + 16 * i + 4 * q + r;
+              const int col = wn * 32 + 16 * jj + j;
+              e[row * CF::EPI_STRIDE + col] = acc[i][2 * pc + jj][r];
+            }
+      }
+      wait_all_and_barrier();  // accumulators and C of this pass are in LDS
+#pragma unroll
+      for (int k = 0; k < CF::EPI_PER; ++k) {
+        int row, lcol, m, n;
+        epi_coords<CF>(threadIdx.x + kThreads * k, ph, pc, m0, n0, row, lcol, m, n);
+        if (m < p.M && n < p.N) {
+          v4f v = *(const v4f*)(e + row * CF::EPI_STRIDE + lcol);
+          if (p.C) v += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
+          __builtin_nontemporal_store(v, (v4f*)(p.D + gbase + (size_t)m * p.N + n));
+        }
       }
     }
   }
@@ -214,28 +267,27 @@ __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, in
 // slices (rows past the expert's end read as zero), plus the scale rows that
 // cover them.
 template <int KIND, class CF>
-__device__ inline void load_stage(const Params& p, unsigned char* st, int64_t t_begin, int Kg,
-                                  int boff_g, int kb, int m0, int n0) {
+__device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, unsigned char* st,
+                                  int64_t t_begin, int Kg, int boff_g, int kb, int m0, int n0) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rows = uniform(min(CF::TK, Kg - CF::TK * kb));
   const int64_t t0 = t_begin + (int64_t)CF::TK * kb;
   const int eM = p.M * CF::ELT, eN = p.N * CF::ELT;
-  const v4i ra = make_rsrc(p.A + t0 * eM, (uint32_t)(rows * eM));
-  const v4i rb = make_rsrc(p.B + t0 * eN, (uint32_t)(rows * eN));
+  // the resource starts at (row 0, column m0) and ends with the expert's last row
+  // of this stage: rows past it, and columns past the row end of the last row,
+  // read as zero
+  const v4i ra = make_rsrc(p.A + t0 * eM + m0 * CF::ELT, (uint32_t)(rows * eM - m0 * CF::ELT));
+  const v4i rb = make_rsrc(p.B + t0 * eN + n0 * CF::ELT, (uint32_t)(rows * eN - n0 * CF::ELT));
   const uint32_t sA = lds_addr(st), sB = sA + CF::OPA;
-  for (int k = w; k < CF::LOADS_A; k += kWaves) {
-    const int idx = 64 * k + lane;
-    const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
-    const uint32_t v =
-        ch == CF::CHA - 1 ? kOobOffset : (uint32_t)(row * eM + m0 * CF::ELT + 16 * ch);
-    load16_lds(ra, sA + 1024 * k, v);
+#pragma unroll
+  for (int s = 0; s < CF::SLOTS_A; ++s) {
+    const int k = w + kWaves * s;
+    if (CF::LOADS_A % kWaves == 0 || k < CF::LOADS_A) load16_lds(ra, sA + 1024 * k, lo.a[s]);
   }
-  for (int k = w; k < CF::LOADS_B; k += kWaves) {
-    const int idx = 64 * k + lane;
-    const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
-    const uint32_t v =
-        ch == CF::CHB - 1 ? kOobOffset : (uint32_t)(row * eN + n0 * CF::ELT + 16 * ch);
-    load16_lds(rb, sB + 1024 * k, v);
+#pragma unroll
+  for (int s = 0; s < CF::SLOTS_B; ++s) {
+    const int k = w + kWaves * s;
+    if (CF::LOADS_B % kWaves == 0 || k < CF::LOADS_B) load16_lds(rb, sB + 1024 * k, lo.b[s]);
   }
   if constexpr (KIND != BF16) {
     // scale tiles: fp32 -> one row of BM (BN) floats; E8M0 -> TK/gran rows of BM (BN) bytes
@@ -263,14 +315,20 @@ __device__ inline void load_stage(const Params& p, unsigned char* st, int64_t t_
 
 // ---------------------------------------------------------------- fragments
 
-// fast fp8: 32 contraction bytes per lane for the 16x16x128 MFMA: tokens 16q..16q+15
-// then 64+16q..64+16q+15. `p` is the lane's base (row 16q + j/2, byte 8*(j&1)).
+// fast fp8: the 32 contraction bytes of lane group q for the 16x16x128 MFMA. Byte
+// run p (8 bytes, p = 0..3) of group q falls in the instruction's 32-element scale
+// block b = 2*(p>>1) + (q>>1); it carries tokens 32b + 16*(p&1) + 8*(q&1) + 0..7 of
+// the stage, so every scale block of 32 tokens lands in one hardware block, and a
+// half-wave's reads touch 16 consecutive token rows. `p` is the lane's base: row
+// 8*(q&1) + 32*(q>>1) + j/2, byte 8*(j&1).
+__device__ inline int fast_row(int q, int j) { return 8 * (q & 1) + 32 * (q >> 1) + (j >> 1); }
+
 template <int ROW>
 __device__ inline v8i frag_f8(const unsigned char* p) {
   const v2i x0 = tr8(p + 0 * ROW);
-  const v2i x1 = tr8(p + 8 * ROW);
+  const v2i x1 = tr8(p + 16 * ROW);
   const v2i x2 = tr8(p + 64 * ROW);
-  const v2i x3 = tr8(p + 72 * ROW);
+  const v2i x3 = tr8(p + 80 * ROW);
   return v8i{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
 }
 
@@ -301,7 +359,7 @@ __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF:
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
-  const int lrow = 16 * q + (j >> 1);
+  const int lrow = fast_row(q, j);
   const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
   const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const float* sSa = (const float*)(st + CF::SA_OFF);
@@ -309,31 +367,26 @@ __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF:
   v8i af[CF::NI];
 #pragma unroll
   for (int i = 0; i < CF::NI; ++i) af[i] = frag_f8<CF::ROWA>(aBase + 16 * i);
-  v4f sa[CF::NI];
-#pragma unroll
-  for (int i = 0; i < CF::NI; ++i) sa[i] = *(const v4f*)(sSa + wm * CF::WM + 16 * i + 4 * q);
-  float sbv[CF::NJ];
-#pragma unroll
-  for (int jn = 0; jn < CF::NJ; ++jn) sbv[jn] = sSb[wn * CF::WN + 16 * jn + j];
   constexpr int S = CF::NI * CF::NJ;
   v8i bcur = frag_f8<CF::ROWB>(bBase), bnext = bcur;
   v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
+  // rescale of sub-tile (pi, pj): acc += (sa[rows] * sb[col]) * partial
+  auto rescale = [&](int pi, int pj, const v4f& part) {
+    const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * pi + 4 * q);
+    const float sb = sSb[wn * CF::WN + 16 * pj + j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[r] * sb, part[r], acc[pi][pj][r]);
+  };
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int jn = s / CF::NI, i = s % CF::NI;
     if (i == 0 && jn + 1 < CF::NJ) bnext = frag_f8<CF::ROWB>(bBase + 16 * (jn + 1));
     const v4f part = mfma_fp8(af[i], bcur, v4f{0.f, 0.f, 0.f, 0.f});
-    if (s > 0) {
-      const int pj = (s - 1) / CF::NI, pi = (s - 1) % CF::NI;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[pi][r] * sbv[pj], prev[r], acc[pi][pj][r]);
-    }
+    if (s > 0) rescale((s - 1) % CF::NI, (s - 1) / CF::NI, prev);
     prev = part;
     if (i == CF::NI - 1) bcur = bnext;
   }
-  constexpr int li = CF::NI - 1, lj = CF::NJ - 1;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) acc[li][lj][r] = fmaf(sa[li][r] * sbv[lj], prev[r], acc[li][lj][r]);
+  rescale(CF::NI - 1, CF::NJ - 1, prev);
 }
 
 // fast fp8 + E8M0: the scaled MFMA takes lane 16b+i's exponent for (row i, 32-token
@@ -344,7 +397,7 @@ __device__ inline void compute_fast_e8m0(const unsigned char* st, int gran,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
-  const int lrow = 16 * q + (j >> 1);
+  const int lrow = fast_row(q, j);
   const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
   const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const unsigned char* sSa = st + CF::SA_OFF;
@@ -473,13 +526,14 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
 }
 
 // bf16: lane 4r+c of a 16-lane group names token row r, halfwords 4c..4c+3; lane
-// base row 8q + j/4. MFMA kk takes tokens 32kk+8q..32kk+8q+7.
+// base row 4q + j/4. For MFMA kk lane group q takes tokens 32kk + 4q + 0..3 and
+// 32kk + 16 + 4q + 0..3 (a half-wave reads 8 consecutive rows per transposing read).
 template <class CF>
 __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
-  const int lrow = 8 * q + (j >> 2);
+  const int lrow = 4 * q + (j >> 2);
   const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 3) + 2 * (wm * CF::WM);
   const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 3) + 2 * (wn * CF::WN);
 #pragma unroll
@@ -488,13 +542,13 @@ __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][
 #pragma unroll
     for (int i = 0; i < CF::NI; ++i) {
       const v4bf x0 = tr16(aBase + (32 * kk + 0) * CF::ROWA + 32 * i);
-      const v4bf x1 = tr16(aBase + (32 * kk + 4) * CF::ROWA + 32 * i);
+      const v4bf x1 = tr16(aBase + (32 * kk + 16) * CF::ROWA + 32 * i);
       af[i] = v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
 #pragma unroll
     for (int jn = 0; jn < CF::NJ; ++jn) {
       const v4bf y0 = tr16(bBase + (32 * kk + 0) * CF::ROWB + 32 * jn);
-      const v4bf y1 = tr16(bBase + (32 * kk + 4) * CF::ROWB + 32 * jn);
+      const v4bf y1 = tr16(bBase + (32 * kk + 16) * CF::ROWB + 32 * jn);
       const v8bf b = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
 #pragma unroll
       for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i], b, acc[i][jn]);
@@ -537,6 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
   // of items per round so its workgroups share operand rows in its L2.
   const int b = blockIdx.x;
   const int slot = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
+  const LoadOffsets<CF> lo = load_offsets<CF>(p);
 
   for (int base = 0; base < total; base += grid) {
     const int idx = base + slot;
@@ -559,12 +614,12 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
 #pragma unroll
       for (int jn = 0; jn < CF::NJ; ++jn) acc[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    load_stage<KIND, CF>(p, smem, t_begin, Kg, boff_g, 0, m0, n0);
+    load_stage<KIND, CF>(p, lo, smem, t_begin, Kg, boff_g, 0, m0, n0);
     for (int kb = 0; kb < nk; ++kb) {
       wait_all_and_barrier();  // block kb has landed; everyone is done with block kb-1
       if (kb + 1 < nk)
-        load_stage<KIND, CF>(p, smem + ((kb + 1) & 1) * CF::STAGE, t_begin, Kg, boff_g, kb + 1,
-                             m0, n0);
+        load_stage<KIND, CF>(p, lo, smem + ((kb + 1) & 1) * CF::STAGE, t_begin, Kg, boff_g,
+                             kb + 1, m0, n0);
       compute_stage<KIND, FAST, CF>(smem + (kb & 1) * CF::STAGE, p.gran, acc);
     }
     store_tile<CF>(p, smem, g, m0, n0, acc);
@@ -606,10 +661,11 @@ static Launch launch_of() {
   return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF>, 2 * CF::STAGE, CF::BM, CF::BN};
 }
 
-static Launch pick(int kind, bool fast) {
-  if (kind == BF16) return launch_of<BF16, false, CfgB16>();
-  if (kind == F32S) return fast ? launch_of<F32S, true, CfgF8>() : launch_of<F32S, false, CfgF8>();
-  return fast ? launch_of<E8M0, true, CfgF8>() : launch_of<E8M0, false, CfgF8>();
+static Launch pick(int kind, bool fast, bool small = false) {
+  if (kind == BF16)
+    return small ? launch_of<BF16, false, CfgB16s>() : launch_of<BF16, false, CfgB16>();
+  if (kind == F32S) return fast ? launch_of<F32S, true, CfgF8>() : launch_of<F32S, false, CfgF8h>();
+  return fast ? launch_of<E8M0, true, CfgF8>() : launch_of<E8M0, false, CfgF8h>();
 }
 
 struct DeviceInfo {
@@ -627,8 +683,8 @@ static int device_setup(int dev) {
     int cus = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const Launch all[5] = {pick(BF16, false), pick(F32S, false), pick(F32S, true),
-                           pick(E8M0, false), pick(E8M0, true)};
+    const Launch all[6] = {pick(BF16, false), pick(BF16, false, true), pick(F32S, false),
+                           pick(F32S, true),  pick(E8M0, false),       pick(E8M0, true)};
     for (const Launch& l : all) {
       e = hipFuncSetAttribute(l.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                               l.stage_bytes + sched_bytes(kMaxGroups));
@@ -669,6 +725,7 @@ extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void
   if (dtype == KG_E4M3_F32SCALE && gran_k != 128) return KG_ERR_UNSUPPORTED;
   if (G > kMaxGroups) return KG_ERR_UNSUPPORTED;
   if (M > (1 << 24) || N > (1 << 24) || K_total > INT32_MAX) return KG_ERR_UNSUPPORTED;
+  if ((int64_t)M * N > (int64_t)1 << 30) return KG_ERR_UNSUPPORTED;  // one expert's C in 32-bit offsets
   if (G == 0 || M == 0 || N == 0) return KG_OK;
   if (D == nullptr || ks == nullptr) return KG_ERR_NULL;
   if (K_total > 0 && (A == nullptr || B == nullptr)) return KG_ERR_NULL;
@@ -689,16 +746,18 @@ extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void
     return KG_ERR_ALIAS;
 
   const int kind = dtype == KG_E4M3_F32SCALE ? F32S : dtype == KG_E4M3_UE8M0 ? E8M0 : BF16;
-  const Launch L = pick(kind, fast);
-  const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
-  const int64_t total = (int64_t)G * tiles_m * tiles_n;
-  if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;
-
   int dev = 0;
   const hipError_t eg = hipGetDevice(&dev);
   if (eg != hipSuccess) return hip_fail(eg, "hipGetDevice");
   const int rc = device_setup(dev);
   if (rc != KG_OK) return rc;
+  const int cus = g_dev[dev].cus > 0 ? g_dev[dev].cus : 256;
+  // bf16: halve the tile along M when full tiles would leave most CUs idle
+  const int64_t big_tiles = (int64_t)G * ((M + 255) / 256) * ((N + 255) / 256);
+  const Launch L = pick(kind, fast, kind == BF16 && big_tiles < 2 * (int64_t)cus);
+  const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
+  const int64_t total = (int64_t)G * tiles_m * tiles_n;
+  if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;
 
   Params p;
   p.A = (const unsigned char*)A;
@@ -715,7 +774,6 @@ extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void
   p.gran = dtype == KG_BF16 ? 0 : gran_k;
   p.tiles_m = tiles_m;
   p.tiles_n = tiles_n;
-  const int cus = g_dev[dev].cus > 0 ? g_dev[dev].cus : 256;
   const int grid = (int)(total < cus ? total : cus);
   void* args[] = {&p};
   const hipError_t e = hipLaunchKernel(L.fn, dim3(grid), dim3(kThreads), args,

@@ -82,7 +82,8 @@ typedef enum {
  *
  * Implemented combinations: (KG_E4M3_F32SCALE, 128), (KG_E4M3_UE8M0, 32),
  * (KG_E4M3_UE8M0, 128) and KG_BF16. (KG_E4M3_F32SCALE, 32) returns
- * KG_ERR_UNSUPPORTED. G is limited to 1024 (kg_max_groups).
+ * KG_ERR_UNSUPPORTED. G is limited to 1024 (kg_max_groups), M and N to 2^24, M * N to
+ * 2^30 and K_total to 2^31 - 1 (KG_ERR_UNSUPPORTED beyond).
  *
  * Returns KG_OK after enqueueing, or an error code before enqueueing anything (D
  * untouched). G == 0, M == 0 or N == 0 return KG_OK without a launch. A ks that
