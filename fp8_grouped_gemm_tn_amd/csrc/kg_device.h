@@ -89,6 +89,30 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt
+// and lgkmcnt left at their maxima, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+
+// Wait until at most n (0 <= n <= 31) of this wave's vector-memory operations are
+// outstanding. Loads complete in issue order, so this waits for all but the n
+// most recent ones.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define KG_W(k) \
+  case k:       \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(k)); \
+    break;
+    KG_W(1) KG_W(2) KG_W(3) KG_W(4) KG_W(5) KG_W(6) KG_W(7) KG_W(8) KG_W(9) KG_W(10)
+    KG_W(11) KG_W(12) KG_W(13) KG_W(14) KG_W(15) KG_W(16) KG_W(17) KG_W(18) KG_W(19)
+    KG_W(20) KG_W(21) KG_W(22) KG_W(23) KG_W(24) KG_W(25) KG_W(26) KG_W(27) KG_W(28)
+    KG_W(29) KG_W(30) KG_W(31)
+#undef KG_W
+    default:
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
+
 // Wait for every outstanding vector-memory operation of this wave (including
 // loads into LDS), then barrier the workgroup.
 __device__ __forceinline__ void wait_all_and_barrier() {

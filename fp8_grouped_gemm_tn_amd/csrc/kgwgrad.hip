@@ -71,10 +71,11 @@ struct Params {
 };
 
 // Tile configuration: BM x BN per workgroup, 8 waves as WAVES_M x WAVES_N, TK tokens
-// per LDS stage, ELT bytes per operand element, SCALE_BYTES of scale tile per operand.
-template <int BM_, int BN_, int WAVES_M_, int TK_, int ELT_, int SCALE_BYTES_>
+// per LDS stage, NS stages in the ring, ELT bytes per operand element, SCALE_BYTES of
+// scale tile per operand.
+template <int BM_, int BN_, int WAVES_M_, int TK_, int NS_, int ELT_, int SCALE_BYTES_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, TK = TK_, ELT = ELT_;
+  static constexpr int BM = BM_, BN = BN_, TK = TK_, NS = NS_, ELT = ELT_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = kWaves / WAVES_M_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int NI = WM / 16, NJ = WN / 16;
@@ -99,8 +100,8 @@ struct Cfg {
   static constexpr int EPI_COLS = WAVES_N * 32;
   static constexpr int EPI_STRIDE = EPI_COLS + 4;
   static constexpr int EPI_ROWS =
-      BM * (EPI_STRIDE + EPI_COLS) * 4 <= 2 * STAGE ? BM
-      : (BM / 2) * (EPI_STRIDE + EPI_COLS) * 4 <= 2 * STAGE ? BM / 2 : BM / 4;
+      BM * (EPI_STRIDE + EPI_COLS) * 4 <= NS * STAGE ? BM
+      : (BM / 2) * (EPI_STRIDE + EPI_COLS) * 4 <= NS * STAGE ? BM / 2 : BM / 4;
   static constexpr int EPI_C_OFF = EPI_ROWS * EPI_STRIDE * 4;
   static constexpr int EPI_BYTES = EPI_C_OFF + EPI_ROWS * EPI_COLS * 4;
   static constexpr int EPI_CPR = EPI_COLS / 4;                    // float4 per row
@@ -108,21 +109,23 @@ struct Cfg {
   static constexpr int EPI_LOADS = EPI_ROWS * EPI_CPR / 64;       // wave loads of C
   static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile must be whole sub-tile pairs");
   static_assert(TK * CHA % 64 == 0 && TK * CHB % 64 == 0, "stage must be whole wave loads");
-  static_assert(EPI_BYTES <= 2 * STAGE, "epilogue must fit the stages");
+  static_assert(EPI_BYTES <= NS * STAGE, "epilogue must fit the stages");
+  static_assert(NS >= 2, "at least two stages");
   static_assert(EPI_ROWS * EPI_CPR % kThreads == 0, "epilogue work must split evenly");
   static_assert(EPI_ROWS % WM == 0, "epilogue row blocks hold whole wave rows");
   static_assert(SCALE_BYTES <= 1024, "one wave load per scale tile");
 };
 
-// fp8 with the fp8 MFMA: 256 x 256 per workgroup, 64 x 128 per wave, 128 tokens per stage
-using CfgF8 = Cfg<256, 256, 4, 128, 1, 1024>;
+// fp8 with the fp8 MFMA: 256 x 256 per workgroup, 64 x 128 per wave, two stages of
+// 128 tokens (one MFMA consumes 128 tokens)
+using CfgF8 = Cfg<256, 256, 4, 128, 2, 1, 1024>;
 // fp8 widened to bf16: 256 x 128 per workgroup, 64 x 64 per wave (the widened
-// fragments need the registers a wider wave tile would take)
-using CfgF8h = Cfg<256, 128, 4, 128, 1, 1024>;
-// bf16, same tile, 64 tokens per stage
-using CfgB16 = Cfg<256, 256, 4, 64, 2, 0>;
+// fragments need the registers a wider wave tile would take); two stages of 128
+using CfgF8h = Cfg<256, 128, 4, 128, 2, 1, 1024>;
+// bf16: 256 x 256 per workgroup, two stages of 64 tokens
+using CfgB16 = Cfg<256, 256, 4, 64, 2, 2, 0>;
 // bf16, 128 x 256 per workgroup (64 x 64 per wave) for problems with few tiles
-using CfgB16s = Cfg<128, 256, 2, 64, 2, 0>;
+using CfgB16s = Cfg<128, 256, 2, 64, 2, 2, 0>;
 
 // This lane's global byte offsets for its share of a stage's operand loads,
 // relative to the first loaded byte of the stage (row 0, column m0 or n0); the
@@ -292,9 +295,11 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
   if constexpr (KIND != BF16) {
     // scale tiles: fp32 -> one row of BM (BN) floats; E8M0 -> TK/gran rows of BM (BN) bytes
     constexpr int esz = KIND == F32S ? 4 : 1;
-    const int per = KIND == F32S ? 1 : CF::TK / p.gran;  // scale rows per stage
+    // scale rows per stage: fp32 -> the block's row (blocks of 128 span 128/TK stages);
+    // E8M0 -> TK/gran rows, or the one row of the block when gran > TK
+    const int per = KIND == F32S || p.gran >= CF::TK ? 1 : CF::TK / p.gran;
     const int nb_g = (Kg + p.gran - 1) / p.gran;
-    const int r0 = per * kb;
+    const int r0 = (CF::TK * kb) / p.gran;
     const int nrows = uniform(min(per, nb_g - r0));
     const int64_t r = (int64_t)boff_g + r0;
     if (w == 0) {
@@ -424,12 +429,14 @@ __device__ inline void compute_fast_e8m0(const unsigned char* st, int gran,
 // precise fp8: lane base row 8q + j/2; MFMA kk (tokens 32kk..32kk+31) takes this
 // lane's 8 tokens 32kk+8q..32kk+8q+7 for its row (A) or column (B).
 
-// precise fp8 + fp32 scales: per block, four chained bf16 MFMAs (K = 32 each) give
-// the partial sum of sub-tile (i, jn), which is rescaled on the VALU one sub-tile
-// behind the MFMAs.
-template <class CF>
-__device__ inline void compute_precise_f32s(const unsigned char* st,
-                                            v4f (&acc)[CF::NI][CF::NJ]) {
+// precise fp8 + fp32 scales: a 128-token block spans 128/TK stages. Each stage
+// chains its TK/32 bf16 MFMAs (K = 32 each) onto part[i][jn]; on the block's last
+// stage (PROMOTE) the finished partial sum of sub-tile (i, jn) is rescaled by
+// sa (x) sb on the VALU, one sub-tile behind the MFMAs, and part is cleared.
+template <class CF, bool PROMOTE>
+__device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ],
+                                            v4f (&part)[CF::NI][CF::NJ]) {
+  constexpr int KK = CF::TK / 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
@@ -438,46 +445,47 @@ __device__ inline void compute_precise_f32s(const unsigned char* st,
   const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const float* sSa = (const float*)(st + CF::SA_OFF);
   const float* sSb = (const float*)(st + CF::SB_OFF);
-  v8bf af[CF::NI][4];
+  v8bf af[CF::NI][KK];
 #pragma unroll
   for (int i = 0; i < CF::NI; ++i)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) af[i][kk] = widen8(tr8(aBase + 32 * kk * CF::ROWA + 16 * i), 1.0f);
-  constexpr int S = CF::NI * CF::NJ;
-  v2i rnext[4];
+    for (int kk = 0; kk < KK; ++kk)
+      af[i][kk] = widen8(tr8(aBase + 32 * kk * CF::ROWA + 16 * i), 1.0f);
+  auto rescale = [&](int pi, int pj, const v4f& x) {
+    const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * pi + 4 * q);
+    const float sb = sSb[wn * CF::WN + 16 * pj + j];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
-  v8bf bf[4];
+    for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[r] * sb, x[r], acc[pi][pj][r]);
+  };
+  constexpr int S = CF::NI * CF::NJ;
+  v2i rnext[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+  v8bf bf[KK];
   v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int jn = s / CF::NI, i = s % CF::NI;
     if (i == 0) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
+      for (int kk = 0; kk < KK; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
       if (jn + 1 < CF::NJ) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+        for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
       }
     }
-    v4f part = mfma_bf16(af[i][0], bf[0], v4f{0.f, 0.f, 0.f, 0.f});
-    part = mfma_bf16(af[i][1], bf[1], part);
-    part = mfma_bf16(af[i][2], bf[2], part);
-    part = mfma_bf16(af[i][3], bf[3], part);
-    if (s > 0) {
-      const int pj = (s - 1) / CF::NI, pi = (s - 1) % CF::NI;
-      const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * pi + 4 * q);
-      const float sb = sSb[wn * CF::WN + 16 * pj + j];
+    v4f x = part[i][jn];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[r] * sb, prev[r], acc[pi][pj][r]);
+    for (int kk = 0; kk < KK; ++kk) x = mfma_bf16(af[i][kk], bf[kk], x);
+    if constexpr (PROMOTE) {
+      if (s > 0) rescale((s - 1) % CF::NI, (s - 1) / CF::NI, prev);
+      prev = x;
+      part[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
+    } else {
+      part[i][jn] = x;
     }
-    prev = part;
   }
-  constexpr int li = CF::NI - 1, lj = CF::NJ - 1;
-  const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * li + 4 * q);
-  const float sb = sSb[wn * CF::WN + 16 * lj + j];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) acc[li][lj][r] = fmaf(sa[r] * sb, prev[r], acc[li][lj][r]);
+  if constexpr (PROMOTE) rescale(CF::NI - 1, CF::NJ - 1, prev);
 }
 
 // precise fp8 + E8M0: every fragment is widened with its power-of-two scale
@@ -493,33 +501,34 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
   const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const unsigned char* sSa = st + CF::SA_OFF;
   const unsigned char* sSb = st + CF::SB_OFF;
-  // 32-token block kk uses scale row kk (gran 32) or row 0 (gran 128)
+  // 32-token run kk of the stage uses scale row kk (gran 32) or row 0 (gran 128)
   const int g32 = gran == 32 ? 1 : 0;
-  v8bf af[CF::NI][4];
+  constexpr int KK = CF::TK / 32;
+  v8bf af[CF::NI][KK];
 #pragma unroll
   for (int i = 0; i < CF::NI; ++i)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const float s = e8m0_scale(sSa[g32 * kk * CF::BM + wm * CF::WM + 16 * i + j]);
       af[i][kk] = widen8(tr8(aBase + 32 * kk * CF::ROWA + 16 * i), s);
     }
-  v2i rnext[4];
+  v2i rnext[KK];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
 #pragma unroll
   for (int jn = 0; jn < CF::NJ; ++jn) {
-    v8bf bf[4];
+    v8bf bf[KK];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const float s = e8m0_scale(sSb[g32 * kk * CF::BN + wn * CF::WN + 16 * jn + j]);
       bf[kk] = widen8(rnext[kk], s);
     }
     if (jn + 1 < CF::NJ) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+      for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
     }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i][kk], bf[kk], acc[i][jn]);
   }
@@ -557,18 +566,22 @@ __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][
 }
 
 template <int KIND, bool FAST, class CF>
-__device__ inline void compute_stage(const unsigned char* st, int gran,
-                                     v4f (&acc)[CF::NI][CF::NJ]) {
-  if constexpr (KIND == BF16)
+__device__ inline void compute_stage(const unsigned char* st, int gran, bool promote,
+                                     v4f (&acc)[CF::NI][CF::NJ], v4f (&part)[CF::NI][CF::NJ]) {
+  if constexpr (KIND == BF16) {
     compute_bf16<CF>(st, acc);
-  else if constexpr (KIND == F32S && FAST)
+  } else if constexpr (KIND == F32S && FAST) {
     compute_fast_f32s<CF>(st, acc);
-  else if constexpr (KIND == F32S)
-    compute_precise_f32s<CF>(st, acc);
-  else if constexpr (FAST)
+  } else if constexpr (KIND == F32S) {
+    if (promote)
+      compute_precise_f32s<CF, true>(st, acc, part);
+    else
+      compute_precise_f32s<CF, false>(st, acc, part);
+  } else if constexpr (FAST) {
     compute_fast_e8m0<CF>(st, gran, acc);
-  else
+  } else {
     compute_precise_e8m0<CF>(st, gran, acc);
+  }
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -578,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int64_t wsum_k[kWaves];
   __shared__ int32_t wsum_b[kWaves];
-  Sched s = sched_carve(smem + 2 * CF::STAGE, p.G);
+  Sched s = sched_carve(smem + CF::NS * CF::STAGE, p.G);
   const int gran = KIND == BF16 ? CF::TK : p.gran;
   if (sched_build(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
     if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
@@ -592,6 +605,14 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
   const int b = blockIdx.x;
   const int slot = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
   const LoadOffsets<CF> lo = load_offsets<CF>(p);
+  // vector-memory instructions this wave issues per stage
+  const int w = threadIdx.x >> 6;
+  int my_loads = (KIND != BF16 && w < 2) ? 1 : 0;
+#pragma unroll
+  for (int k = 0; k < CF::SLOTS_A; ++k) my_loads += (w + kWaves * k < CF::LOADS_A) ? 1 : 0;
+#pragma unroll
+  for (int k = 0; k < CF::SLOTS_B; ++k) my_loads += (w + kWaves * k < CF::LOADS_B) ? 1 : 0;
+  my_loads = uniform(my_loads);
 
   for (int base = 0; base < total; base += grid) {
     const int idx = base + slot;
@@ -613,14 +634,35 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
     for (int i = 0; i < CF::NI; ++i)
 #pragma unroll
       for (int jn = 0; jn < CF::NJ; ++jn) acc[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
+    // partial sums of the open 128-token block (used by fp32 scales with TK < 128;
+    // dead and removed by the compiler for the other policies)
+    v4f part[CF::NI][CF::NJ];
+#pragma unroll
+    for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+      for (int jn = 0; jn < CF::NJ; ++jn) part[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    load_stage<KIND, CF>(p, lo, smem, t_begin, Kg, boff_g, 0, m0, n0);
+    // Ring of NS stages: stage kb lives in buffer kb % NS and is loaded NS-1 stages
+    // before it is used. Each wave waits only for its own loads of stage kb (the
+    // later stages' loads may stay in flight), then the barrier makes every wave's
+    // loads visible.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the previous item's stores
+#pragma unroll
+    for (int st0 = 0; st0 < CF::NS - 1; ++st0)
+      if (st0 < nk) load_stage<KIND, CF>(p, lo, smem + st0 * CF::STAGE, t_begin, Kg, boff_g, st0, m0, n0);
+    int buf = 0;  // kb % NS
     for (int kb = 0; kb < nk; ++kb) {
-      wait_all_and_barrier();  // block kb has landed; everyone is done with block kb-1
-      if (kb + 1 < nk)
-        load_stage<KIND, CF>(p, lo, smem + ((kb + 1) & 1) * CF::STAGE, t_begin, Kg, boff_g,
-                             kb + 1, m0, n0);
-      compute_stage<KIND, FAST, CF>(smem + (kb & 1) * CF::STAGE, p.gran, acc);
+      const int ahead = min(CF::NS - 2, nk - 1 - kb);
+      wait_vmcnt(ahead * my_loads);
+      __syncthreads();
+      if (kb + CF::NS - 1 < nk) {
+        const int nb = buf == 0 ? CF::NS - 1 : buf - 1;  // (kb + NS - 1) % NS
+        load_stage<KIND, CF>(p, lo, smem + nb * CF::STAGE, t_begin, Kg, boff_g, kb + CF::NS - 1,
+                             m0, n0);
+      }
+      const bool promote = ((kb + 1) % (128 / CF::TK) == 0) || kb + 1 == nk;
+      compute_stage<KIND, FAST, CF>(smem + buf * CF::STAGE, p.gran, promote, acc, part);
+      buf = buf + 1 == CF::NS ? 0 : buf + 1;
     }
     store_tile<CF>(p, smem, g, m0, n0, acc);
   }
@@ -658,7 +700,7 @@ struct Launch {
 
 template <int KIND, bool FAST, class CF>
 static Launch launch_of() {
-  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF>, 2 * CF::STAGE, CF::BM, CF::BN};
+  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF>, CF::NS * CF::STAGE, CF::BM, CF::BN};
 }
 
 static Launch pick(int kind, bool fast, bool small = false) {
