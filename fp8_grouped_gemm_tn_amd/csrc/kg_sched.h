@@ -16,9 +16,8 @@
 namespace kg {
 
 constexpr int kMaxGroups = 1024;
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kPanelM = 4;  // m-tiles per panel of the tile walk
+constexpr int kMaxWaves = 8;  // largest workgroup: 512 threads
+constexpr int kPanelM = 4;    // m-tiles per panel of the tile walk
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 
@@ -62,21 +61,30 @@ __device__ inline T wave_incl_scan(T v) {
 }
 
 // Block-wide: load ks, check counts, scan offsets, order experts. Returns KG_OK
-// or KG_ERR_KSUM; every thread returns the same value.
+// or KG_ERR_KSUM; every thread returns the same value. THREADS is the block size
+// (256 or 512); each thread owns kMaxGroups / THREADS consecutive experts.
+template <int THREADS>
 __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, Sched s,
                            int64_t* wsum_k, int32_t* wsum_b) {
+  constexpr int E = kMaxGroups / THREADS, W = THREADS / 64;
+  static_assert(E * THREADS == kMaxGroups && W <= kMaxWaves, "block size");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  // each thread owns experts 2t and 2t+1 (G <= 1024)
-  const int g0 = 2 * t, g1 = 2 * t + 1;
-  const int k0 = g0 < G ? ks[g0] : 0;
-  const int k1 = g1 < G ? ks[g1] : 0;
-  const int neg = (k0 < 0) | (k1 < 0);
-  const int b0 = k0 > 0 ? (k0 + gran - 1) / gran : 0;
-  const int b1 = k1 > 0 ? (k1 + gran - 1) / gran : 0;
-  if (g0 < G) s.ks[g0] = k0;
-  if (g1 < G) s.ks[g1] = k1;
-  const int64_t sk = wave_incl_scan<int64_t>((int64_t)k0 + k1);
-  const int32_t sbk = wave_incl_scan<int32_t>(b0 + b1);
+  const int g0 = E * t;
+  int kv[E], bv[E];
+  int neg = 0;
+  int64_t own_k = 0;
+  int32_t own_b = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kv[e] = g0 + e < G ? ks[g0 + e] : 0;
+    neg |= kv[e] < 0;
+    bv[e] = kv[e] > 0 ? (kv[e] + gran - 1) / gran : 0;
+    if (g0 + e < G) s.ks[g0 + e] = kv[e];
+    own_k += kv[e];
+    own_b += bv[e];
+  }
+  const int64_t sk = wave_incl_scan<int64_t>(own_k);
+  const int32_t sbk = wave_incl_scan<int32_t>(own_b);
   if (lane == 63) {
     wsum_k[w] = sk;
     wsum_b[w] = sbk;
@@ -88,37 +96,38 @@ __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, 
     pk += wsum_k[i];
     pb += wsum_b[i];
   }
-  const int64_t ex_k = pk + sk - ((int64_t)k0 + k1);
-  const int32_t ex_b = pb + sbk - (b0 + b1);
-  if (g0 < G) {
-    s.off[g0 + 1] = ex_k + k0;
-    s.boff[g0 + 1] = ex_b + b0;
-  }
-  if (g1 < G) {
-    s.off[g1 + 1] = ex_k + k0 + k1;
-    s.boff[g1 + 1] = ex_b + b0 + b1;
+  int64_t run_k = pk + sk - own_k;
+  int32_t run_b = pb + sbk - own_b;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    run_k += kv[e];
+    run_b += bv[e];
+    if (g0 + e < G) {
+      s.off[g0 + e + 1] = run_k;
+      s.boff[g0 + e + 1] = run_b;
+    }
   }
   if (t == 0) {
     s.off[0] = 0;
     s.boff[0] = 0;
   }
   int64_t total = 0;
-  for (int i = 0; i < kWaves; ++i) total += wsum_k[i];
+  for (int i = 0; i < W; ++i) total += wsum_k[i];
   __syncthreads();
   if (any_neg || total != K_total) return KG_ERR_KSUM;
   // Longest-first order of experts (ties by index) when G is small; identity otherwise.
   if (G <= 256) {
-    if (t < G) {
-      const int kt = s.ks[t];
+    for (int g = t; g < G; g += THREADS) {
+      const int kt = s.ks[g];
       int rank = 0;
       for (int h = 0; h < G; ++h) {
         const int kh = s.ks[h];
-        rank += (kh > kt) | ((kh == kt) & (h < t));
+        rank += (kh > kt) | ((kh == kt) & (h < g));
       }
-      s.order[rank] = (uint16_t)t;
+      s.order[rank] = (uint16_t)g;
     }
   } else {
-    for (int g = t; g < G; g += kThreads) s.order[g] = (uint16_t)g;
+    for (int g = t; g < G; g += THREADS) s.order[g] = (uint16_t)g;
   }
   __syncthreads();
   return KG_OK;

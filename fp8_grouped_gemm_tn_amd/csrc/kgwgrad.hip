@@ -70,13 +70,18 @@ struct Params {
   int tiles_m, tiles_n;
 };
 
-// Tile configuration: BM x BN per workgroup, 8 waves as WAVES_M x WAVES_N, TK tokens
-// per LDS stage, NS stages in the ring, ELT bytes per operand element, SCALE_BYTES of
-// scale tile per operand.
-template <int BM_, int BN_, int WAVES_M_, int TK_, int NS_, int ELT_, int SCALE_BYTES_>
+// Tile configuration: BM x BN per workgroup, THREADS / 64 waves as WAVES_M x WAVES_N,
+// TK tokens per LDS stage, NS stages in the ring, ELT bytes per operand element,
+// SCALE_BYTES of scale tile per operand. PIPE: one 32-token MFMA step per stage, and
+// each wave reads stage kb+1's fragments into registers before it issues stage kb's
+// MFMAs (bf16 only).
+template <int BM_, int BN_, int WAVES_M_, int TK_, int NS_, int ELT_, int SCALE_BYTES_,
+          int THREADS_ = 512, bool PIPE_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, TK = TK_, NS = NS_, ELT = ELT_;
-  static constexpr int WAVES_M = WAVES_M_, WAVES_N = kWaves / WAVES_M_;
+  static constexpr int THREADS = THREADS_, WAVES = THREADS_ / 64;
+  static constexpr bool PIPE = PIPE_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES / WAVES_M_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int NI = WM / 16, NJ = WN / 16;
   // LDS rows: one token each, BM (BN) elements + PAD bytes. With the lane-to-row
@@ -87,9 +92,13 @@ struct Cfg {
   static constexpr int ROWA = BM * ELT + PAD, ROWB = BN * ELT + PAD;
   static constexpr int CHA = ROWA / 16, CHB = ROWB / 16;        // 16-byte chunks per row
   static constexpr int DCA = BM * ELT / 16, DCB = BN * ELT / 16;  // of which data
+  // A stage is LOADS wave loads of 1 KB: LOADS_A of A rows, LOADS_B of B rows and,
+  // with scales, one scale tile per operand. Load k of a stage is issued by wave
+  // k % WAVES, so the first HEAVY waves issue PER + 1 loads and the others PER.
   static constexpr int LOADS_A = TK * CHA / 64, LOADS_B = TK * CHB / 64;
-  static constexpr int SLOTS_A = (LOADS_A + kWaves - 1) / kWaves;  // per wave
-  static constexpr int SLOTS_B = (LOADS_B + kWaves - 1) / kWaves;
+  static constexpr int LOADS = LOADS_A + LOADS_B + (SCALE_BYTES_ > 0 ? 2 : 0);
+  static constexpr int SLOTS = (LOADS + WAVES - 1) / WAVES;  // per wave
+  static constexpr int PER = LOADS / WAVES, HEAVY = LOADS % WAVES;
   static constexpr int OPA = TK * ROWA, OPB = TK * ROWB;
   static constexpr int SCALE_BYTES = SCALE_BYTES_;
   static constexpr int SA_OFF = OPA + OPB, SB_OFF = SA_OFF + SCALE_BYTES;
@@ -105,15 +114,17 @@ struct Cfg {
   static constexpr int EPI_C_OFF = EPI_ROWS * EPI_STRIDE * 4;
   static constexpr int EPI_BYTES = EPI_C_OFF + EPI_ROWS * EPI_COLS * 4;
   static constexpr int EPI_CPR = EPI_COLS / 4;                    // float4 per row
-  static constexpr int EPI_PER = EPI_ROWS * EPI_CPR / kThreads;   // float4 per thread
+  static constexpr int EPI_PER = EPI_ROWS * EPI_CPR / THREADS;    // float4 per thread
   static constexpr int EPI_LOADS = EPI_ROWS * EPI_CPR / 64;       // wave loads of C
   static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile must be whole sub-tile pairs");
   static_assert(TK * CHA % 64 == 0 && TK * CHB % 64 == 0, "stage must be whole wave loads");
   static_assert(EPI_BYTES <= NS * STAGE, "epilogue must fit the stages");
   static_assert(NS >= 2, "at least two stages");
-  static_assert(EPI_ROWS * EPI_CPR % kThreads == 0, "epilogue work must split evenly");
+  static_assert(EPI_ROWS * EPI_CPR % THREADS == 0, "epilogue work must split evenly");
+  static_assert(!PIPE || (TK == 32 && NS >= 3 && ELT == 2), "pipelined stages: bf16, 32 tokens");
   static_assert(EPI_ROWS % WM == 0, "epilogue row blocks hold whole wave rows");
   static_assert(SCALE_BYTES <= 1024, "one wave load per scale tile");
+  static_assert((PER + 1) * (NS - 1) <= 63, "stage loads in flight fit the wait counter");
 };
 
 // fp8 with the fp8 MFMA: 256 x 256 per workgroup, 64 x 128 per wave, two stages of
@@ -122,19 +133,20 @@ using CfgF8 = Cfg<256, 256, 4, 128, 2, 1, 1024>;
 // fp8 widened to bf16: 256 x 128 per workgroup, 64 x 64 per wave (the widened
 // fragments need the registers a wider wave tile would take); two stages of 128
 using CfgF8h = Cfg<256, 128, 4, 128, 2, 1, 1024>;
-// bf16: 256 x 256 per workgroup, two stages of 64 tokens
-using CfgB16 = Cfg<256, 256, 4, 64, 2, 2, 0>;
+// bf16: 256 x 256 per workgroup, 4 waves of 128 x 128, a ring of four 32-token
+// stages with fragments read one stage ahead
+using CfgB16 = Cfg<256, 256, 2, 32, 4, 2, 0, 256, true>;
 // bf16, 128 x 256 per workgroup (64 x 64 per wave) for problems with few tiles
 using CfgB16s = Cfg<128, 256, 2, 64, 2, 2, 0>;
 
-// This lane's global byte offsets for its share of a stage's operand loads,
-// relative to the first loaded byte of the stage (row 0, column m0 or n0); the
-// same for every stage and item of a launch. Padding chunks get an offset past
-// any buffer range, so they load zeros.
+// This lane's global byte offsets for its loads of a stage (slot s: load
+// k = w + WAVES * s), relative to the stage's first byte (row 0, column m0 or n0) of
+// the operand the load belongs to; the same for every stage and item of a launch.
+// Padding chunks get an offset past any buffer range, so they load zeros. Scale
+// loads are addressed per stage.
 template <class CF>
 struct LoadOffsets {
-  uint32_t a[CF::SLOTS_A];
-  uint32_t b[CF::SLOTS_B];
+  uint32_t off[CF::SLOTS];
 };
 
 template <class CF>
@@ -143,18 +155,44 @@ __device__ inline LoadOffsets<CF> load_offsets(const Params& p) {
   const uint32_t eM = p.M * CF::ELT, eN = p.N * CF::ELT;
   LoadOffsets<CF> o;
 #pragma unroll
-  for (int s = 0; s < CF::SLOTS_A; ++s) {
-    const int idx = 64 * (w + kWaves * s) + lane;
-    const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
-    o.a[s] = ch >= CF::DCA ? kOobOffset : row * eM + 16 * ch;
-  }
-#pragma unroll
-  for (int s = 0; s < CF::SLOTS_B; ++s) {
-    const int idx = 64 * (w + kWaves * s) + lane;
-    const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
-    o.b[s] = ch >= CF::DCB ? kOobOffset : row * eN + 16 * ch;
+  for (int s = 0; s < CF::SLOTS; ++s) {
+    const int k = w + CF::WAVES * s;
+    o.off[s] = kOobOffset;
+    if (k < CF::LOADS_A) {
+      const int idx = 64 * k + lane;
+      const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
+      if (ch < CF::DCA) o.off[s] = row * eM + 16 * ch;
+    } else if (k < CF::LOADS_A + CF::LOADS_B) {
+      const int idx = 64 * (k - CF::LOADS_A) + lane;
+      const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
+      if (ch < CF::DCB) o.off[s] = row * eN + 16 * ch;
+    }
   }
   return o;
+}
+
+// Wait until this wave's loads of all but the last n stages it issued are done
+// (0 <= n <= NS - 2): loads complete in issue order, and every stage is PER or
+// PER + 1 loads of this wave.
+template <int PERW, int NS>
+__device__ inline void wait_stages_n(int n) {
+  if (NS > 3 && n >= 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PERW));
+  } else if (n == 1) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PERW));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
+
+template <class CF>
+__device__ inline void wait_stages(int n) {
+  static_assert(CF::NS <= 4, "waits cover at most two stages in flight");
+  const int w = threadIdx.x >> 6;
+  if (CF::HEAVY > 0 && w < CF::HEAVY)
+    wait_stages_n<CF::PER + 1, CF::NS>(n);
+  else
+    wait_stages_n<CF::PER, CF::NS>(n);
 }
 
 // ---------------------------------------------------------------- fill
@@ -165,7 +203,7 @@ __device__ void fill_tile(const Params& p, int g, int m0, int n0) {
   if (p.C == p.D) return;  // in place: D already holds C
   const int t = threadIdx.x;
   constexpr int kCols4 = CF::BN / 4;
-  constexpr int kPer = CF::BM * kCols4 / kThreads;
+  constexpr int kPer = CF::BM * kCols4 / CF::THREADS;
   constexpr int kBatch = kPer < 16 ? kPer : 16;
   static_assert(kPer % kBatch == 0, "fill batches");
   const size_t base = (size_t)g * p.M * p.N;
@@ -174,7 +212,7 @@ __device__ void fill_tile(const Params& p, int g, int m0, int n0) {
     v4f v[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int e = t + kThreads * (b0 + k);
+      const int e = t + CF::THREADS * (b0 + k);
       const int r = e / kCols4, c4 = e - r * kCols4;
       const int m = m0 + r, n = n0 + 4 * c4;
       v[k] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -183,7 +221,7 @@ __device__ void fill_tile(const Params& p, int g, int m0, int n0) {
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int e = t + kThreads * (b0 + k);
+      const int e = t + CF::THREADS * (b0 + k);
       const int r = e / kCols4, c4 = e - r * kCols4;
       const int m = m0 + r, n = n0 + 4 * c4;
       if (m < p.M && n < p.N)
@@ -229,7 +267,7 @@ __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, in
     for (int pc = 0; pc < CF::NJ / 2; ++pc) {
       __syncthreads();  // stage buffers / previous pass no longer read
       if (p.C) {
-        for (int k = w; k < CF::EPI_LOADS; k += kWaves) {
+        for (int k = w; k < CF::EPI_LOADS; k += CF::WAVES) {
           int row, lcol, m, n;
           epi_coords<CF>(64 * k + lane, ph, pc, m0, n0, row, lcol, m, n);
           load16_lds(rc, lds_addr(lds + CF::EPI_C_OFF) + 1024 * k,
@@ -253,7 +291,7 @@ __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, in
 #pragma unroll
       for (int k = 0; k < CF::EPI_PER; ++k) {
         int row, lcol, m, n;
-        epi_coords<CF>(threadIdx.x + kThreads * k, ph, pc, m0, n0, row, lcol, m, n);
+        epi_coords<CF>(threadIdx.x + CF::THREADS * k, ph, pc, m0, n0, row, lcol, m, n);
         if (m < p.M && n < p.N) {
           v4f v = *(const v4f*)(e + row * CF::EPI_STRIDE + lcol);
           if (p.C) v += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
@@ -283,37 +321,31 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
   const v4i rb = make_rsrc(p.B + t0 * eN + n0 * CF::ELT, (uint32_t)(rows * eN - n0 * CF::ELT));
   const uint32_t sA = lds_addr(st), sB = sA + CF::OPA;
 #pragma unroll
-  for (int s = 0; s < CF::SLOTS_A; ++s) {
-    const int k = w + kWaves * s;
-    if (CF::LOADS_A % kWaves == 0 || k < CF::LOADS_A) load16_lds(ra, sA + 1024 * k, lo.a[s]);
-  }
-#pragma unroll
-  for (int s = 0; s < CF::SLOTS_B; ++s) {
-    const int k = w + kWaves * s;
-    if (CF::LOADS_B % kWaves == 0 || k < CF::LOADS_B) load16_lds(rb, sB + 1024 * k, lo.b[s]);
-  }
-  if constexpr (KIND != BF16) {
-    // scale tiles: fp32 -> one row of BM (BN) floats; E8M0 -> TK/gran rows of BM (BN) bytes
-    constexpr int esz = KIND == F32S ? 4 : 1;
-    // scale rows per stage: fp32 -> the block's row (blocks of 128 span 128/TK stages);
-    // E8M0 -> TK/gran rows, or the one row of the block when gran > TK
-    const int per = KIND == F32S || p.gran >= CF::TK ? 1 : CF::TK / p.gran;
-    const int nb_g = (Kg + p.gran - 1) / p.gran;
-    const int r0 = (CF::TK * kb) / p.gran;
-    const int nrows = uniform(min(per, nb_g - r0));
-    const int64_t r = (int64_t)boff_g + r0;
-    if (w == 0) {
-      constexpr int cpr = CF::BM * esz / 16;  // 16-byte chunks per scale row
+  for (int s = 0; s < CF::SLOTS; ++s) {
+    const int k = w + CF::WAVES * s;
+    if (k < CF::LOADS_A) {
+      load16_lds(ra, sA + 1024 * k, lo.off[s]);
+    } else if (k < CF::LOADS_A + CF::LOADS_B) {
+      load16_lds(rb, sB + 1024 * (k - CF::LOADS_A), lo.off[s]);
+    } else if (KIND != BF16 && k < CF::LOADS) {
+      // scale tiles: fp32 -> one row of BM (BN) floats; E8M0 -> TK/gran rows of BM
+      // (BN) bytes. Scale rows per stage: fp32 -> the block's row (blocks of 128
+      // span 128/TK stages); E8M0 -> TK/gran rows, or the one row of the block when
+      // gran > TK.
+      constexpr int esz = KIND == F32S ? 4 : 1;
+      const int per = KIND == F32S || p.gran >= CF::TK ? 1 : CF::TK / p.gran;
+      const int nb_g = (Kg + p.gran - 1) / p.gran;
+      const int r0 = (CF::TK * kb) / p.gran;
+      const int nrows = uniform(min(per, nb_g - r0));
+      const int64_t r = (int64_t)boff_g + r0;
+      const bool is_a = k == CF::LOADS_A + CF::LOADS_B;
+      const int ext = is_a ? p.M : p.N, c0 = is_a ? m0 : n0;
+      const int width = is_a ? CF::BM : CF::BN;
+      const int cpr = width * esz / 16;  // 16-byte chunks per scale row
       const int sr = lane / cpr, c = lane - sr * cpr;
-      const v4i rs = make_rsrc(p.sa + r * p.M * esz, (uint32_t)(nrows * p.M * esz));
-      load16_lds(rs, sA + CF::SA_OFF,
-                 sr < per ? (uint32_t)(sr * p.M * esz + m0 * esz + 16 * c) : kOobOffset);
-    } else if (w == 1) {
-      constexpr int cpr = CF::BN * esz / 16;
-      const int sr = lane / cpr, c = lane - sr * cpr;
-      const v4i rs = make_rsrc(p.sb + r * p.N * esz, (uint32_t)(nrows * p.N * esz));
-      load16_lds(rs, sA + CF::SB_OFF,
-                 sr < per ? (uint32_t)(sr * p.N * esz + n0 * esz + 16 * c) : kOobOffset);
+      const v4i rs = make_rsrc((is_a ? p.sa : p.sb) + r * ext * esz, (uint32_t)(nrows * ext * esz));
+      load16_lds(rs, sA + (is_a ? CF::SA_OFF : CF::SB_OFF),
+                 sr < per ? (uint32_t)(sr * ext * esz + c0 * esz + 16 * c) : kOobOffset);
     }
   }
 }
@@ -565,6 +597,33 @@ __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][
   }
 }
 
+// bf16, pipelined stages of 32 tokens (same lane-to-token map as compute_bf16):
+// this lane's byte offsets of its A and B fragments within a stage, and the
+// fragment readers.
+template <class CF>
+struct PipeBase {
+  uint32_t a, b;
+};
+
+template <class CF>
+__device__ inline PipeBase<CF> pipe_base() {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  const int lrow = 4 * q + (j >> 2);
+  PipeBase<CF> pb;
+  pb.a = lrow * CF::ROWA + 8 * (j & 3) + 2 * (wm * CF::WM);
+  pb.b = CF::OPA + lrow * CF::ROWB + 8 * (j & 3) + 2 * (wn * CF::WN);
+  return pb;
+}
+
+template <int ROW>
+__device__ inline v8bf frag_b16(const unsigned char* p) {
+  const v4bf x0 = tr16(p);
+  const v4bf x1 = tr16(p + 16 * ROW);
+  return v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+
 template <int KIND, bool FAST, class CF>
 __device__ inline void compute_stage(const unsigned char* st, int gran, bool promote,
                                      v4f (&acc)[CF::NI][CF::NJ], v4f (&part)[CF::NI][CF::NJ]) {
@@ -587,13 +646,13 @@ __device__ inline void compute_stage(const unsigned char* st, int gran, bool pro
 // ---------------------------------------------------------------- the kernel
 
 template <int KIND, bool FAST, class CF>
-__global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
+__global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int64_t wsum_k[kWaves];
-  __shared__ int32_t wsum_b[kWaves];
+  __shared__ int64_t wsum_k[kMaxWaves];
+  __shared__ int32_t wsum_b[kMaxWaves];
   Sched s = sched_carve(smem + CF::NS * CF::STAGE, p.G);
   const int gran = KIND == BF16 ? CF::TK : p.gran;
-  if (sched_build(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
+  if (sched_build<CF::THREADS>(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
     if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
     return;
   }
@@ -605,14 +664,6 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
   const int b = blockIdx.x;
   const int slot = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
   const LoadOffsets<CF> lo = load_offsets<CF>(p);
-  // vector-memory instructions this wave issues per stage
-  const int w = threadIdx.x >> 6;
-  int my_loads = (KIND != BF16 && w < 2) ? 1 : 0;
-#pragma unroll
-  for (int k = 0; k < CF::SLOTS_A; ++k) my_loads += (w + kWaves * k < CF::LOADS_A) ? 1 : 0;
-#pragma unroll
-  for (int k = 0; k < CF::SLOTS_B; ++k) my_loads += (w + kWaves * k < CF::LOADS_B) ? 1 : 0;
-  my_loads = uniform(my_loads);
 
   for (int base = 0; base < total; base += grid) {
     const int idx = base + slot;
@@ -650,10 +701,53 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
 #pragma unroll
     for (int st0 = 0; st0 < CF::NS - 1; ++st0)
       if (st0 < nk) load_stage<KIND, CF>(p, lo, smem + st0 * CF::STAGE, t_begin, Kg, boff_g, st0, m0, n0);
+    if constexpr (CF::PIPE) {
+      // Stage kb's A fragments and its first B fragment are in registers (or in
+      // flight) when step kb starts. The step waits for stage kb+1, issues the load
+      // of stage kb+NS-1 into the buffer of stage kb-1 (every wave has consumed that
+      // stage's fragments before this step's barrier), then runs stage kb's MFMAs
+      // column by column, reading the next B fragment and one A fragment of stage
+      // kb+1 ahead of each column.
+      static_assert(CF::NI <= CF::NJ, "one A fragment of the next stage per column");
+      const PipeBase<CF> pb = pipe_base<CF>();
+      wait_stages<CF>(min(CF::NS - 2, nk - 1));
+      __syncthreads();
+      v8bf af[CF::NI];
+#pragma unroll
+      for (int i = 0; i < CF::NI; ++i) af[i] = frag_b16<CF::ROWA>(smem + pb.a + 32 * i);
+      v8bf bq = frag_b16<CF::ROWB>(smem + pb.b);
+      for (int kb = 0; kb < nk; ++kb) {
+        if (kb + 1 < nk) {
+          wait_stages<CF>(min(CF::NS - 3, nk - 2 - kb));
+          __syncthreads();
+          if (kb + CF::NS - 1 < nk)
+            load_stage<KIND, CF>(p, lo, smem + ((kb + CF::NS - 1) % CF::NS) * CF::STAGE, t_begin,
+                                 Kg, boff_g, kb + CF::NS - 1, m0, n0);
+        }
+        const unsigned char* cur = smem + (kb % CF::NS) * CF::STAGE;
+        const unsigned char* nxt = smem + ((kb + 1) % CF::NS) * CF::STAGE;
+        // (on the last step the reads of "stage kb+1" fetch stale data from a valid
+        // buffer and are never used; reading anyway keeps the MFMA loop branch-free)
+        v8bf an[CF::NI];
+#pragma unroll
+        for (int jn = 0; jn < CF::NJ; ++jn) {
+          const v8bf bn = jn + 1 < CF::NJ ? frag_b16<CF::ROWB>(cur + pb.b + 32 * (jn + 1))
+                                          : frag_b16<CF::ROWB>(nxt + pb.b);
+          if (jn < CF::NI) an[jn] = frag_b16<CF::ROWA>(nxt + pb.a + 32 * jn);
+#pragma unroll
+          for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i], bq, acc[i][jn]);
+          bq = bn;
+        }
+#pragma unroll
+        for (int i = 0; i < CF::NI; ++i) af[i] = an[i];
+      }
+      store_tile<CF>(p, smem, g, m0, n0, acc);
+      continue;
+    }
     int buf = 0;  // kb % NS
     for (int kb = 0; kb < nk; ++kb) {
       const int ahead = min(CF::NS - 2, nk - 1 - kb);
-      wait_vmcnt(ahead * my_loads);
+      wait_stages<CF>(ahead);
       __syncthreads();
       if (kb + CF::NS - 1 < nk) {
         const int nb = buf == 0 ? CF::NS - 1 : buf - 1;  // (kb + NS - 1) % NS
@@ -669,15 +763,17 @@ __global__ __launch_bounds__(kThreads, 1) void kg_wgrad_kernel(Params p) {
 }
 
 // Same scan as the main kernel, written out for tests.
-__global__ __launch_bounds__(kThreads, 1) void kg_offsets_kernel(const int32_t* ks, int G, int gran,
-                                                                 int64_t* off, int32_t* boff) {
+constexpr int kOffThreads = 512;
+__global__ __launch_bounds__(kOffThreads, 1) void kg_offsets_kernel(const int32_t* ks, int G,
+                                                                    int gran, int64_t* off,
+                                                                    int32_t* boff) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int64_t wsum_k[kWaves];
-  __shared__ int32_t wsum_b[kWaves];
+  __shared__ int64_t wsum_k[kMaxWaves];
+  __shared__ int32_t wsum_b[kMaxWaves];
   Sched s = sched_carve(smem, G);
   // K_total is not known here: the sum check fails, the scans are still written
-  sched_build(ks, G, gran, -1, s, wsum_k, wsum_b);
-  for (int g = threadIdx.x; g <= G; g += kThreads) {
+  sched_build<kOffThreads>(ks, G, gran, -1, s, wsum_k, wsum_b);
+  for (int g = threadIdx.x; g <= G; g += kOffThreads) {
     off[g] = s.off[g];
     boff[g] = s.boff[g];
   }
@@ -694,13 +790,14 @@ static int hip_fail(hipError_t e, const char* what) {
 
 struct Launch {
   const void* fn;
-  int stage_bytes;  // both stages
-  int bm, bn;
+  int stage_bytes;  // all stages
+  int bm, bn, threads;
 };
 
 template <int KIND, bool FAST, class CF>
 static Launch launch_of() {
-  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF>, CF::NS * CF::STAGE, CF::BM, CF::BN};
+  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF>, CF::NS * CF::STAGE, CF::BM, CF::BN,
+                CF::THREADS};
 }
 
 static Launch pick(int kind, bool fast, bool small = false) {
@@ -818,7 +915,7 @@ extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void
   p.tiles_n = tiles_n;
   const int grid = (int)(total < cus ? total : cus);
   void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel(L.fn, dim3(grid), dim3(kThreads), args,
+  const hipError_t e = hipLaunchKernel(L.fn, dim3(grid), dim3(L.threads), args,
                                        L.stage_bytes + sched_bytes(G), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return KG_OK;
@@ -844,7 +941,7 @@ extern "C" int kg_debug_offsets(const int32_t* ks, int G, int gran_k, int64_t* o
   if (G < 0 || G > kMaxGroups) return KG_ERR_SHAPE;
   if (gran_k <= 0) return KG_ERR_GRAN;
   if (off == nullptr || boff == nullptr || (G > 0 && ks == nullptr)) return KG_ERR_NULL;
-  hipLaunchKernelGGL(kg_offsets_kernel, dim3(1), dim3(kThreads), sched_bytes(G),
+  hipLaunchKernelGGL(kg_offsets_kernel, dim3(1), dim3(kOffThreads), sched_bytes(G),
                      (hipStream_t)stream, ks, G, gran_k, off, boff);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

@@ -165,6 +165,22 @@ def test_fast_fp8_mfma_mode(dtype, gran, with_c):
         assert torch.equal(D[g].cpu().view(torch.int32), case.C[g].view(torch.int32))
 
 
+def test_bf16_many_tiles_large_tile_config():
+    # enough 256 x 256 tiles (G * 1 * 1 >= 2 per CU) that the bf16 path takes its
+    # full-size tile configuration; ragged and empty experts throughout
+    say("bf16 many tiles")
+    rng = np.random.default_rng(14)
+    ks = rng.integers(0, 97, 600).astype(np.int32)
+    ks[rng.choice(600, 60, replace=False)] = 0
+    case = small_case(BF, 128, ks, 256, 256, seed=14)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "bf16 many tiles")
+    for g in np.nonzero(ks == 0)[0]:
+        assert torch.equal(D[g].cpu().view(torch.int32), case.C[g].view(torch.int32))
+
+
 @pytest.mark.parametrize("dtype,gran", [(F32, 128), (BF, 128)])
 def test_in_place_accumulate(dtype, gran):
     say("in place", dtype)
