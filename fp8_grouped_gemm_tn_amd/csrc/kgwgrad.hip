@@ -133,9 +133,10 @@ using CfgF8 = Cfg<256, 256, 4, 128, 2, 1, 1024>;
 // fp8 widened to bf16: 256 x 128 per workgroup, 64 x 64 per wave (the widened
 // fragments need the registers a wider wave tile would take); two stages of 128
 using CfgF8h = Cfg<256, 128, 4, 128, 2, 1, 1024>;
-// bf16: 256 x 256 per workgroup, 4 waves of 128 x 128, a ring of four 32-token
-// stages with fragments read one stage ahead
-using CfgB16 = Cfg<256, 256, 2, 32, 4, 2, 0, 256, true>;
+// bf16: 256 x 256 per workgroup, 8 waves of 64 x 128 (two per SIMD), a ring of four
+// 32-token stages; each wave reads stage kb+1's fragments while it runs stage kb's
+// MFMAs
+using CfgB16 = Cfg<256, 256, 4, 32, 4, 2, 0, 512, true>;
 // bf16, 128 x 256 per workgroup (64 x 64 per wave) for problems with few tiles
 using CfgB16s = Cfg<128, 256, 2, 64, 2, 2, 0>;
 
@@ -310,7 +311,8 @@ __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, in
 template <int KIND, class CF>
 __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, unsigned char* st,
                                   int64_t t_begin, int Kg, int boff_g, int kb, int m0, int n0) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index is uniform: the slot tests below become scalar selects
+  const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
   const int rows = uniform(min(CF::TK, Kg - CF::TK * kb));
   const int64_t t0 = t_begin + (int64_t)CF::TK * kb;
   const int eM = p.M * CF::ELT, eN = p.N * CF::ELT;
@@ -323,10 +325,11 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
 #pragma unroll
   for (int s = 0; s < CF::SLOTS; ++s) {
     const int k = w + CF::WAVES * s;
-    if (k < CF::LOADS_A) {
-      load16_lds(ra, sA + 1024 * k, lo.off[s]);
-    } else if (k < CF::LOADS_A + CF::LOADS_B) {
-      load16_lds(rb, sB + 1024 * (k - CF::LOADS_A), lo.off[s]);
+    if (k < CF::LOADS_A + CF::LOADS_B) {
+      // one load instruction per slot; the operand (resource and LDS base) is a
+      // scalar select, not a branch
+      const bool is_a = k < CF::LOADS_A;
+      load16_lds(is_a ? ra : rb, is_a ? sA + 1024 * k : sB + 1024 * (k - CF::LOADS_A), lo.off[s]);
     } else if (KIND != BF16 && k < CF::LOADS) {
       // scale tiles: fp32 -> one row of BM (BN) floats; E8M0 -> TK/gran rows of BM
       // (BN) bytes. Scale rows per stage: fp32 -> the block's row (blocks of 128
@@ -702,45 +705,66 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
     for (int st0 = 0; st0 < CF::NS - 1; ++st0)
       if (st0 < nk) load_stage<KIND, CF>(p, lo, smem + st0 * CF::STAGE, t_begin, Kg, boff_g, st0, m0, n0);
     if constexpr (CF::PIPE) {
-      // Stage kb's A fragments and its first B fragment are in registers (or in
-      // flight) when step kb starts. The step waits for stage kb+1, issues the load
-      // of stage kb+NS-1 into the buffer of stage kb-1 (every wave has consumed that
-      // stage's fragments before this step's barrier), then runs stage kb's MFMAs
-      // column by column, reading the next B fragment and one A fragment of stage
-      // kb+1 ahead of each column.
-      static_assert(CF::NI <= CF::NJ, "one A fragment of the next stage per column");
+      // Ring of NS buffers. Stage kb's fragments are read into registers during
+      // step kb-1, so at the top of step kb (after the barrier) buffer kb % NS is
+      // free and receives stage kb + NS.
       const PipeBase<CF> pb = pipe_base<CF>();
       wait_stages<CF>(min(CF::NS - 2, nk - 1));
       __syncthreads();
-      v8bf af[CF::NI];
+      if (CF::NS - 1 < nk)
+        load_stage<KIND, CF>(p, lo, smem + (CF::NS - 1) * CF::STAGE, t_begin, Kg, boff_g,
+                             CF::NS - 1, m0, n0);
+      // fragment halves: [2i] tokens 4q..4q+3, [2i+1] tokens 16+4q..16+4q+3
+      v4bf xa[2 * CF::NI], xb[2 * CF::NJ], ya[2 * CF::NI], yb[2 * CF::NJ];
 #pragma unroll
-      for (int i = 0; i < CF::NI; ++i) af[i] = frag_b16<CF::ROWA>(smem + pb.a + 32 * i);
-      v8bf bq = frag_b16<CF::ROWB>(smem + pb.b);
-      for (int kb = 0; kb < nk; ++kb) {
-        if (kb + 1 < nk) {
-          wait_stages<CF>(min(CF::NS - 3, nk - 2 - kb));
-          __syncthreads();
-          if (kb + CF::NS - 1 < nk)
-            load_stage<KIND, CF>(p, lo, smem + ((kb + CF::NS - 1) % CF::NS) * CF::STAGE, t_begin,
-                                 Kg, boff_g, kb + CF::NS - 1, m0, n0);
-        }
-        const unsigned char* cur = smem + (kb % CF::NS) * CF::STAGE;
-        const unsigned char* nxt = smem + ((kb + 1) % CF::NS) * CF::STAGE;
-        // (on the last step the reads of "stage kb+1" fetch stale data from a valid
-        // buffer and are never used; reading anyway keeps the MFMA loop branch-free)
-        v8bf an[CF::NI];
-#pragma unroll
-        for (int jn = 0; jn < CF::NJ; ++jn) {
-          const v8bf bn = jn + 1 < CF::NJ ? frag_b16<CF::ROWB>(cur + pb.b + 32 * (jn + 1))
-                                          : frag_b16<CF::ROWB>(nxt + pb.b);
-          if (jn < CF::NI) an[jn] = frag_b16<CF::ROWA>(nxt + pb.a + 32 * jn);
-#pragma unroll
-          for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i], bq, acc[i][jn]);
-          bq = bn;
-        }
-#pragma unroll
-        for (int i = 0; i < CF::NI; ++i) af[i] = an[i];
+      for (int i = 0; i < CF::NI; ++i) {
+        xa[2 * i] = tr16(smem + pb.a + 32 * i);
+        xa[2 * i + 1] = tr16(smem + pb.a + 32 * i + 16 * CF::ROWA);
       }
+#pragma unroll
+      for (int jn = 0; jn < CF::NJ; ++jn) {
+        xb[2 * jn] = tr16(smem + pb.b + 32 * jn);
+        xb[2 * jn + 1] = tr16(smem + pb.b + 32 * jn + 16 * CF::ROWB);
+      }
+      // Step kb: wait for stage kb+1 and barrier, refill the freed buffer, then the
+      // stage's MFMAs from (ca, cb) with the reads of stage kb+1 into (na, nb) spread
+      // between them. On the last step the reads fetch a stale but valid buffer and
+      // are never used.
+      auto step = [&](int kb, v4bf (&ca)[2 * CF::NI], v4bf (&cb)[2 * CF::NJ],
+                      v4bf (&na)[2 * CF::NI], v4bf (&nb)[2 * CF::NJ]) {
+        if (kb + 1 < nk) {
+          wait_stages<CF>(min(CF::NS - 2, nk - 2 - kb));
+          __syncthreads();
+          if (kb + CF::NS < nk)
+            load_stage<KIND, CF>(p, lo, smem + (kb % CF::NS) * CF::STAGE, t_begin, Kg, boff_g,
+                                 kb + CF::NS, m0, n0);
+        }
+        const unsigned char* nxt = smem + ((kb + 1) % CF::NS) * CF::STAGE;
+        constexpr int R = 2 * (CF::NI + CF::NJ);  // reads of the next stage
+        constexpr int S = CF::NI * CF::NJ;        // MFMAs of this stage
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int jn = s / CF::NI, i = s % CF::NI;
+          const v8bf a = __builtin_shufflevector(ca[2 * i], ca[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const v8bf b = __builtin_shufflevector(cb[2 * jn], cb[2 * jn + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[i][jn] = mfma_bf16(a, b, acc[i][jn]);
+#pragma unroll
+          for (int r = (s * R + S - 1) / S; r < ((s + 1) * R + S - 1) / S; ++r) {
+            if (r < 2 * CF::NI)
+              na[r] = tr16(nxt + pb.a + 32 * (r / 2) + 16 * CF::ROWA * (r % 2));
+            else
+              nb[r - 2 * CF::NI] = tr16(nxt + pb.b + 32 * ((r - 2 * CF::NI) / 2) +
+                                        16 * CF::ROWB * (r % 2));
+          }
+        }
+      };
+      // two steps per trip so that the register sets swap roles without copies
+      int kb = 0;
+      for (; kb + 1 < nk; kb += 2) {
+        step(kb, xa, xb, ya, yb);
+        step(kb + 1, ya, yb, xa, xb);
+      }
+      if (kb < nk) step(kb, xa, xb, ya, yb);
       store_tile<CF>(p, smem, g, m0, n0, acc);
       continue;
     }
