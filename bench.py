@@ -145,6 +145,8 @@ def main():
     ap.add_argument("--workload", default="bf16", choices=list(DESCR))
     ap.add_argument("--fast", action="store_true", help="fp8 kinds: contract with the fp8 MFMA")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="call kg_wgrad without a workspace (no stream-K split of small problems)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run one plain 1 GiB device copy (untimed), so that a counter "
@@ -181,9 +183,13 @@ def main():
     D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev)
     flags = kg.KG_FLAG_FP8_MFMA if (args.fast and case.dtype != kg.KG_BF16) else 0
     dtype = case.dtype | flags
+    # the library's workspace (zeroed once, left zeroed by every call), allocated
+    # before the timed region; it lets small bf16 problems spread over every CU
+    ws = None if args.no_workspace else kg.new_workspace(dev)
 
     def step():
-        kg.kg_wgrad(A, sa, B, sb, C, D, ks, case.gran_k, dtype, K_total=case.K_total)
+        kg.kg_wgrad(A, sa, B, sb, C, D, ks, case.gran_k, dtype, K_total=case.K_total,
+                    workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -243,7 +249,7 @@ def main():
         "data": "synthetic (seeded generators, fp8 values quantised per 128/32-token block)",
         "config": {"workload": DESCR[args.workload], "G": case.G, "M": case.M, "N": case.N,
                    "tokens": case.K_total, "gran_k": case.gran_k if not is_bf16 else None,
-                   "fp8_mfma": bool(flags)},
+                   "fp8_mfma": bool(flags), "workspace": ws is not None},
         "roofline": roof,
         "pct_fp8_peak": round(100.0 * value / PEAK["fp8"], 2),
         "hbm_gbs": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),

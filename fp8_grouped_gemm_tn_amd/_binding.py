@@ -15,15 +15,21 @@ KG_FLAG_FP8_MFMA = 0x100
 KG_OK = 0
 KG_ERR_NULL, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_DTYPE = -1, -2, -3, -4
 KG_ERR_ALIGN, KG_ERR_ALIAS, KG_ERR_UNSUPPORTED, KG_ERR_HIP, KG_ERR_KSUM = -5, -6, -7, -8, -9
+KG_ERR_SPLIT = -10
 ERROR_NAMES = {0: "KG_OK", -1: "KG_ERR_NULL", -2: "KG_ERR_SHAPE", -3: "KG_ERR_GRAN",
                -4: "KG_ERR_DTYPE", -5: "KG_ERR_ALIGN", -6: "KG_ERR_ALIAS",
-               -7: "KG_ERR_UNSUPPORTED", -8: "KG_ERR_HIP", -9: "KG_ERR_KSUM"}
+               -7: "KG_ERR_UNSUPPORTED", -8: "KG_ERR_HIP", -9: "KG_ERR_KSUM",
+               -10: "KG_ERR_SPLIT"}
 
 # name -> (restype, argtypes): the symbols include/kgwgrad.h declares
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
 SIGNATURES = {
     "kg_wgrad": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32,
                         _vp]),
+    "kg_wgrad_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32,
+                           _vp, _i64, _vp]),
+    "kg_wgrad_workspace_bytes": (_i64, []),
+    "kg_wgrad_workspace_flag_bytes": (_i64, []),
     "kg_status": (_i32, [_vp]),
     "kg_debug_offsets": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "kg_max_groups": (_i32, []),
@@ -72,13 +78,46 @@ def kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream
                           _stream(stream))
 
 
-def kg_wgrad(A, sa, B, sb, C, D, ks, gran_k, dtype, K_total=None, stream=None):
+def kg_wgrad_ws_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, ws, ws_bytes,
+                    stream=None):
+    """Call kg_wgrad_ws with torch device tensors (or None); returns the status code."""
+    return lib().kg_wgrad_ws(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D), _ptr(ks),
+                             int(G), int(M), int(N), int(K_total), int(gran_k), int(dtype),
+                             _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def kg_wgrad_workspace_bytes():
+    n = lib().kg_wgrad_workspace_bytes()
+    if n < 0:
+        raise KgError(KG_ERR_HIP, "kg_wgrad_workspace_bytes")
+    return n
+
+
+def kg_wgrad_workspace_flag_bytes():
+    n = lib().kg_wgrad_workspace_flag_bytes()
+    if n < 0:
+        raise KgError(KG_ERR_HIP, "kg_wgrad_workspace_flag_bytes")
+    return n
+
+
+def new_workspace(device=None):
+    """A zeroed workspace tensor for kg_wgrad(..., workspace=...) on `device`."""
+    import torch
+    return torch.zeros(kg_wgrad_workspace_bytes(), dtype=torch.uint8, device=device or "cuda")
+
+
+def kg_wgrad(A, sa, B, sb, C, D, ks, gran_k, dtype, K_total=None, stream=None, workspace=None):
     """D = C + K-grouped A^T B. Shapes are read from the tensors:
-    A [K_total, M], B [K_total, N], D [G, M, N], ks [G] int32 (all on the GPU)."""
+    A [K_total, M], B [K_total, N], D [G, M, N], ks [G] int32 (all on the GPU).
+    `workspace` (from new_workspace) lets small bf16 problems use every CU."""
     G, M, N = D.shape
     if K_total is None:
         K_total = A.shape[0]
-    rc = kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream)
+    if workspace is None:
+        rc = kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream)
+    else:
+        rc = kg_wgrad_ws_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, workspace,
+                             workspace.numel() * workspace.element_size(), stream)
     if rc != KG_OK:
         raise KgError(rc, "kg_wgrad")
     return D

@@ -65,6 +65,25 @@ __device__ __forceinline__ void load16_lds(v4i r, uint32_t lds, uint32_t voff) {
                : "memory", "m0");
 }
 
+// load16_lds that reads around the L2 (sc0 sc1): sees data that other XCDs wrote
+// with store16_sys without any cache-wide invalidation.
+__device__ __forceinline__ void load16_lds_sys(v4i r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen sc0 sc1 lds"
+               :
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane((int)lds))
+               : "memory", "m0");
+}
+
+// 16-byte store at byte `voff` of [base, base + bytes), written through to memory
+// (cache policy sc0 sc1): visible to every XCD once this wave's vmcnt reaches zero,
+// without a cache-wide write-back.
+__device__ __forceinline__ void store16_sys(void* base, uint32_t bytes, uint32_t voff, v4f v) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kRsrcWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)voff, 0,
+                                         /* sc0 | sc1 */ 1 | 16);
+}
+
 __device__ __forceinline__ v2i tr8(const unsigned char* lds) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((KG_LDS v2i*)lds);
 }

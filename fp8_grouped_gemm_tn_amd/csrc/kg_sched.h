@@ -16,6 +16,7 @@
 namespace kg {
 
 constexpr int kMaxGroups = 1024;
+constexpr int kMaxSplitGroups = 64;  // largest G that runs in stream-K mode
 constexpr int kMaxWaves = 8;  // largest workgroup: 512 threads
 constexpr int kPanelM = 4;    // m-tiles per panel of the tile walk
 

@@ -68,6 +68,9 @@ struct Params {
   int64_t K_total;
   int gran;  // tokens per scale row
   int tiles_m, tiles_n;
+  // stream-K mode when ws != nullptr: per-workgroup partial tiles and ready flags
+  float* ws;
+  int* wsflag;
 };
 
 // Tile configuration: BM x BN per workgroup, THREADS / 64 waves as WAVES_M x WAVES_N,
@@ -243,6 +246,105 @@ __device__ inline void epi_coords(int idx, int ph, int pc, int m0, int n0, int& 
   lcol = 4 * c4;
   m = m0 + ph * CF::EPI_ROWS + row;
   n = n0 + strip * CF::WN + 32 * pc + 4 * (c4 & 7);
+}
+
+// Stream-K epilogue of one tile: acc (this lane's 4 rows x 1 column of each 16x16 sub-tile),
+// plus an optional addend tile `add` (C), plus `nparts` partial tiles (stream-K),
+// added in that order, stored to `dst`. Tiles are row-major from the tile origin:
+// dst and add with row stride `ld` floats (rows and columns past rows x cols are
+// not stored; addend bytes past add_bytes read as zero), partial q at parts + q *
+// BM * BN with row stride BN. Per pass (EPI_ROWS rows x two 16-column sub-tiles of
+// every wave column): the waves owning the pass's rows write their accumulators to
+// LDS while the addend goes global -> LDS by buffer loads; every thread adds the
+// addend to its float4 runs, then each partial in turn through the same LDS
+// buffer, and stores whole float4 runs along N, non-temporally.
+template <class CF, bool SYS_STORE = false>
+__device__ inline void store_tile_gen(unsigned char* lds, const v4f (&acc)[CF::NI][CF::NJ],
+                                      float* dst, int ld, int rows, int cols, const float* add,
+                                      uint32_t add_bytes, const float* parts, int nparts) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  float* e = (float*)lds;
+  const float* cl = (const float*)(lds + CF::EPI_C_OFF);
+  const uint32_t cl_lds = lds_addr(lds + CF::EPI_C_OFF);
+  const v4i rc = make_rsrc(add, add_bytes);
+  constexpr int kPH = CF::BM / CF::EPI_ROWS;
+#pragma unroll
+  for (int ph = 0; ph < kPH; ++ph) {
+#pragma unroll
+    for (int pc = 0; pc < CF::NJ / 2; ++pc) {
+      __syncthreads();  // stage buffers / previous pass no longer read
+      if (add) {
+        for (int k = w; k < CF::EPI_LOADS; k += CF::WAVES) {
+          int row, lcol, m, n;
+          epi_coords<CF>(64 * k + lane, ph, pc, 0, 0, row, lcol, m, n);
+          load16_lds(rc, cl_lds + 1024 * k, (uint32_t)((m * ld + n) * 4));
+        }
+      }
+      const int wrow0 = wm * CF::WM - ph * CF::EPI_ROWS;  // this wave's first row in the pass
+      if (wrow0 >= 0 && wrow0 < CF::EPI_ROWS) {
+#pragma unroll
+        for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = wrow0 + 16 * i + 4 * q + r;
+              const int col = wn * 32 + 16 * jj + j;
+              e[row * CF::EPI_STRIDE + col] = acc[i][2 * pc + jj][r];
+            }
+      }
+      wait_all_and_barrier();  // accumulators and addend of this pass are in LDS
+      // partial tiles: every thread adds each one, in order, to its own float4 runs
+      // of the staged sums (LDS read-modify-write; no cross-thread hazards)
+      for (int pq = 0; pq < nparts; ++pq) {
+        if (add || pq > 0) {
+#pragma unroll
+          for (int k = 0; k < CF::EPI_PER; ++k) {
+            int row, lcol, m, n;
+            epi_coords<CF>(threadIdx.x + CF::THREADS * k, ph, pc, 0, 0, row, lcol, m, n);
+            *(v4f*)(e + row * CF::EPI_STRIDE + lcol) += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
+          }
+        }
+        const v4i rp = make_rsrc(parts + (size_t)pq * CF::BM * CF::BN, CF::BM * CF::BN * 4);
+        __syncthreads();  // the previous addend in LDS is no longer read
+        for (int k = w; k < CF::EPI_LOADS; k += CF::WAVES) {
+          int row, lcol, m, n;
+          epi_coords<CF>(64 * k + lane, ph, pc, 0, 0, row, lcol, m, n);
+          load16_lds_sys(rp, cl_lds + 1024 * k, (uint32_t)((m * CF::BN + n) * 4));
+        }
+        wait_all_and_barrier();
+      }
+      // the LDS addend buffer holds C (no partials) or the last partial
+      const bool addl = add != nullptr || nparts > 0;
+#pragma unroll
+      for (int k = 0; k < CF::EPI_PER; ++k) {
+        int row, lcol, m, n;
+        epi_coords<CF>(threadIdx.x + CF::THREADS * k, ph, pc, 0, 0, row, lcol, m, n);
+        if (m < rows && n < cols) {
+          v4f v = *(const v4f*)(e + row * CF::EPI_STRIDE + lcol);
+          if (addl) v += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
+          if constexpr (SYS_STORE)
+            store16_sys(dst, (uint32_t)((size_t)rows * ld * 4), (uint32_t)((m * ld + n) * 4), v);
+          else
+            __builtin_nontemporal_store(v, (v4f*)(dst + (size_t)m * ld + n));
+        }
+      }
+    }
+  }
+}
+
+// acc + C + partial tiles -> D for expert g's tile at (m0, n0) (stream-K mode).
+template <class CF>
+__device__ inline void store_tile_parts(const Params& p, unsigned char* lds, int g, int m0, int n0,
+                                        const v4f (&acc)[CF::NI][CF::NJ], const float* parts,
+                                        int nparts) {
+  const size_t org = (size_t)g * p.M * p.N + (size_t)m0 * p.N + n0;
+  // C from the tile origin to the end of the expert's matrix
+  const uint32_t cbytes = (uint32_t)((((size_t)(p.M - m0) - 1) * p.N + (p.N - n0)) * 4);
+  store_tile_gen<CF>(lds, acc, p.D + org, p.N, p.M - m0, p.N - n0, p.C ? p.C + org : nullptr,
+                     cbytes, parts, nparts);
 }
 
 // acc (this lane's 4 rows x 1 column of each 16x16 sub-tile) + C -> D. Per pass:
@@ -648,7 +750,132 @@ __device__ inline void compute_stage(const unsigned char* st, int gran, bool pro
 
 // ---------------------------------------------------------------- the kernel
 
+// Stages [kb0, kb1) of one item (expert g's tile at (m0, n0)), accumulated into acc.
+// nk is the expert's stage count; stage kb is token rows [TK*kb, TK*kb + TK) of the
+// expert. The stage buffers must be free on entry (callers barrier first); on
+// return every load of the unit has completed (LDS may still be read by other waves).
 template <int KIND, bool FAST, class CF>
+__device__ inline void item_gemm(const Params& p, const LoadOffsets<CF>& lo, unsigned char* smem,
+                                 int64_t t_begin, int Kg, int boff_g, int m0, int n0, int nk,
+                                 int kb0, int kb1, v4f (&acc)[CF::NI][CF::NJ]) {
+  const int n = kb1 - kb0;  // stages of this unit
+  // partial sums of the open 128-token block (used by fp32 scales with TK < 128;
+  // dead and removed by the compiler for the other policies)
+  v4f part[CF::NI][CF::NJ];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+    for (int jn = 0; jn < CF::NJ; ++jn) part[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Ring of NS stage buffers: step j (stage kb0 + j) lives in buffer j % NS. Each
+  // wave waits only for its own loads of a stage (the later stages' loads may stay in
+  // flight), then the barrier makes every wave's loads visible.
+#pragma unroll
+  for (int j = 0; j < CF::NS - 1; ++j)
+    if (j < n) load_stage<KIND, CF>(p, lo, smem + j * CF::STAGE, t_begin, Kg, boff_g, kb0 + j, m0, n0);
+  if constexpr (CF::PIPE) {
+    // Step j's fragments are read into registers during step j-1, so at the top of
+    // step j (after the barrier) buffer j % NS is free and receives step j + NS.
+    const PipeBase<CF> pb = pipe_base<CF>();
+    wait_stages<CF>(min(CF::NS - 2, n - 1));
+    __syncthreads();
+    if (CF::NS - 1 < n)
+      load_stage<KIND, CF>(p, lo, smem + (CF::NS - 1) * CF::STAGE, t_begin, Kg, boff_g,
+                           kb0 + CF::NS - 1, m0, n0);
+    // fragment halves: [2i] tokens 4q..4q+3, [2i+1] tokens 16+4q..16+4q+3
+    v4bf xa[2 * CF::NI], xb[2 * CF::NJ], ya[2 * CF::NI], yb[2 * CF::NJ];
+#pragma unroll
+    for (int i = 0; i < CF::NI; ++i) {
+      xa[2 * i] = tr16(smem + pb.a + 32 * i);
+      xa[2 * i + 1] = tr16(smem + pb.a + 32 * i + 16 * CF::ROWA);
+    }
+#pragma unroll
+    for (int jn = 0; jn < CF::NJ; ++jn) {
+      xb[2 * jn] = tr16(smem + pb.b + 32 * jn);
+      xb[2 * jn + 1] = tr16(smem + pb.b + 32 * jn + 16 * CF::ROWB);
+    }
+    // Step j: wait for step j+1's stage and barrier, refill the freed buffer, then
+    // the stage's MFMAs from (ca, cb) with the reads of step j+1 into (na, nb) spread
+    // between them. On the last step the reads fetch a stale but valid buffer and
+    // are never used.
+    auto step = [&](int j, v4bf (&ca)[2 * CF::NI], v4bf (&cb)[2 * CF::NJ],
+                    v4bf (&na)[2 * CF::NI], v4bf (&nb)[2 * CF::NJ]) {
+      if (j + 1 < n) {
+        wait_stages<CF>(min(CF::NS - 2, n - 2 - j));
+        __syncthreads();
+        if (j + CF::NS < n)
+          load_stage<KIND, CF>(p, lo, smem + (j % CF::NS) * CF::STAGE, t_begin, Kg, boff_g,
+                               kb0 + j + CF::NS, m0, n0);
+      }
+      const unsigned char* nxt = smem + ((j + 1) % CF::NS) * CF::STAGE;
+      constexpr int R = 2 * (CF::NI + CF::NJ);  // reads of the next stage
+      constexpr int S = CF::NI * CF::NJ;        // MFMAs of this stage
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int jn = s / CF::NI, i = s % CF::NI;
+        const v8bf a = __builtin_shufflevector(ca[2 * i], ca[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8bf b = __builtin_shufflevector(cb[2 * jn], cb[2 * jn + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[i][jn] = mfma_bf16(a, b, acc[i][jn]);
+#pragma unroll
+        for (int r = (s * R + S - 1) / S; r < ((s + 1) * R + S - 1) / S; ++r) {
+          if (r < 2 * CF::NI)
+            na[r] = tr16(nxt + pb.a + 32 * (r / 2) + 16 * CF::ROWA * (r % 2));
+          else
+            nb[r - 2 * CF::NI] = tr16(nxt + pb.b + 32 * ((r - 2 * CF::NI) / 2) +
+                                      16 * CF::ROWB * (r % 2));
+        }
+      }
+    };
+    // two steps per trip so that the register sets swap roles without copies
+    int j = 0;
+    for (; j + 1 < n; j += 2) {
+      step(j, xa, xb, ya, yb);
+      step(j + 1, ya, yb, xa, xb);
+    }
+    if (j < n) step(j, xa, xb, ya, yb);
+    return;
+  }
+  int buf = 0;  // j % NS
+  for (int j = 0; j < n; ++j) {
+    const int ahead = min(CF::NS - 2, n - 1 - j);
+    wait_stages<CF>(ahead);
+    __syncthreads();
+    if (j + CF::NS - 1 < n) {
+      const int nb = buf == 0 ? CF::NS - 1 : buf - 1;  // (j + NS - 1) % NS
+      load_stage<KIND, CF>(p, lo, smem + nb * CF::STAGE, t_begin, Kg, boff_g, kb0 + j + CF::NS - 1,
+                           m0, n0);
+    }
+    const int kb = kb0 + j;
+    const bool promote = ((kb + 1) % (128 / CF::TK) == 0) || kb + 1 == nk;
+    compute_stage<KIND, FAST, CF>(smem + buf * CF::STAGE, p.gran, promote, acc, part);
+    buf = buf + 1 == CF::NS ? 0 : buf + 1;
+  }
+}
+
+template <class CF>
+__device__ inline void zero_acc(v4f (&acc)[CF::NI][CF::NJ]) {
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+    for (int jn = 0; jn < CF::NJ; ++jn) acc[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
+}
+
+// Split-tile partial sums (stream-K mode): slot c holds workgroup c's partial of the
+// tile it starts inside, a row-major BM x BN tile.
+template <class CF>
+__device__ inline float* partial_slot(const Params& p, int c) {
+  return p.ws + (size_t)c * CF::BM * CF::BN;
+}
+
+// Longest wait for a partial (s_sleep 2 units each): a missing partial ends the wait
+// with KG_ERR_SPLIT in the status word instead of a hang.
+constexpr int kSpinLimit = 1 << 22;
+
+template <int KIND, bool FAST, class CF>
+__device__ void split_tiles(const Params& p, const Sched& s, unsigned char* smem,
+                            const LoadOffsets<CF>& lo, int slot);
+
+template <int KIND, bool FAST, class CF, bool SPLIT = false>
 __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int64_t wsum_k[kMaxWaves];
@@ -660,129 +887,136 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
     return;
   }
   const int T = p.tiles_m * p.tiles_n;
-  const int total = p.G * T;
   const int grid = gridDim.x;
   // XCD-aware deal: workgroup b runs on XCD b % 8; give each XCD a contiguous run
-  // of items per round so its workgroups share operand rows in its L2.
+  // of work so its workgroups share operand rows in its L2.
   const int b = blockIdx.x;
   const int slot = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
   const LoadOffsets<CF> lo = load_offsets<CF>(p);
 
-  for (int base = 0; base < total; base += grid) {
-    const int idx = base + slot;
-    if (idx >= total) break;
-    const Item it = decode_item(idx, T, p.tiles_m, p.tiles_n, s.order);
-    const int g = it.g;
-    const int m0 = it.tm * CF::BM, n0 = it.tn * CF::BN;
+  if constexpr (SPLIT) {
+    split_tiles<KIND, FAST, CF>(p, s, smem, lo, slot);
+  } else {
+    // One item (expert, m-tile, n-tile) at a time, longest experts first.
+    const int total = p.G * T;
+    for (int base = 0; base < total; base += grid) {
+      const int idx = base + slot;
+      if (idx >= total) break;
+      const Item it = decode_item(idx, T, p.tiles_m, p.tiles_n, s.order);
+      const int g = it.g;
+      const int m0 = it.tm * CF::BM, n0 = it.tn * CF::BN;
+      const int64_t t_begin = s.off[g];
+      const int Kg = uniform((int)(s.off[g + 1] - t_begin));
+      __syncthreads();  // the previous item is done with the stage buffers
+      if (Kg == 0) {
+        fill_tile<CF>(p, g, m0, n0);
+        continue;
+      }
+      const int boff_g = uniform(s.boff[g]);
+      const int nk = (Kg + CF::TK - 1) / CF::TK;
+      v4f acc[CF::NI][CF::NJ];
+      zero_acc<CF>(acc);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the previous item's stores
+      item_gemm<KIND, FAST, CF>(p, lo, smem, t_begin, Kg, boff_g, m0, n0, nk, 0, nk, acc);
+      store_tile<CF>(p, smem, g, m0, n0, acc);
+    }
+  }
+}
+
+// Stream-K mode (few tiles): the stages of all non-empty tiles, in item order, form
+// one line of length W; workgroup `slot` takes [W*slot/grid, W*(slot+1)/grid). A
+// tile cut by range ends is summed by the workgroup that holds its first stage: it
+// finishes that unit last in its range, and adds, in workgroup order, the partials
+// that the following workgroups wrote from the first unit of their ranges (so the
+// result does not depend on timing). Empty experts' fill tiles follow.
+template <int KIND, bool FAST, class CF>
+__device__ void split_tiles(const Params& p, const Sched& s, unsigned char* smem,
+                            const LoadOffsets<CF>& lo, int slot) {
+  __shared__ int64_t sk_cum[kMaxSplitGroups + 1];
+  __shared__ int sk_flag;
+  const int T = p.tiles_m * p.tiles_n;
+  const int grid = gridDim.x;
+  if (threadIdx.x == 0) {
+    int64_t c = 0;
+    for (int r = 0; r < p.G; ++r) {
+      sk_cum[r] = c;
+      c += (int64_t)T * ((s.ks[s.order[r]] + CF::TK - 1) / CF::TK);
+    }
+    sk_cum[p.G] = c;
+  }
+  __syncthreads();
+  const int64_t W = sk_cum[p.G];
+  // no range is empty: with fewer stages than workgroups, workgroup c < W takes
+  // stage c and the rest take none (they come last, so never sit between a tile's
+  // first workgroup and its later ones)
+  auto range_lo = [&](int c) { return W >= grid ? W * c / grid : (int64_t)min(c, (int)W); };
+  const int64_t lo_pos = range_lo(slot), hi_pos = range_lo(slot + 1);
+  for (int64_t pos = lo_pos; pos < hi_pos;) {
+    int r = 0;
+    while (sk_cum[r + 1] <= pos) ++r;
+    const int g = uniform((int)s.order[r]);
     const int64_t t_begin = s.off[g];
     const int Kg = uniform((int)(s.off[g + 1] - t_begin));
-    __syncthreads();  // the previous item is done with the stage buffers
-    if (Kg == 0) {
-      fill_tile<CF>(p, g, m0, n0);
-      continue;
-    }
-    const int boff_g = uniform(s.boff[g]);
     const int nk = (Kg + CF::TK - 1) / CF::TK;
+    const int64_t rel = pos - sk_cum[r];
+    const int t = (int)(rel / nk);
+    const int kb0 = (int)(rel - (int64_t)t * nk);
+    const int kb1 = (int)min((int64_t)nk, kb0 + (hi_pos - pos));
+    const Item it = decode_item(r * T + t, T, p.tiles_m, p.tiles_n, s.order);
+    const int m0 = it.tm * CF::BM, n0 = it.tn * CF::BN;
+    const int boff_g = uniform(s.boff[g]);
+    __syncthreads();  // the previous unit is done with the stage buffers
     v4f acc[CF::NI][CF::NJ];
-#pragma unroll
-    for (int i = 0; i < CF::NI; ++i)
-#pragma unroll
-      for (int jn = 0; jn < CF::NJ; ++jn) acc[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
-    // partial sums of the open 128-token block (used by fp32 scales with TK < 128;
-    // dead and removed by the compiler for the other policies)
-    v4f part[CF::NI][CF::NJ];
-#pragma unroll
-    for (int i = 0; i < CF::NI; ++i)
-#pragma unroll
-      for (int jn = 0; jn < CF::NJ; ++jn) part[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // Ring of NS stages: stage kb lives in buffer kb % NS and is loaded NS-1 stages
-    // before it is used. Each wave waits only for its own loads of stage kb (the
-    // later stages' loads may stay in flight), then the barrier makes every wave's
-    // loads visible.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the previous item's stores
-#pragma unroll
-    for (int st0 = 0; st0 < CF::NS - 1; ++st0)
-      if (st0 < nk) load_stage<KIND, CF>(p, lo, smem + st0 * CF::STAGE, t_begin, Kg, boff_g, st0, m0, n0);
-    if constexpr (CF::PIPE) {
-      // Ring of NS buffers. Stage kb's fragments are read into registers during
-      // step kb-1, so at the top of step kb (after the barrier) buffer kb % NS is
-      // free and receives stage kb + NS.
-      const PipeBase<CF> pb = pipe_base<CF>();
-      wait_stages<CF>(min(CF::NS - 2, nk - 1));
+    zero_acc<CF>(acc);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the previous unit's stores
+    item_gemm<KIND, FAST, CF>(p, lo, smem, t_begin, Kg, boff_g, m0, n0, nk, kb0, kb1, acc);
+    if (kb0 > 0) {
+      // a later part of a cut tile: publish it for the tile's first workgroup
+      // written through to memory, so no cache-wide write-back is needed
+      store_tile_gen<CF, true>(smem, acc, partial_slot<CF>(p, slot), CF::BN, CF::BM, CF::BN,
+                               nullptr, 0, nullptr, 0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's partial stores are done
       __syncthreads();
-      if (CF::NS - 1 < nk)
-        load_stage<KIND, CF>(p, lo, smem + (CF::NS - 1) * CF::STAGE, t_begin, Kg, boff_g,
-                             CF::NS - 1, m0, n0);
-      // fragment halves: [2i] tokens 4q..4q+3, [2i+1] tokens 16+4q..16+4q+3
-      v4bf xa[2 * CF::NI], xb[2 * CF::NJ], ya[2 * CF::NI], yb[2 * CF::NJ];
-#pragma unroll
-      for (int i = 0; i < CF::NI; ++i) {
-        xa[2 * i] = tr16(smem + pb.a + 32 * i);
-        xa[2 * i + 1] = tr16(smem + pb.a + 32 * i + 16 * CF::ROWA);
-      }
-#pragma unroll
-      for (int jn = 0; jn < CF::NJ; ++jn) {
-        xb[2 * jn] = tr16(smem + pb.b + 32 * jn);
-        xb[2 * jn + 1] = tr16(smem + pb.b + 32 * jn + 16 * CF::ROWB);
-      }
-      // Step kb: wait for stage kb+1 and barrier, refill the freed buffer, then the
-      // stage's MFMAs from (ca, cb) with the reads of stage kb+1 into (na, nb) spread
-      // between them. On the last step the reads fetch a stale but valid buffer and
-      // are never used.
-      auto step = [&](int kb, v4bf (&ca)[2 * CF::NI], v4bf (&cb)[2 * CF::NJ],
-                      v4bf (&na)[2 * CF::NI], v4bf (&nb)[2 * CF::NJ]) {
-        if (kb + 1 < nk) {
-          wait_stages<CF>(min(CF::NS - 2, nk - 2 - kb));
-          __syncthreads();
-          if (kb + CF::NS < nk)
-            load_stage<KIND, CF>(p, lo, smem + (kb % CF::NS) * CF::STAGE, t_begin, Kg, boff_g,
-                                 kb + CF::NS, m0, n0);
-        }
-        const unsigned char* nxt = smem + ((kb + 1) % CF::NS) * CF::STAGE;
-        constexpr int R = 2 * (CF::NI + CF::NJ);  // reads of the next stage
-        constexpr int S = CF::NI * CF::NJ;        // MFMAs of this stage
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int jn = s / CF::NI, i = s % CF::NI;
-          const v8bf a = __builtin_shufflevector(ca[2 * i], ca[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-          const v8bf b = __builtin_shufflevector(cb[2 * jn], cb[2 * jn + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[i][jn] = mfma_bf16(a, b, acc[i][jn]);
-#pragma unroll
-          for (int r = (s * R + S - 1) / S; r < ((s + 1) * R + S - 1) / S; ++r) {
-            if (r < 2 * CF::NI)
-              na[r] = tr16(nxt + pb.a + 32 * (r / 2) + 16 * CF::ROWA * (r % 2));
-            else
-              nb[r - 2 * CF::NI] = tr16(nxt + pb.b + 32 * ((r - 2 * CF::NI) / 2) +
-                                        16 * CF::ROWB * (r % 2));
+      if (threadIdx.x == 0)
+        __hip_atomic_store(p.wsflag + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      int nparts = 0;
+      if (kb1 < nk) {
+        // the first part: wait for the following workgroups' partials, which the
+        // epilogue adds in workgroup order
+        const int64_t tile_end = sk_cum[r] + (int64_t)(t + 1) * nk;
+        while (slot + 1 + nparts < grid && range_lo(slot + 1 + nparts) < tile_end) ++nparts;
+        if (threadIdx.x == 0) {
+          int ok = 1;
+          for (int c = slot + 1; c <= slot + nparts && ok; ++c) {
+            ok = 0;
+            for (int spin = 0; spin < kSpinLimit; ++spin) {
+              if (__hip_atomic_load(p.wsflag + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1) {
+                ok = 1;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+            if (ok) __hip_atomic_store(p.wsflag + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
+          if (!ok) kgwgrad_status_word = KG_ERR_SPLIT;
+          sk_flag = ok;
         }
-      };
-      // two steps per trip so that the register sets swap roles without copies
-      int kb = 0;
-      for (; kb + 1 < nk; kb += 2) {
-        step(kb, xa, xb, ya, yb);
-        step(kb + 1, ya, yb, xa, xb);
+        __syncthreads();  // the partials are read around the caches (sc0 sc1)
+        if (!sk_flag) nparts = 0;
       }
-      if (kb < nk) step(kb, xa, xb, ya, yb);
-      store_tile<CF>(p, smem, g, m0, n0, acc);
-      continue;
+      store_tile_parts<CF>(p, smem, g, m0, n0, acc, partial_slot<CF>(p, slot + 1), nparts);
     }
-    int buf = 0;  // kb % NS
-    for (int kb = 0; kb < nk; ++kb) {
-      const int ahead = min(CF::NS - 2, nk - 1 - kb);
-      wait_stages<CF>(ahead);
-      __syncthreads();
-      if (kb + CF::NS - 1 < nk) {
-        const int nb = buf == 0 ? CF::NS - 1 : buf - 1;  // (kb + NS - 1) % NS
-        load_stage<KIND, CF>(p, lo, smem + nb * CF::STAGE, t_begin, Kg, boff_g, kb + CF::NS - 1,
-                             m0, n0);
-      }
-      const bool promote = ((kb + 1) % (128 / CF::TK) == 0) || kb + 1 == nk;
-      compute_stage<KIND, FAST, CF>(smem + buf * CF::STAGE, p.gran, promote, acc, part);
-      buf = buf + 1 == CF::NS ? 0 : buf + 1;
-    }
-    store_tile<CF>(p, smem, g, m0, n0, acc);
+    pos += kb1 - kb0;
+  }
+  // fill tiles of the empty experts (at the end of the longest-first order)
+  int first_empty = 0;
+  while (first_empty < p.G && sk_cum[first_empty + 1] > sk_cum[first_empty]) ++first_empty;
+  const int nfill = (p.G - first_empty) * T;
+  for (int f = slot; f < nfill; f += grid) {
+    const Item it = decode_item(first_empty * T + f, T, p.tiles_m, p.tiles_n, s.order);
+    __syncthreads();
+    fill_tile<CF>(p, it.g, it.tm * CF::BM, it.tn * CF::BN);
   }
 }
 
@@ -818,13 +1052,22 @@ struct Launch {
   int bm, bn, threads;
 };
 
-template <int KIND, bool FAST, class CF>
+template <int KIND, bool FAST, class CF, bool SPLIT = false>
 static Launch launch_of() {
-  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF>, CF::NS * CF::STAGE, CF::BM, CF::BN,
-                CF::THREADS};
+  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF, SPLIT>, CF::NS * CF::STAGE, CF::BM,
+                CF::BN, CF::THREADS};
 }
 
-static Launch pick(int kind, bool fast, bool small = false) {
+// small: half tiles for problems with few full tiles; split: stream-K (bf16 only)
+// small: half tiles (bf16) for problems with few full tiles; split: stream-K over the
+// full-size tiles
+static Launch pick(int kind, bool fast, bool small = false, bool split = false) {
+  if (split) {
+    if (kind == BF16) return launch_of<BF16, false, CfgB16, true>();
+    if (kind == F32S)
+      return fast ? launch_of<F32S, true, CfgF8, true>() : launch_of<F32S, false, CfgF8h, true>();
+    return fast ? launch_of<E8M0, true, CfgF8, true>() : launch_of<E8M0, false, CfgF8h, true>();
+  }
   if (kind == BF16)
     return small ? launch_of<BF16, false, CfgB16s>() : launch_of<BF16, false, CfgB16>();
   if (kind == F32S) return fast ? launch_of<F32S, true, CfgF8>() : launch_of<F32S, false, CfgF8h>();
@@ -846,8 +1089,17 @@ static int device_setup(int dev) {
     int cus = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const Launch all[6] = {pick(BF16, false), pick(BF16, false, true), pick(F32S, false),
-                           pick(F32S, true),  pick(E8M0, false),       pick(E8M0, true)};
+    const Launch all[11] = {pick(BF16, false),
+                            pick(BF16, false, true),
+                            pick(F32S, false),
+                            pick(F32S, true),
+                            pick(E8M0, false),
+                            pick(E8M0, true),
+                            pick(BF16, false, false, true),
+                            pick(F32S, false, false, true),
+                            pick(F32S, true, false, true),
+                            pick(E8M0, false, false, true),
+                            pick(E8M0, true, false, true)};
     for (const Launch& l : all) {
       e = hipFuncSetAttribute(l.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                               l.stage_bytes + sched_bytes(kMaxGroups));
@@ -873,9 +1125,41 @@ using namespace kg;
 
 extern "C" int kg_max_groups(void) { return kMaxGroups; }
 
-extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb,
-                        const float* C, float* D, const int32_t* ks, int G, int M, int N,
-                        int64_t K_total, int gran_k, int dtype_flags, void* stream) {
+// Stream-K workspace: one int ready flag per workgroup (the flag area is padded to a
+// multiple of 256 bytes), then one partial tile per workgroup of the bf16 full-tile
+// configuration.
+static size_t split_flag_bytes(int cus) { return ((size_t)cus * sizeof(int) + 255) & ~(size_t)255; }
+
+static size_t split_ws_bytes(int cus) {
+  return split_flag_bytes(cus) + (size_t)cus * CfgB16::BM * CfgB16::BN * sizeof(float);
+}
+
+static int current_cus(int* cus) {
+  int dev = 0;
+  const hipError_t eg = hipGetDevice(&dev);
+  if (eg != hipSuccess) return hip_fail(eg, "hipGetDevice");
+  const int rc = device_setup(dev);
+  if (rc != KG_OK) return rc;
+  *cus = g_dev[dev].cus > 0 ? g_dev[dev].cus : 256;
+  return KG_OK;
+}
+
+extern "C" int64_t kg_wgrad_workspace_bytes(void) {
+  int cus = 0;
+  if (current_cus(&cus) != KG_OK) return -1;
+  return (int64_t)split_ws_bytes(cus);
+}
+
+extern "C" int64_t kg_wgrad_workspace_flag_bytes(void) {
+  int cus = 0;
+  if (current_cus(&cus) != KG_OK) return -1;
+  return (int64_t)split_flag_bytes(cus);
+}
+
+extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb,
+                           const float* C, float* D, const int32_t* ks, int G, int M, int N,
+                           int64_t K_total, int gran_k, int dtype_flags, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
   const int dtype = dtype_flags & 0xFF;
   const int flags = dtype_flags & ~0xFF;
   if (dtype != KG_E4M3_F32SCALE && dtype != KG_E4M3_UE8M0 && dtype != KG_BF16)
@@ -883,12 +1167,12 @@ extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void
   if (flags & ~KG_FLAG_FP8_MFMA) return KG_ERR_DTYPE;
   const bool fast = (flags & KG_FLAG_FP8_MFMA) != 0;
   if (fast && dtype == KG_BF16) return KG_ERR_DTYPE;
-  if (G < 0 || M < 0 || N < 0 || K_total < 0) return KG_ERR_SHAPE;
+  if (G < 0 || M < 0 || N < 0 || K_total < 0 || workspace_bytes < 0) return KG_ERR_SHAPE;
   if (dtype != KG_BF16 && gran_k != 32 && gran_k != 128) return KG_ERR_GRAN;
   if (dtype == KG_E4M3_F32SCALE && gran_k != 128) return KG_ERR_UNSUPPORTED;
   if (G > kMaxGroups) return KG_ERR_UNSUPPORTED;
   if (M > (1 << 24) || N > (1 << 24) || K_total > INT32_MAX) return KG_ERR_UNSUPPORTED;
-  if ((int64_t)M * N > (int64_t)1 << 30) return KG_ERR_UNSUPPORTED;  // one expert's C in 32-bit offsets
+  if ((int64_t)M * N > (int64_t)1 << 29) return KG_ERR_UNSUPPORTED;  // 32-bit byte offsets in one expert's C
   if (G == 0 || M == 0 || N == 0) return KG_OK;
   if (D == nullptr || ks == nullptr) return KG_ERR_NULL;
   if (K_total > 0 && (A == nullptr || B == nullptr)) return KG_ERR_NULL;
@@ -899,25 +1183,33 @@ extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void
   }
   if (M % 16 != 0 || N % 16 != 0) return KG_ERR_ALIGN;
   if (misaligned(A) || misaligned(B) || misaligned(sa) || misaligned(sb) || misaligned(C) ||
-      misaligned(D) || ((uintptr_t)ks & 3) != 0)
+      misaligned(D) || ((uintptr_t)ks & 3) != 0 || ((uintptr_t)workspace & 255) != 0)
     return KG_ERR_ALIGN;
   const int elt = dtype == KG_BF16 ? 2 : 1;
   const size_t dbytes = (size_t)G * M * N * 4;
   if (C != nullptr && C != D && overlap(C, dbytes, D, dbytes)) return KG_ERR_ALIAS;
   if (overlap(A, (size_t)K_total * M * elt, D, dbytes) ||
-      overlap(B, (size_t)K_total * N * elt, D, dbytes) || overlap(ks, (size_t)G * 4, D, dbytes))
+      overlap(B, (size_t)K_total * N * elt, D, dbytes) || overlap(ks, (size_t)G * 4, D, dbytes) ||
+      overlap(workspace, (size_t)workspace_bytes, D, dbytes) ||
+      (C != nullptr && overlap(workspace, (size_t)workspace_bytes, C, dbytes)))
     return KG_ERR_ALIAS;
 
   const int kind = dtype == KG_E4M3_F32SCALE ? F32S : dtype == KG_E4M3_UE8M0 ? E8M0 : BF16;
-  int dev = 0;
-  const hipError_t eg = hipGetDevice(&dev);
-  if (eg != hipSuccess) return hip_fail(eg, "hipGetDevice");
-  const int rc = device_setup(dev);
+  int cus = 0;
+  const int rc = current_cus(&cus);
   if (rc != KG_OK) return rc;
-  const int cus = g_dev[dev].cus > 0 ? g_dev[dev].cus : 256;
-  // bf16: halve the tile along M when full tiles would leave most CUs idle
-  const int64_t big_tiles = (int64_t)G * ((M + 255) / 256) * ((N + 255) / 256);
-  const Launch L = pick(kind, fast, kind == BF16 && big_tiles < 2 * (int64_t)cus);
+  // bf16 problems with fewer than two full 256 x 256 tiles per CU use half tiles.
+  // When even then at most half of the CUs would get a tile, and a workspace is
+  // given, the tiles' token ranges are cut across all CUs instead (stream-K).
+  auto tiles_of = [&](const Launch& l) {
+    return (int64_t)G * ((M + l.bm - 1) / l.bm) * ((N + l.bn - 1) / l.bn);
+  };
+  const int64_t big_tiles = tiles_of(pick(BF16, false));
+  const bool small = kind == BF16 && big_tiles < 2 * (int64_t)cus;
+  const bool split = workspace != nullptr && G <= kMaxSplitGroups &&
+                     (size_t)workspace_bytes >= split_ws_bytes(cus) &&
+                     2 * tiles_of(pick(kind, fast, small)) <= (int64_t)cus;
+  const Launch L = pick(kind, fast, small && !split, split);
   const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
   const int64_t total = (int64_t)G * tiles_m * tiles_n;
   if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;
@@ -937,12 +1229,21 @@ extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void
   p.gran = dtype == KG_BF16 ? 0 : gran_k;
   p.tiles_m = tiles_m;
   p.tiles_n = tiles_n;
-  const int grid = (int)(total < cus ? total : cus);
+  p.ws = split ? (float*)((unsigned char*)workspace + split_flag_bytes(cus)) : nullptr;
+  p.wsflag = split ? (int*)workspace : nullptr;
+  const int grid = split ? cus : (int)(total < cus ? total : cus);
   void* args[] = {&p};
   const hipError_t e = hipLaunchKernel(L.fn, dim3(grid), dim3(L.threads), args,
                                        L.stage_bytes + sched_bytes(G), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return KG_OK;
+}
+
+extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb,
+                        const float* C, float* D, const int32_t* ks, int G, int M, int N,
+                        int64_t K_total, int gran_k, int dtype_flags, void* stream) {
+  return kg_wgrad_ws(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags, nullptr, 0,
+                     stream);
 }
 
 extern "C" int kg_status(void* stream) {

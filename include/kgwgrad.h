@@ -63,7 +63,10 @@ typedef enum {
   KG_ERR_ALIAS = -6,       /* C and D overlap without being the same buffer                */
   KG_ERR_UNSUPPORTED = -7, /* a combination this build does not implement (see kg_wgrad)   */
   KG_ERR_HIP = -8,         /* the HIP runtime reported an error                            */
-  KG_ERR_KSUM = -9         /* some ks[g] < 0, or sum(ks) != K_total (reported by kg_status) */
+  KG_ERR_KSUM = -9,        /* some ks[g] < 0, or sum(ks) != K_total (reported by kg_status) */
+  KG_ERR_SPLIT = -10       /* stream-K mode: a partial tile never became ready (reported by
+                              kg_status; D is incomplete and the workspace must be zeroed
+                              again before its next use)                                    */
 } kg_status_code;
 
 /*
@@ -83,7 +86,7 @@ typedef enum {
  * Implemented combinations: (KG_E4M3_F32SCALE, 128), (KG_E4M3_UE8M0, 32),
  * (KG_E4M3_UE8M0, 128) and KG_BF16. (KG_E4M3_F32SCALE, 32) returns
  * KG_ERR_UNSUPPORTED. G is limited to 1024 (kg_max_groups), M and N to 2^24, M * N to
- * 2^30 and K_total to 2^31 - 1 (KG_ERR_UNSUPPORTED beyond).
+ * 2^29 and K_total to 2^31 - 1 (KG_ERR_UNSUPPORTED beyond).
  *
  * Returns KG_OK after enqueueing, or an error code before enqueueing anything (D
  * untouched). G == 0, M == 0 or N == 0 return KG_OK without a launch. A ks that
@@ -95,9 +98,52 @@ int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb, const
              int dtype, void* stream);
 
 /*
+ * kg_wgrad_ws -- kg_wgrad with a caller-owned workspace that lets small bf16
+ * problems use every compute unit.
+ *
+ * When the bf16 problem has fewer than two 256 x 256 output tiles per compute unit
+ * and G <= 64, the token range of every tile is cut across all compute units
+ * (stream-K): the workgroup that holds a tile's first tokens adds the partial
+ * tiles of the workgroups that hold its later tokens, in a fixed order, so results
+ * do not depend on timing. Other problems, or a NULL / too small workspace, run
+ * exactly as kg_wgrad.
+ *
+ *   workspace        device memory, 256-byte aligned, at least
+ *                    kg_wgrad_workspace_bytes() bytes. Its first
+ *                    kg_wgrad_workspace_flag_bytes() bytes are ready flags: they must
+ *                    be zero before the first use, and every call that completes
+ *                    with KG_OK leaves them zero again; the rest is scratch for
+ *                    partial tiles and needs no initialisation. It must not overlap
+ *                    C or D. Calls that share a workspace must not run concurrently.
+ *   workspace_bytes  its size in bytes
+ *
+ * Returns and errors as kg_wgrad; KG_ERR_ALIGN for a workspace that is not 256-byte
+ * aligned, KG_ERR_ALIAS for one that overlaps C or D. kg_status reports
+ * KG_ERR_SPLIT if a partial tile was never published (the kernel then gives up
+ * after about 0.2 s instead of waiting forever).
+ */
+int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, const float* C,
+                float* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
+                int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * kg_wgrad_workspace_bytes -- workspace size that kg_wgrad_ws needs on the current
+ * device (one 256 KB partial tile per compute unit plus flags), or -1 if the HIP
+ * runtime reports an error.
+ */
+int64_t kg_wgrad_workspace_bytes(void);
+
+/*
+ * kg_wgrad_workspace_flag_bytes -- size of the flag area at the start of the
+ * workspace (zero before first use, kept zero by successful calls), or -1 if the
+ * HIP runtime reports an error.
+ */
+int64_t kg_wgrad_workspace_flag_bytes(void);
+
+/*
  * kg_status -- synchronise `stream`, then return and clear the device status
- * word of the current device (KG_OK, or KG_ERR_KSUM if a kg_wgrad call since the
- * last kg_status found an inconsistent ks). Returns KG_ERR_HIP if the stream
+ * word of the current device (KG_OK, KG_ERR_KSUM if a kg_wgrad call since the
+ * last kg_status found an inconsistent ks, or KG_ERR_SPLIT). Returns KG_ERR_HIP if the stream
  * reports an error.
  */
 int kg_status(void* stream);

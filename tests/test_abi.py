@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "kgwgrad.h")
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*int\s+(kg_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t)\s+(kg_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -76,6 +76,27 @@ def call(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE 
 ])
 def test_synchronous_errors(kw, code):
     assert call(**kw) == code
+
+
+def call_ws(ws=FAKE + (1 << 32), ws_bytes=1 << 26, **kw):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    a = dict(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE + (1 << 31),
+             G=3, M=64, N=128, K=104, gran=128, dtype=kg.KG_E4M3_F32SCALE)
+    a.update(kw)
+    return B.lib().kg_wgrad_ws(v(a["A"]), v(a["sa"]), v(a["Bp"]), v(a["sb"]), v(a["C"]), v(a["D"]),
+                               v(a["ks"]), a["G"], a["M"], a["N"], a["K"], a["gran"], a["dtype"],
+                               v(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=FAKE + (1 << 32) + 16), B.KG_ERR_ALIGN),        # workspace not 256-byte aligned
+    (dict(ws=FAKE + (1 << 30) - 256), B.KG_ERR_ALIAS),       # workspace overlaps D
+    (dict(ws_bytes=-1), B.KG_ERR_SHAPE),
+    (dict(M=1 << 15, N=1 << 15), B.KG_ERR_UNSUPPORTED),      # M * N above 2^29
+    (dict(gran=64), B.KG_ERR_GRAN),
+])
+def test_workspace_entry_point_errors(kw, code):
+    assert call_ws(**kw) == code
 
 
 def test_empty_shapes_are_ok_without_launch():

@@ -181,6 +181,62 @@ def test_bf16_many_tiles_large_tile_config():
         assert torch.equal(D[g].cpu().view(torch.int32), case.C[g].view(torch.int32))
 
 
+def _ws_clean(ws):
+    """The workspace's flag area is zero again after a successful call."""
+    torch.cuda.synchronize()
+    return int(ws[:kg.kg_wgrad_workspace_flag_bytes()].count_nonzero()) == 0
+
+
+SPLIT_SHAPES = [
+    ([300, 0, 517], 256, 256, True),      # few stages over every CU: tiles cut into 1-stage units
+    ([4000, 1234], 512, 1024, False),     # several tiles per expert, cuts inside tiles
+    ([0, 1, 33, 0], 256, 512, True),      # tiny and empty experts
+]
+
+
+@pytest.mark.parametrize("dtype,gran,flags", [(BF, 128, 0), (F32, 128, 0), (UE8, 32, 0),
+                                              (UE8, 128, 0), (F32, 128, FAST), (UE8, 32, FAST)])
+@pytest.mark.parametrize("ks,M,N,with_c", SPLIT_SHAPES)
+def test_stream_k_workspace(ks, M, N, with_c, dtype, gran, flags):
+    say("stream-K", dtype, gran, flags, ks, M, N, with_c)
+    case = small_case(dtype, gran, ks, M, N, with_c=with_c, seed=15, b_std=1e-3, a_outlier_p=0.01)
+    t = to_dev(case)
+    ws = kg.new_workspace()
+    D = torch.full((case.G, M, N), float("nan"), device=dev())
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D, t["ks"], gran, dtype | flags,
+                workspace=ws)
+    assert kg.kg_status() == kg.KG_OK
+    assert _ws_clean(ws), "workspace flags not left zero"
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "stream-K", fast=bool(flags))
+    for g in np.nonzero(np.asarray(ks) == 0)[0]:
+        want = case.C[g] if with_c else torch.zeros_like(case.C[g] if with_c else D[g].cpu())
+        assert torch.equal(D[g].cpu().view(torch.int32), want.view(torch.int32))
+    # same bits on a second call through the same workspace
+    D2 = torch.full_like(D, float("nan"))
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D2, t["ks"], gran, dtype | flags,
+                workspace=ws)
+    assert kg.kg_status() == kg.KG_OK
+    assert torch.equal(D.view(torch.int32), D2.view(torch.int32))
+    assert _ws_clean(ws)
+
+
+def test_bf16_stream_k_full_workload_and_in_place():
+    say("stream-K full bf16 workload")
+    case = inputs.workload("bf16", device="cuda")
+    t = to_dev(case)
+    ws = kg.new_workspace()
+    D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev())
+    kg.kg_wgrad(t["A"], None, t["B"], None, t["C"], D, t["ks"], 128, BF, workspace=ws)
+    assert kg.kg_status() == kg.KG_OK and _ws_clean(ws)
+    sampled_check(case, t, D)
+    # in place: D starts as C
+    Di = t["C"].clone()
+    kg.kg_wgrad(t["A"], None, t["B"], None, Di, Di, t["ks"], 128, BF, workspace=ws)
+    assert kg.kg_status() == kg.KG_OK and _ws_clean(ws)
+    assert torch.equal(Di.view(torch.int32), D.view(torch.int32))
+
+
 @pytest.mark.parametrize("dtype,gran", [(F32, 128), (BF, 128)])
 def test_in_place_accumulate(dtype, gran):
     say("in place", dtype)
