@@ -378,3 +378,114 @@ int kgref_wgrad_sampled(const void* A, const void* sa, const void* B, const void
   free(boff);
   return rc;
 }
+
+/* ---------------------------------------------------------------- requantiser
+ *
+ * The step before the GEMM that the issue page's discussion calls inevitable
+ * (soundOfDestiny, 2025-03-12): activations or output gradients, stored as bf16 or
+ * as the forward pass's fp8 copy with one fp32 scale per token per 128 channels,
+ * become fp8 e4m3fn operands with one scale per channel per gran_k tokens of an
+ * expert. Every step is done in the precision the kernels use (fp32 values and
+ * divisions), so that the fp8 bytes and the scales are compared bit for bit.
+ */
+
+/* Nearest e4m3fn code to v, ties to the even code, magnitudes at or above 448
+ * saturating to 448; the sign bit follows v (also for zero); NaN -> 0x7F. The
+ * positive codes 0..126 decode to increasing magnitudes, so a binary search over
+ * the decode table finds the two neighbours. */
+uint8_t kgref_e4m3_encode(double v) {
+  pthread_once(&g_once, build_tables);
+  if (isnan(v)) return 0x7F;
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  int lo = 0, hi = 126; /* g_e4m3[lo] <= a < g_e4m3[hi] */
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (g_e4m3[mid] <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const double dlo = a - g_e4m3[lo], dhi = g_e4m3[hi] - a;
+  int c;
+  if (dlo < dhi)
+    c = lo;
+  else if (dhi < dlo)
+    c = hi;
+  else
+    c = (lo % 2 == 0) ? lo : hi;
+  return sign | (uint8_t)c;
+}
+
+/* Smallest power-of-two exponent k with 2^k >= r (r > 0, a normal or subnormal
+ * binary32 value), as the E8M0 byte k + 127 clamped to [0, 254]. */
+static uint8_t e8m0_ceil(float r) {
+  int k;
+  const double f = frexp((double)r, &k); /* r = f * 2^k, f in [0.5, 1) */
+  if (f == 0.5) k -= 1;                   /* r is a power of two */
+  int e = k + 127;
+  if (e < 0) e = 0;
+  if (e > 254) e = 254;
+  return (uint8_t)e;
+}
+
+int kgref_requant(const void* X, const float* xs, const int32_t* ks, int G, int H,
+                  int64_t K_total, int gran_k, int src, int scale_kind, uint8_t* Q, void* S) {
+  if (G < 0 || H < 0 || K_total < 0) return KGREF_ERR_SHAPE;
+  if (gran_k != 32 && gran_k != 128) return KGREF_ERR_GRAN;
+  if ((src != KGREF_SRC_BF16 && src != KGREF_SRC_E4M3_1X128) ||
+      (scale_kind != KGREF_SCALE_F32 && scale_kind != KGREF_SCALE_UE8M0))
+    return KGREF_ERR_DTYPE;
+  if (src == KGREF_SRC_E4M3_1X128 && H % 128 != 0) return KGREF_ERR_SHAPE;
+  if (G > 0 && ks == NULL) return KGREF_ERR_NULL;
+  int64_t sum = 0;
+  for (int g = 0; g < G; ++g) {
+    if (ks[g] < 0) return KGREF_ERR_KSUM;
+    sum += ks[g];
+  }
+  if (sum != K_total) return KGREF_ERR_KSUM;
+  if (K_total > 0 && H > 0 && (X == NULL || Q == NULL || S == NULL)) return KGREF_ERR_NULL;
+  if (src == KGREF_SRC_E4M3_1X128 && K_total > 0 && H > 0 && xs == NULL) return KGREF_ERR_NULL;
+  pthread_once(&g_once, build_tables);
+
+  float* col = (float*)malloc(sizeof(float) * (size_t)(gran_k > 0 ? gran_k : 1));
+  if (!col) return KGREF_ERR_SHAPE;
+  int64_t t_first = 0, brow = 0;
+  for (int g = 0; g < G; ++g) {
+    for (int64_t t0 = t_first; t0 < t_first + ks[g]; t0 += gran_k, ++brow) {
+      const int64_t t1 = t0 + gran_k < t_first + ks[g] ? t0 + gran_k : t_first + ks[g];
+      for (int h = 0; h < H; ++h) {
+        /* the block's values of channel h, in fp32, and their largest magnitude */
+        float amax = 0.0f;
+        for (int64_t t = t0; t < t1; ++t) {
+          float x;
+          if (src == KGREF_SRC_BF16) {
+            x = (float)kgref_bf16(((const uint16_t*)X)[t * H + h]);
+          } else {
+            const float d = (float)g_e4m3[((const uint8_t*)X)[t * H + h]];
+            x = d * xs[t * (H / 128) + h / 128]; /* binary32 product */
+          }
+          col[t - t0] = x;
+          if (fabsf(x) > amax) amax = fabsf(x);
+        }
+        if (scale_kind == KGREF_SCALE_F32) {
+          const float s = amax == 0.0f ? 1.0f : amax / 448.0f; /* binary32 quotient */
+          ((float*)S)[brow * H + h] = s;
+          for (int64_t t = t0; t < t1; ++t) {
+            const float y = col[t - t0] / s; /* binary32 quotient */
+            Q[t * H + h] = kgref_e4m3_encode((double)y);
+          }
+        } else {
+          const uint8_t e = amax == 0.0f ? 127 : e8m0_ceil(amax / 448.0f);
+          ((uint8_t*)S)[brow * H + h] = e;
+          for (int64_t t = t0; t < t1; ++t)
+            Q[t * H + h] = kgref_e4m3_encode(ldexp((double)col[t - t0], 127 - (int)e));
+        }
+      }
+    }
+    t_first += ks[g];
+  }
+  free(col);
+  return KGREF_OK;
+}

@@ -71,6 +71,26 @@ int kgref_wgrad_sampled(const void* A, const void* sa, const void* B, const void
 /* Number of threads the last kgref_wgrad / kgref_wgrad_sampled call used. */
 int kgref_last_threads(void);
 
+/* ---- requantiser: the step that produces the GEMM's operands ----
+ *
+ * For expert g's token block kb (rows [t0, t1), gran_k tokens from the expert's first
+ * token, the last block partial) and channel h, with x(t,h) the binary32 source value
+ * (bf16 widened, or e4m3 decoded times the token's 1x128 scale as a binary32
+ * product) and amax the largest |x| of the block:
+ *   SCALE_F32:   s = amax / 448 (binary32; 1 if amax == 0), q = enc(x / s) (binary32 quotient)
+ *   SCALE_UE8M0: e = 127 + smallest k with 2^k >= amax / 448 (binary32 quotient), clamped to
+ *                [0, 254] (127 if amax == 0); q = enc(x * 2^(127 - e))
+ * where enc rounds to the nearest e4m3fn value (ties to the even code, saturating at
+ * +-448, sign kept). Scale rows are packed per expert as in the GEMM (boff). */
+#define KGREF_SRC_BF16 0       /* X: uint16 bf16 [K_total][H]; xs NULL                       */
+#define KGREF_SRC_E4M3_1X128 1 /* X: uint8 e4m3fn [K_total][H]; xs: float [K_total][H/128]   */
+#define KGREF_SCALE_F32 0      /* S: float [nblocks][H]                                       */
+#define KGREF_SCALE_UE8M0 1    /* S: uint8 [nblocks][H]                                       */
+
+uint8_t kgref_e4m3_encode(double v);
+int kgref_requant(const void* X, const float* xs, const int32_t* ks, int G, int H,
+                  int64_t K_total, int gran_k, int src, int scale_kind, uint8_t* Q, void* S);
+
 #ifdef __cplusplus
 }
 #endif

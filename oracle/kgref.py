@@ -14,6 +14,8 @@ from . import build as _build
 
 OK, ERR_NULL, ERR_SHAPE, ERR_GRAN, ERR_DTYPE, ERR_KSUM = 0, -1, -2, -3, -4, -9
 E4M3_F32SCALE, E4M3_UE8M0, BF16 = 0, 1, 2
+SRC_BF16, SRC_E4M3_1X128 = 0, 1
+SCALE_F32, SCALE_UE8M0 = 0, 1
 
 _lib = None
 
@@ -48,6 +50,11 @@ def lib():
                                           i64, vp, vp, vp, vp, vp, ctypes.c_int]
         L.kgref_last_threads.restype = ctypes.c_int
         L.kgref_last_threads.argtypes = []
+        L.kgref_e4m3_encode.restype = ctypes.c_uint8
+        L.kgref_e4m3_encode.argtypes = [ctypes.c_double]
+        L.kgref_requant.restype = ctypes.c_int
+        L.kgref_requant.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, vp, vp]
         _lib = L
         del i32
     return _lib
@@ -152,3 +159,23 @@ def wgrad_sampled(A, sa, B, sb, C, ks, M, N, gran_k, dtype, sg, sm, sn, threads=
 
 def last_threads():
     return lib().kgref_last_threads()
+
+
+def e4m3_encode(v):
+    return int(lib().kgref_e4m3_encode(float(v)))
+
+
+def requant(X, xs, ks, H, gran_k, src, scale_kind, K_total=None):
+    """Reference requantisation: returns (rc, Q uint8 [K_total, H], S [nblocks, H])."""
+    ks = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    G = ks.size
+    if K_total is None:
+        K_total = int(ks.astype(np.int64).sum())
+    X = _c(X, np.uint16 if src == SRC_BF16 else np.uint8)
+    xs = _c(xs, np.float32)
+    nblk = int(sum((int(k) + gran_k - 1) // gran_k for k in ks))
+    Q = np.zeros((K_total, H), np.uint8)
+    S = np.zeros((nblk, H), np.float32 if scale_kind == SCALE_F32 else np.uint8)
+    rc = lib().kgref_requant(_ptr(X), _ptr(xs), _ptr(ks) if G > 0 else None, G, H, K_total,
+                             gran_k, src, scale_kind, _ptr(Q), _ptr(S))
+    return rc, Q, S
