@@ -16,6 +16,7 @@ KG_OK = 0
 KG_ERR_NULL, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_DTYPE = -1, -2, -3, -4
 KG_ERR_ALIGN, KG_ERR_ALIAS, KG_ERR_UNSUPPORTED, KG_ERR_HIP, KG_ERR_KSUM = -5, -6, -7, -8, -9
 KG_ERR_SPLIT = -10
+KG_SRC_BF16, KG_SRC_E4M3_1X128 = 0, 1
 ERROR_NAMES = {0: "KG_OK", -1: "KG_ERR_NULL", -2: "KG_ERR_SHAPE", -3: "KG_ERR_GRAN",
                -4: "KG_ERR_DTYPE", -5: "KG_ERR_ALIGN", -6: "KG_ERR_ALIAS",
                -7: "KG_ERR_UNSUPPORTED", -8: "KG_ERR_HIP", -9: "KG_ERR_KSUM",
@@ -33,6 +34,7 @@ SIGNATURES = {
     "kg_status": (_i32, [_vp]),
     "kg_debug_offsets": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "kg_max_groups": (_i32, []),
+    "kg_requant": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -136,3 +138,29 @@ def kg_debug_offsets(ks, gran_k, off, boff, stream=None):
 
 def kg_max_groups():
     return lib().kg_max_groups()
+
+
+def kg_requant_raw(X, xs, ks, G, H, K_total, gran_k, src, scale_kind, Q, S, stream=None):
+    """Call kg_requant with torch device tensors (or None); returns the status code."""
+    return lib().kg_requant(_ptr(X), _ptr(xs), _ptr(ks), int(G), int(H), int(K_total), int(gran_k),
+                            int(src), int(scale_kind), _ptr(Q), _ptr(S), _stream(stream))
+
+
+def kg_requant(X, xs, ks, gran_k, scale_kind, nblk, Q=None, S=None, stream=None):
+    """fp8 operand and per-(expert block, channel) scales for kg_wgrad from X.
+
+    X: bf16 [K_total, H] (xs None) or e4m3fn bytes / float8 [K_total, H] with xs fp32
+    [K_total, H/128]; ks int32 [G] on the GPU; nblk = sum(ceil(ks / gran_k)) (the scale
+    rows; the caller knows ks). Returns (Q uint8 [K_total, H], S [nblk, H])."""
+    import torch
+    K_total, H = X.shape
+    src = KG_SRC_BF16 if X.dtype == torch.bfloat16 else KG_SRC_E4M3_1X128
+    if Q is None:
+        Q = torch.empty((K_total, H), dtype=torch.uint8, device=X.device)
+    if S is None:
+        sdt = torch.float32 if scale_kind == KG_E4M3_F32SCALE else torch.uint8
+        S = torch.empty((nblk, H), dtype=sdt, device=X.device)
+    rc = kg_requant_raw(X, xs, ks, ks.numel(), H, K_total, gran_k, src, scale_kind, Q, S, stream)
+    if rc != KG_OK:
+        raise KgError(rc, "kg_requant")
+    return Q, S

@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkgwgrad.so")
-SOURCES = [os.path.join(PKG, "csrc", "kgwgrad.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "kgwgrad.hip")]  # includes kg_requant.h
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -1,0 +1,295 @@
+// kg_requant.h -- requantiser on MI355X (gfx950), C ABI: the step that produces the
+// K-grouped GEMM's fp8 operands. Included at the end of kgwgrad.hip, so that it
+// shares the library's single translation unit (and its device status word).
+//
+// The issue page "Is DeepGEMM directly applicable to backward in training?" explains
+// that the weight-gradient GEMM needs its operands scaled per channel per 128 tokens
+// of an expert, while the forward pass stores activations as fp8 with one scale per
+// token per 128 channels, so a requantisation is needed in between (comments of
+// soundOfDestiny, 2025-03-12). For expert g's token block kb (gran_k tokens from the
+// expert's first token, the last one partial) and channel h, with x the binary32
+// source value (bf16 widened, or e4m3 decoded times the token's 1x128 scale as one
+// binary32 product) and amax the block's largest |x|:
+//   fp32 scales: s = amax / 448 (1 if amax is 0) and q = e4m3(x / s), both binary32
+//                quotients rounded to nearest;
+//   UE8M0:       e = 127 + the smallest k with 2^k >= amax / 448, clamped to
+//                [0, 254] (127 if amax is 0), and q = e4m3(x * 2^(127 - e));
+// where e4m3() rounds to the nearest e4m3fn value, ties to the even code, with
+// saturation at +-448 and the sign kept. Scale rows are packed per expert exactly
+// as kg_wgrad reads them.
+//
+// Design: HBM-bound, one pass. A work item is (scale row, 128-channel slice): 256
+// threads hold the block's values in registers (16 channel groups of 8 channels x 16
+// row groups), reduce the column maxima with lane shuffles and one LDS exchange, and
+// write 8-byte runs of fp8 codes. A persistent grid walks the items; each workgroup
+// scans ks once (the same scan as the GEMM) and finds an item's expert by binary
+// search over the scale-row offsets.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kg_device.h"
+#include "kg_sched.h"
+#include "kgwgrad.h"
+
+namespace kg {
+
+constexpr int kQThreads = 256;
+constexpr int kQCols = 128;   // channels per item
+constexpr int kQColGroups = 16;  // threads per row: 8 channels each
+constexpr int kQRowGroups = kQThreads / kQColGroups;
+
+struct QParams {
+  const unsigned char* X;  // bf16 or e4m3 [K_total, H]
+  const float* xs;         // [K_total, H/128] for the e4m3 source
+  unsigned char* Q;        // e4m3 [K_total, H]
+  void* S;                 // fp32 or uint8 [nblk, H]
+  const int32_t* ks;
+  int G, H;
+  int64_t K_total;
+  int gran;
+};
+
+// binary32 -> e4m3fn code: nearest value, ties to the even code, saturating at
+// +-448, sign kept, NaN -> 0x7F. Exact: scaling by powers of two and the
+// round-to-nearest-even of v_rndne_f32 introduce no other rounding.
+__device__ inline uint32_t e4m3_rne(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(y);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;  // -6..8
+  int m8 = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - E));              // 8..16
+  if (m8 == 16) {
+    E += 1;
+    m8 = 8;
+  }
+  return sign | (uint32_t)(((E + 7) << 3) | (m8 - 8));
+}
+
+// E8M0 byte of the smallest power of two >= r (r = amax / 448 > 0), clamped to
+// [0, 254].
+__device__ inline int e8m0_ceil(float r) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, r);
+  const int ex = (int)((b >> 23) & 0xFFu);
+  const uint32_t mant = b & 0x7FFFFFu;
+  int e;
+  if (ex > 0)
+    e = ex + (mant != 0 ? 1 : 0);   // (ex - 127 + carry) + 127
+  else
+    e = mant > (1u << 22) ? 1 : 0;  // subnormal r: 2^-126 > r > 2^-127 -> 1
+  return e < 0 ? 0 : e > 254 ? 254 : e;
+}
+
+template <int SRC, int SK>
+__global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int64_t wsum_k[kMaxWaves];
+  __shared__ int32_t wsum_b[kMaxWaves];
+  __shared__ float red[kQThreads / 64][kQCols];
+  Sched s = sched_carve(smem, p.G);
+  if (sched_build<kQThreads>(p.ks, p.G, p.gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cg = tid % kQColGroups, rg = tid / kQColGroups;
+  const int ctiles = p.H / kQCols;
+  const int64_t nblk = s.boff[p.G];
+  const int64_t total = nblk * ctiles;
+  constexpr int kMaxRows = 128 / kQRowGroups;  // rows per thread at gran 128
+  for (int64_t item = blockIdx.x; item < total; item += gridDim.x) {
+    const int b = (int)(item / ctiles), ct = (int)(item - (int64_t)b * ctiles);
+    // expert of scale row b: the last g with boff[g] <= b (binary search; empty
+    // experts own no rows and are skipped by the strict comparison)
+    int lo = 0, hi = p.G;  // boff[lo] <= b < boff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s.boff[mid] <= b)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int g = lo;
+    const int kb = b - s.boff[g];
+    const int64_t t0 = s.off[g] + (int64_t)kb * p.gran;
+    const int rows = (int)min((int64_t)p.gran, s.off[g + 1] - t0);
+    const int h0 = ct * kQCols + cg * 8;
+    // load this thread's rows (rg, rg + 16, ...) of its 8 channels as binary32
+    float v[kMaxRows][8];
+    float amax[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) amax[c] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxRows; ++i) {
+      const int r = rg + kQRowGroups * i;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
+      if (r < rows) {
+        const int64_t t = t0 + r;
+        if constexpr (SRC == KG_SRC_BF16) {
+          const uint4 x = *(const uint4*)(p.X + (t * p.H + h0) * 2);
+          const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[i][2 * k] = __builtin_bit_cast(float, wds[k] << 16);
+            v[i][2 * k + 1] = __builtin_bit_cast(float, wds[k] & 0xFFFF0000u);
+          }
+        } else {
+          const uint2 x = *(const uint2*)(p.X + t * p.H + h0);
+          const float sc = p.xs[t * (p.H / 128) + h0 / 128];
+          const uint32_t wds[2] = {x.x, x.y};
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            // e4m3 decode (exact, through bf16), then one binary32 product per value
+            const v2bf d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[k], 1.0f, false);
+            const v2bf d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[k], 1.0f, true);
+            v[i][4 * k + 0] = (float)d0[0] * sc;
+            v[i][4 * k + 1] = (float)d0[1] * sc;
+            v[i][4 * k + 2] = (float)d1[0] * sc;
+            v[i][4 * k + 3] = (float)d1[1] * sc;
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) amax[c] = __builtin_fmaxf(amax[c], __builtin_fabsf(v[i][c]));
+      }
+    }
+    // column maxima: the 4 row groups of a wave share a channel group at lanes
+    // l, l + 16, l + 32, l + 48; then across the 4 waves through LDS
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      amax[c] = __builtin_fmaxf(amax[c], __shfl_xor(amax[c], 16, 64));
+      amax[c] = __builtin_fmaxf(amax[c], __shfl_xor(amax[c], 32, 64));
+    }
+    if (lane < kQColGroups) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) red[w][cg * 8 + c] = amax[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float m = red[0][cg * 8 + c];
+#pragma unroll
+      for (int ww = 1; ww < kQThreads / 64; ++ww) m = __builtin_fmaxf(m, red[ww][cg * 8 + c]);
+      amax[c] = m;
+    }
+    __syncthreads();  // red is rewritten by the next item
+    // scales and codes
+    float mul[8];   // UE8M0: 2^(127 - e)
+    float sdiv[8];  // fp32 scales: s
+    uint32_t eb[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (SK == KG_E4M3_F32SCALE) {
+        sdiv[c] = amax[c] == 0.0f ? 1.0f : amax[c] / 448.0f;
+      } else {
+        const int e = amax[c] == 0.0f ? 127 : e8m0_ceil(amax[c] / 448.0f);
+        eb[c] = (uint32_t)e;
+        mul[c] = __builtin_ldexpf(1.0f, 127 - e);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxRows; ++i) {
+      const int r = rg + kQRowGroups * i;
+      if (r < rows) {
+        uint32_t lo4 = 0, hi4 = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float y;
+          if constexpr (SK == KG_E4M3_F32SCALE)
+            y = v[i][c] / sdiv[c];
+          else
+            y = v[i][c] * mul[c];  // exact: a power of two
+          const uint32_t q = e4m3_rne(y);
+          if (c < 4)
+            lo4 |= q << (8 * c);
+          else
+            hi4 |= q << (8 * (c - 4));
+        }
+        *(uint2*)(p.Q + (t0 + r) * p.H + h0) = uint2{lo4, hi4};
+      }
+    }
+    if (rg == 0) {
+      if constexpr (SK == KG_E4M3_F32SCALE) {
+        float4* dst = (float4*)((float*)p.S + (int64_t)b * p.H + h0);
+        dst[0] = float4{sdiv[0], sdiv[1], sdiv[2], sdiv[3]};
+        dst[1] = float4{sdiv[4], sdiv[5], sdiv[6], sdiv[7]};
+      } else {
+        uint32_t lo4 = 0, hi4 = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (c < 4)
+            lo4 |= eb[c] << (8 * c);
+          else
+            hi4 |= eb[c] << (8 * (c - 4));
+        }
+        *(uint2*)((unsigned char*)p.S + (int64_t)b * p.H + h0) = uint2{lo4, hi4};
+      }
+    }
+  }
+}
+
+}  // namespace kg
+
+using namespace kg;
+
+extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int G, int H,
+                          int64_t K_total, int gran_k, int src, int scale_kind, void* Q, void* S,
+                          void* stream) {
+  if (src != KG_SRC_BF16 && src != KG_SRC_E4M3_1X128) return KG_ERR_DTYPE;
+  if (scale_kind != KG_E4M3_F32SCALE && scale_kind != KG_E4M3_UE8M0) return KG_ERR_DTYPE;
+  if (G < 0 || H < 0 || K_total < 0) return KG_ERR_SHAPE;
+  if (gran_k != 32 && gran_k != 128) return KG_ERR_GRAN;
+  if (G > kMaxGroups) return KG_ERR_UNSUPPORTED;
+  if (K_total > INT32_MAX || (int64_t)H * K_total > ((int64_t)1 << 46)) return KG_ERR_UNSUPPORTED;
+  if (G == 0 || H == 0) return KG_OK;
+  if (ks == nullptr) return KG_ERR_NULL;
+  if (K_total > 0 && (X == nullptr || Q == nullptr || S == nullptr)) return KG_ERR_NULL;
+  if (src == KG_SRC_E4M3_1X128 && K_total > 0 && xs == nullptr) return KG_ERR_NULL;
+  if (src == KG_SRC_BF16 && xs != nullptr) return KG_ERR_NULL;
+  if (H % 128 != 0) return KG_ERR_ALIGN;
+  if (((uintptr_t)X & 15) || ((uintptr_t)Q & 15) || ((uintptr_t)S & 15) || ((uintptr_t)xs & 3) ||
+      ((uintptr_t)ks & 3))
+    return KG_ERR_ALIGN;
+  const size_t qbytes = (size_t)K_total * H;
+  const size_t xbytes = qbytes * (src == KG_SRC_BF16 ? 2 : 1);
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || !na || !nb) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(X, xbytes, Q, qbytes) || overlap(S, 1, Q, qbytes) || overlap(X, xbytes, S, 1))
+    return KG_ERR_ALIAS;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return KG_ERR_HIP;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return KG_ERR_HIP;
+  QParams p;
+  p.X = (const unsigned char*)X;
+  p.xs = xs;
+  p.Q = (unsigned char*)Q;
+  p.S = S;
+  p.ks = ks;
+  p.G = G;
+  p.H = H;
+  p.K_total = K_total;
+  p.gran = gran_k;
+  // items are not known on the host (they depend on ks): enough persistent
+  // workgroups for the largest case, eight per CU
+  const int64_t max_items = ((K_total + (int64_t)G * (gran_k - 1)) / gran_k) * (H / 128);
+  const int grid = (int)(max_items < (int64_t)cus * 8 ? (max_items > 0 ? max_items : 1) : (int64_t)cus * 8);
+  const void* fn = src == KG_SRC_BF16
+                       ? (scale_kind == KG_E4M3_F32SCALE ? (const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_F32SCALE>
+                                                         : (const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_UE8M0>)
+                       : (scale_kind == KG_E4M3_F32SCALE ? (const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_F32SCALE>
+                                                         : (const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_UE8M0>);
+  void* args[] = {&p};
+  e = hipLaunchKernel(fn, dim3(grid), dim3(kQThreads), args, sched_bytes(G), (hipStream_t)stream);
+  if (e != hipSuccess) return KG_ERR_HIP;
+  return KG_OK;
+}

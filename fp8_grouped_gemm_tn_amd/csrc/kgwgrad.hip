@@ -1272,3 +1272,6 @@ extern "C" int kg_debug_offsets(const int32_t* ks, int G, int gran_k, int64_t* o
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return KG_OK;
 }
+
+// The requantiser shares this translation unit (and the device status word).
+#include "kg_requant.h"

@@ -160,6 +160,44 @@ int kg_debug_offsets(const int32_t* ks, int G, int gran_k, int64_t* off, int32_t
 /* Largest G accepted by kg_wgrad and kg_debug_offsets. */
 int kg_max_groups(void);
 
+/* Source kinds of kg_requant (argument `src`). */
+#define KG_SRC_BF16 0       /* X: bf16 [K_total, H]; xs must be NULL                       */
+#define KG_SRC_E4M3_1X128 1 /* X: e4m3fn bytes [K_total, H] with xs: fp32 [K_total, H/128],
+                               one scale per token per 128 channels (the forward pass's
+                               1x128 tiles)                                                */
+
+/*
+ * kg_requant -- enqueue the requantisation that produces kg_wgrad's fp8 operands
+ * (GitHub issue "Is DeepGEMM directly applicable to backward in training?",
+ * soundOfDestiny's comments of 2025-03-12: the weight-gradient GEMM needs scales per
+ * channel per 128 tokens, the forward pass keeps fp8 with per-token 1x128 scales, so
+ * a requantisation is inevitable).
+ *
+ *   Q [K_total, H] fp8 e4m3fn bytes and S [nblk, H] (fp32 for KG_E4M3_F32SCALE,
+ *   uint8 E8M0 for KG_E4M3_UE8M0), nblk = sum_g ceil(ks[g] / gran_k), such that
+ *   kg_wgrad(Q, S, ...) reads them as A (or B) and sa (or sb). For expert g's token
+ *   block kb (gran_k tokens from the expert's first token, the last one partial)
+ *   and channel h, with x the binary32 source value (bf16 widened, or the e4m3 value
+ *   times its token's 1x128 scale as one binary32 product) and amax the block's
+ *   largest |x|:
+ *     KG_E4M3_F32SCALE: s = amax / 448 (1 if amax == 0), q = e4m3(x / s), binary32
+ *                       quotients rounded to nearest;
+ *     KG_E4M3_UE8M0:    e = 127 + the smallest k with 2^k >= amax / 448, clamped to
+ *                       [0, 254] (127 if amax == 0), q = e4m3(x * 2^(127 - e));
+ *   e4m3() rounds to the nearest e4m3fn value, ties to the even code, saturating at
+ *   +-448 and keeping the sign.
+ *
+ *   scale_kind  KG_E4M3_F32SCALE or KG_E4M3_UE8M0; gran_k 32 or 128
+ *   H           a multiple of 128; X, Q, S 16-byte aligned
+ *
+ * Errors (before any launch): KG_ERR_DTYPE, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_NULL,
+ * KG_ERR_ALIGN, KG_ERR_ALIAS (X or S overlapping Q), KG_ERR_UNSUPPORTED (G > 1024),
+ * KG_ERR_HIP. A ks that does not add up to K_total is reported by kg_status
+ * (KG_ERR_KSUM) and nothing is written. G == 0 or H == 0: KG_OK, no launch.
+ */
+int kg_requant(const void* X, const float* xs, const int32_t* ks, int G, int H, int64_t K_total,
+               int gran_k, int src, int scale_kind, void* Q, void* S, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

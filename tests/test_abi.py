@@ -99,6 +99,36 @@ def test_workspace_entry_point_errors(kw, code):
     assert call_ws(**kw) == code
 
 
+def call_rq(X=FAKE, xs=None, ks=FAKE + (1 << 31), G=2, H=256, K=300, gran=128,
+            src=B.KG_SRC_BF16, kind=kg.KG_E4M3_F32SCALE, Q=FAKE + (1 << 32), S=FAKE + (1 << 33)):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.lib().kg_requant(v(X), v(xs), v(ks), G, H, K, gran, src, kind, v(Q), v(S), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(src=5), B.KG_ERR_DTYPE),
+    (dict(kind=kg.KG_BF16), B.KG_ERR_DTYPE),
+    (dict(G=-1), B.KG_ERR_SHAPE),
+    (dict(H=-128), B.KG_ERR_SHAPE),
+    (dict(gran=64), B.KG_ERR_GRAN),
+    (dict(G=1025), B.KG_ERR_UNSUPPORTED),
+    (dict(Q=None), B.KG_ERR_NULL),
+    (dict(ks=None), B.KG_ERR_NULL),
+    (dict(src=B.KG_SRC_E4M3_1X128), B.KG_ERR_NULL),      # 1x128 source without its scales
+    (dict(xs=FAKE), B.KG_ERR_NULL),                        # scales given for a bf16 source
+    (dict(H=192), B.KG_ERR_ALIGN),
+    (dict(Q=FAKE + (1 << 32) + 8), B.KG_ERR_ALIGN),
+    (dict(Q=FAKE + 4096), B.KG_ERR_ALIAS),                 # Q overlaps X
+])
+def test_requant_synchronous_errors(kw, code):
+    assert call_rq(**kw) == code
+
+
+def test_requant_empty_is_ok_without_launch():
+    assert call_rq(G=0) == B.KG_OK
+    assert call_rq(H=0) == B.KG_OK
+
+
 def test_empty_shapes_are_ok_without_launch():
     assert call(G=0) == B.KG_OK
     assert call(M=0) == B.KG_OK

@@ -1,0 +1,116 @@
+"""GPU parity of the requantiser (kg_requant, through the C ABI) against the CPU
+oracle: fp8 codes and scales must agree bit for bit (integer/byte work), for both
+sources (bf16; e4m3 with 1x128 per-token scales), both scale kinds and both block
+sizes, on ragged experts with empty ones, and on a larger routed shape."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_grouped_gemm_tn_amd as kg
+from oracle import kgref
+
+pytestmark = pytest.mark.gpu
+
+SRC = {kg.KG_SRC_BF16: kgref.SRC_BF16, kg.KG_SRC_E4M3_1X128: kgref.SRC_E4M3_1X128}
+KIND = {kg.KG_E4M3_F32SCALE: kgref.SCALE_F32, kg.KG_E4M3_UE8M0: kgref.SCALE_UE8M0}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def make_source(src, K, H, seed):
+    g = torch.Generator().manual_seed(seed)
+    if src == kg.KG_SRC_BF16:
+        x = torch.randn(K, H, generator=g)
+        x = torch.where(torch.rand(K, H, generator=g) < 0.01, x * 50, x)
+        x = torch.where(torch.rand(K, H, generator=g) < 0.01, torch.zeros_like(x), x)
+        xb = x.to(torch.bfloat16)
+        return xb, None, xb.view(torch.int16).numpy().view(np.uint16), None
+    codes = torch.randint(0, 256, (K, H), generator=g, dtype=torch.int32).to(torch.uint8)
+    codes = torch.where((codes & 0x7F) == 0x7F, torch.full_like(codes, 0x30), codes)
+    xs = torch.rand(K, H // 128, generator=g) * 0.01 + 1e-4
+    return codes, xs, codes.numpy(), xs.numpy()
+
+
+def run_case(src, kind, gran, ks, H, seed):
+    ks = np.asarray(ks, np.int32)
+    K = int(ks.sum())
+    nblk = int(sum((int(k) + gran - 1) // gran for k in ks))
+    X, xs, Xh, xsh = make_source(src, K, H, seed)
+    d = torch.device("cuda:0")
+    Xd = X.to(d)
+    xsd = None if xs is None else xs.to(d)
+    ksd = torch.from_numpy(ks).to(d)
+    sdt = torch.float32 if kind == kg.KG_E4M3_F32SCALE else torch.uint8
+    Q = torch.full((K, H), 0x5A, dtype=torch.uint8, device=d)
+    S = torch.full((nblk, H), 0x5A, dtype=torch.uint8, device=d).view(sdt) if sdt == torch.uint8 \
+        else torch.full((nblk, H), float("nan"), device=d)
+    rc = kg.kg_requant_raw(Xd, xsd, ksd, ks.size, H, K, gran, src, kind, Q, S)
+    assert rc == kg.KG_OK
+    assert kg.kg_status() == kg.KG_OK
+    rc, Qr, Sr = kgref.requant(Xh, xsh, ks, H, gran, SRC[src], KIND[kind])
+    assert rc == kgref.OK
+    Qg = Q.cpu().numpy()
+    Sg = S.cpu().numpy()
+    bad = np.nonzero(Qg != Qr)
+    assert bad[0].size == 0, f"{bad[0].size} fp8 codes differ, first at {bad[0][0], bad[1][0]}: " \
+                             f"{Qg[bad][0]:#x} vs {Qr[bad][0]:#x}"
+    assert np.array_equal(Sg.view(np.uint8), Sr.view(np.uint8)), "scales differ"
+
+
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("kind", [kg.KG_E4M3_F32SCALE, kg.KG_E4M3_UE8M0])
+@pytest.mark.parametrize("src", [kg.KG_SRC_BF16, kg.KG_SRC_E4M3_1X128])
+def test_requant_bit_exact_ragged(src, kind, gran):
+    say("requant", src, kind, gran)
+    run_case(src, kind, gran, [300, 0, 129, 1, 513, 64, 0], 384, seed=gran + 7 * kind + 31 * src)
+
+
+@pytest.mark.parametrize("kind", [kg.KG_E4M3_F32SCALE, kg.KG_E4M3_UE8M0])
+def test_requant_bit_exact_routed_shape(kind):
+    say("requant routed", kind)
+    rng = np.random.default_rng(5)
+    p = 1.0 / np.arange(1, 17) ** 1.2
+    ks = rng.multinomial(16384, p / p.sum()).astype(np.int32)
+    run_case(kg.KG_SRC_BF16, kind, 128 if kind == kg.KG_E4M3_F32SCALE else 32, ks, 1024, seed=9)
+
+
+def test_requant_ksum_mismatch_writes_nothing():
+    say("requant ksum")
+    d = torch.device("cuda:0")
+    X = torch.randn(100, 128, device=d).to(torch.bfloat16)
+    ks = torch.tensor([60, 30], dtype=torch.int32, device=d)
+    Q = torch.full((100, 128), 7, dtype=torch.uint8, device=d)
+    S = torch.full((2, 128), 3.0, device=d)
+    assert kg.kg_requant_raw(X, None, ks, 2, 128, 100, 128, kg.KG_SRC_BF16, kg.KG_E4M3_F32SCALE,
+                             Q, S) == kg.KG_OK
+    assert kg.kg_status() == kg.KG_ERR_KSUM
+    assert (Q == 7).all() and (S == 3.0).all()
+
+
+def test_requant_feeds_wgrad():
+    # the requantised operands run through kg_wgrad and match the oracle GEMM on them
+    say("requant -> wgrad")
+    d = torch.device("cuda:0")
+    ks = np.array([200, 0, 77], np.int32)
+    K, M, N = 277, 128, 256
+    g = torch.Generator().manual_seed(3)
+    a = torch.randn(K, M, generator=g).to(torch.bfloat16)
+    b = (torch.randn(K, N, generator=g) * 1e-3).to(torch.bfloat16)
+    ksd = torch.from_numpy(ks).to(d)
+    A, sa = kg.kg_requant(a.to(d), None, ksd, 128, kg.KG_E4M3_F32SCALE, 3)
+    B, sb = kg.kg_requant(b.to(d), None, ksd, 128, kg.KG_E4M3_F32SCALE, 3)
+    D = torch.empty((3, M, N), device=d)
+    kg.kg_wgrad(A, sa, B, sb, None, D, ksd, 128, kg.KG_E4M3_F32SCALE)
+    assert kg.kg_status() == kg.KG_OK
+    rc, Dr, bound = kgref.wgrad(A.cpu().numpy(), sa.cpu().numpy(), B.cpu().numpy(), sb.cpu().numpy(),
+                                None, ks, M, N, 128, kgref.E4M3_F32SCALE)
+    assert rc == kgref.OK
+    err = np.abs(D.cpu().numpy().astype(np.float64) - Dr)
+    assert (err <= 1e-5 * bound + 1e-6).all()
+    # and the fp8 product stays close to the bf16 one (quantisation error only)
+    ref = [a[:200].float().T @ b[:200].float(), torch.zeros(M, N), a[200:].float().T @ b[200:].float()]
+    for gi in (0, 2):
+        rel = (D[gi].cpu() - ref[gi]).norm() / ref[gi].norm()
+        assert rel < 0.1, float(rel)
