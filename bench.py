@@ -12,6 +12,15 @@ uniformly over three experts (the second expert gets none), D accumulated onto
 C. The other workloads (worked, zipf_fp8, ue8m0_many, local_share) are
 selectable with --workload.
 
+    python bench.py --requant NAME [--steps K] [--warmup W]
+
+times the requantiser (kg_requant) that produces a workload's fp8 operand instead:
+local_share_A (262144 x 7168 bf16 activations -> e4m3 + fp32 scales per 128 tokens),
+local_share_A_fp8 (the same activations stored as e4m3 with 1x128 per-token scales),
+ue8m0_many_B (131072 x 7168 bf16 gradients -> e4m3 + UE8M0 per 32 tokens). Its line
+reports GB/s of algorithmic traffic (source read, codes and scales written) against
+8 TB/s of HBM.
+
 The JSON line carries:
   value / ms_per_step     TFLOP/s of useful work 2*sum(K_g)*M*N over the timed steps
   roofline                the kernel's average launch time (HIP events on its
@@ -137,6 +146,115 @@ def cpu_baseline(case, budget_s=12.0):
                       f"{flops / 1e9:.2f} GFLOP in {t:.2f} s (fp64)"}
 
 
+REQUANT = {
+    # name: (routing workload, H, gran_k, scale kind, source, description)
+    "local_share_A": ("local_share", 7168, 128, 0, 0,
+                      "requantise local-share activations: 262144 x 7168 bf16 -> e4m3 + fp32 "
+                      "scales per 128 tokens of 8 experts ~N(32768,8192)"),
+    "local_share_A_fp8": ("local_share", 7168, 128, 0, 1,
+                          "requantise local-share activations stored as e4m3 with 1x128 per-token "
+                          "scales: 262144 x 7168 -> e4m3 + fp32 scales per 128 tokens"),
+    "ue8m0_many_B": ("ue8m0_many", 7168, 32, 1, 0,
+                     "requantise many-expert gradients: 131072 x 7168 bf16 -> e4m3 + UE8M0 "
+                     "scales per 32 tokens of 256 experts (51 empty)"),
+}
+
+
+def requant_main(args):
+    """Time kg_requant on one workload's operand; print one JSON line."""
+    import numpy as np
+    import torch
+    import fp8_grouped_gemm_tn_amd as kg
+    from fp8_grouped_gemm_tn_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl, H, gran, kind, src, descr = REQUANT[args.requant]
+    dev = torch.device("cuda:0")
+    ks = inputs.workload_ks(wl, args.seed)
+    K = int(ks.astype(np.int64).sum())
+    nblk = int(sum((int(k) + gran - 1) // gran for k in ks))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    x = torch.randn((K, H), generator=gen, device=dev)
+    if src == kg.KG_SRC_BF16:
+        X, xs = x.to(torch.bfloat16), None
+    else:  # the forward pass's copy: e4m3 with one fp32 scale per token per 128 channels
+        amax = x.abs().view(K, H // 128, 128).amax(dim=2).clamp_min(1e-30)
+        xs = (amax / 448.0).float()
+        X = (x.view(K, H // 128, 128) / xs[:, :, None]).view(K, H).to(torch.float8_e4m3fn)
+        X = X.view(torch.uint8)
+    del x
+    ksd = torch.from_numpy(ks).to(dev)
+    Q = torch.empty((K, H), dtype=torch.uint8, device=dev)
+    S = torch.empty((nblk, H), dtype=torch.float32 if kind == kg.KG_E4M3_F32SCALE else torch.uint8,
+                    device=dev)
+
+    def step():
+        rc = kg.kg_requant_raw(X, xs, ksd, ks.size, H, K, gran, src, kind, Q, S)
+        assert rc == kg.KG_OK, rc
+
+    for _ in range(args.warmup):
+        step()
+    assert kg.kg_status() == kg.KG_OK
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    assert kg.kg_status() == kg.KG_OK
+    avg_ms = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev)
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    nbytes = (K * H * (2 if src == kg.KG_SRC_BF16 else 1) + (0 if xs is None else xs.numel() * 4)
+              + K * H + nblk * H * (4 if kind == kg.KG_E4M3_F32SCALE else 1))
+    achieved = nbytes / (avg_ms / 1e3) / 1e9
+    line = {
+        "metric": "requantiser GB/s of algorithmic HBM traffic (source read + codes and scales "
+                  "written) + % of HBM roofline, 1 GPU",
+        "value": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 arithmetic, bf16/e4m3 in, e4m3 out",
+        "data": "synthetic (seeded N(0,1) values, the workload's seeded routing)",
+        "config": {"workload": descr, "tokens": K, "H": H, "G": int(ks.size), "gran_k": gran},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes},
+    }
+    if not args.no_cpu:
+        from oracle import kgref
+        # the oracle on the first expert's first blocks (all channels), ~10 s of CPU
+        g0 = int(np.argmax(ks > 0))
+        rows = min(int(ks[g0]), 4 * gran)
+        t0 = int(ks[:g0].astype(np.int64).sum())
+        Xr = X[t0:t0 + rows]
+        Xs = np.ascontiguousarray((Xr.view(torch.int16) if src == kg.KG_SRC_BF16 else Xr).cpu().numpy())
+        if src == kg.KG_SRC_BF16:
+            Xs = Xs.view(np.uint16)
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[t0:t0 + rows].cpu().numpy())
+        tt = time.perf_counter()
+        rc, _, _ = kgref.requant(Xs, sub(xs), [rows], H, gran,
+                                 kgref.SRC_BF16 if src == kg.KG_SRC_BF16 else kgref.SRC_E4M3_1X128,
+                                 kgref.SCALE_F32 if kind == kg.KG_E4M3_F32SCALE else kgref.SCALE_UE8M0)
+        dt = time.perf_counter() - tt
+        assert rc == kgref.OK
+        sb = rows * H * (2 if src == kg.KG_SRC_BF16 else 1) + rows * H
+        line["cpu_baseline"] = {"value": round(sb / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"expert {g0}, rows 0..{rows - 1}, all {H} channels: "
+                                          f"{sb / 1e6:.1f} MB in {dt:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,7 +272,15 @@ def main():
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "NAME"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) into "
                          "profiles/kg_wgrad_NAME_traffic.json")
+    ap.add_argument("--requant", choices=list(REQUANT),
+                    help="time the requantiser on this operand instead of the GEMM")
     args = ap.parse_args()
+    if args.requant:
+        if args.gpus != 1:
+            print("bench.py measures one GPU; run with --gpus 1.", file=sys.stderr)
+            sys.exit(2)
+        requant_main(args)
+        return
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
         return
