@@ -51,24 +51,37 @@ struct QParams {
 };
 
 // binary32 -> e4m3fn code: nearest value, ties to the even code, saturating at
-// +-448, sign kept, NaN -> 0x7F. Exact: scaling by powers of two and the
-// round-to-nearest-even of v_rndne_f32 introduce no other rounding.
+// +-448, sign kept, NaN -> 0x7F. Branch-free: with E the binary exponent of
+// min(|y|, 448) clamped to [-6, 8], the code is 8 * (E + 7) + rint(|y| * 2^(3 - E))
+// - 8 (exact: scaling by a power of two, then the round-to-nearest-even of
+// v_rndne_f32). E = -6 covers the subnormals (codes 0..8), and a mantissa that
+// rounds up to 16 carries into the exponent field by itself.
 __device__ inline uint32_t e4m3_rne(float y) {
   const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = __builtin_fabsf(y);
-  if (a != a) return 0x7Fu;
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;  // -6..8
-  int m8 = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - E));              // 8..16
-  if (m8 == 16) {
-    E += 1;
-    m8 = 8;
-  }
-  return sign | (uint32_t)(((E + 7) << 3) | (m8 - 8));
+  const float a = __builtin_fminf(__builtin_fabsf(y), 448.0f);
+  int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
+  E = E < -6 ? -6 : E;
+  const int m = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - E));
+  const uint32_t code = (uint32_t)(8 * (E + 7) + m - 8);
+  return y != y ? 0x7Fu : (((u >> 24) & 0x80u) | code);
+}
+
+// e4m3_rne(x / s) for the binary32 quotient fl(x / s), without a division in the
+// common case: y' = x * inv (inv = fl(1 / s)) differs from fl(x / s) by less than
+// 2^-18 of the e4m3 step at |y'|, so both round the same way unless y' lies within
+// 2^-16 of a step midpoint; only lanes with such a value take the exact division.
+__device__ inline uint32_t e4m3_rne_quotient(float x, float s, float inv) {
+  const float y = x * inv;
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const float a = __builtin_fminf(__builtin_fabsf(y), 448.0f);
+  int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
+  E = E < -6 ? -6 : E;
+  const float r = __builtin_ldexpf(a, 3 - E);  // |y| in e4m3 steps (exact)
+  const float m = __builtin_rintf(r);
+  uint32_t q = y != y ? 0x7Fu : (((u >> 24) & 0x80u) | (uint32_t)(8 * (E + 7) + (int)m - 8));
+  if (__builtin_fabsf(__builtin_fabsf(r - m) - 0.5f) < 1.52587890625e-05f)  // 2^-16
+    q = e4m3_rne(x / s);
+  return q;
 }
 
 // E8M0 byte of the smallest power of two >= r (r = amax / 448 > 0), clamped to
@@ -85,7 +98,11 @@ __device__ inline int e8m0_ceil(float r) {
   return e < 0 ? 0 : e > 254 ? 254 : e;
 }
 
-template <int SRC, int SK>
+// Layout of an item (scale row, channel tile): 16 channel groups of 8 channels
+// each form a 128-channel slab. gran_k = 128: one slab, 16 row groups (rows rg + 16i,
+// four waves), column maxima through LDS. gran_k = 32: four slabs, one per wave, 4
+// row groups per wave (rows rg + 4i): the maxima need only lane shuffles.
+template <int SRC, int SK, int GRAN>
 __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int64_t wsum_k[kMaxWaves];
@@ -96,12 +113,16 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
     if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
     return;
   }
+  constexpr int SLABS = GRAN == 32 ? 4 : 1;
+  constexpr int RG = GRAN == 32 ? 4 : kQRowGroups;  // row groups per slab
+  constexpr int kMaxRows = GRAN / RG;                // rows per thread
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int cg = tid % kQColGroups, rg = tid / kQColGroups;
-  const int ctiles = p.H / kQCols;
+  const int cg = tid % kQColGroups;
+  const int rg = GRAN == 32 ? lane / kQColGroups : tid / kQColGroups;
+  const int slab = GRAN == 32 ? w : 0;
+  const int ctiles = (p.H + kQCols * SLABS - 1) / (kQCols * SLABS);
   const int64_t nblk = s.boff[p.G];
   const int64_t total = nblk * ctiles;
-  constexpr int kMaxRows = 128 / kQRowGroups;  // rows per thread at gran 128
   for (int64_t item = blockIdx.x; item < total; item += gridDim.x) {
     const int b = (int)(item / ctiles), ct = (int)(item - (int64_t)b * ctiles);
     // expert of scale row b: the last g with boff[g] <= b (binary search; empty
@@ -117,75 +138,95 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
     const int g = lo;
     const int kb = b - s.boff[g];
     const int64_t t0 = s.off[g] + (int64_t)kb * p.gran;
-    const int rows = (int)min((int64_t)p.gran, s.off[g + 1] - t0);
-    const int h0 = ct * kQCols + cg * 8;
-    // load this thread's rows (rg, rg + 16, ...) of its 8 channels as binary32
+    const int h0 = (ct * SLABS + slab) * kQCols + cg * 8;
+    // rows of the block this thread's slab covers (none past the last channel)
+    const int rows = h0 < p.H ? (int)min((int64_t)GRAN, s.off[g + 1] - t0) : 0;
+    // this thread's rows (rg, rg + 16, ...) of its 8 channels: every load is issued
+    // before any is used, then the values are widened to binary32
+    constexpr int RAW = SRC == KG_SRC_BF16 ? 4 : 2;  // 32-bit words per row
+    uint32_t raw[kMaxRows][RAW];
+    float xsc[kMaxRows];
+#pragma unroll
+    for (int i = 0; i < kMaxRows; ++i) {
+      const int r = rg + RG * i;
+#pragma unroll
+      for (int k = 0; k < RAW; ++k) raw[i][k] = 0;
+      xsc[i] = 0.0f;
+      if (r < rows) {
+        const int64_t t = t0 + r;
+        if constexpr (SRC == KG_SRC_BF16) {
+          const v4i x = __builtin_nontemporal_load((const v4i*)(p.X + (t * p.H + h0) * 2));
+          raw[i][0] = (uint32_t)x.x;
+          raw[i][1] = (uint32_t)x.y;
+          raw[i][2] = (uint32_t)x.z;
+          raw[i][3] = (uint32_t)x.w;
+        } else {
+          const v2i x = __builtin_nontemporal_load((const v2i*)(p.X + t * p.H + h0));
+          raw[i][0] = (uint32_t)x.x;
+          raw[i][1] = (uint32_t)x.y;
+          xsc[i] = p.xs[t * (p.H / 128) + h0 / 128];
+        }
+      }
+    }
     float v[kMaxRows][8];
     float amax[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) amax[c] = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxRows; ++i) {
-      const int r = rg + kQRowGroups * i;
+      if constexpr (SRC == KG_SRC_BF16) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v[i][c] = 0.0f;
-      if (r < rows) {
-        const int64_t t = t0 + r;
-        if constexpr (SRC == KG_SRC_BF16) {
-          const uint4 x = *(const uint4*)(p.X + (t * p.H + h0) * 2);
-          const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[i][2 * k] = __builtin_bit_cast(float, wds[k] << 16);
-            v[i][2 * k + 1] = __builtin_bit_cast(float, wds[k] & 0xFFFF0000u);
-          }
-        } else {
-          const uint2 x = *(const uint2*)(p.X + t * p.H + h0);
-          const float sc = p.xs[t * (p.H / 128) + h0 / 128];
-          const uint32_t wds[2] = {x.x, x.y};
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            // e4m3 decode (exact, through bf16), then one binary32 product per value
-            const v2bf d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[k], 1.0f, false);
-            const v2bf d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[k], 1.0f, true);
-            v[i][4 * k + 0] = (float)d0[0] * sc;
-            v[i][4 * k + 1] = (float)d0[1] * sc;
-            v[i][4 * k + 2] = (float)d1[0] * sc;
-            v[i][4 * k + 3] = (float)d1[1] * sc;
-          }
+        for (int k = 0; k < 4; ++k) {
+          v[i][2 * k] = __builtin_bit_cast(float, raw[i][k] << 16);
+          v[i][2 * k + 1] = __builtin_bit_cast(float, raw[i][k] & 0xFFFF0000u);
         }
+      } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) amax[c] = __builtin_fmaxf(amax[c], __builtin_fabsf(v[i][c]));
+        for (int k = 0; k < 2; ++k) {
+          // e4m3 decode (exact, through bf16), then one binary32 product per value
+          const v2bf d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i][k], 1.0f, false);
+          const v2bf d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i][k], 1.0f, true);
+          v[i][4 * k + 0] = (float)d0[0] * xsc[i];
+          v[i][4 * k + 1] = (float)d0[1] * xsc[i];
+          v[i][4 * k + 2] = (float)d1[0] * xsc[i];
+          v[i][4 * k + 3] = (float)d1[1] * xsc[i];
+        }
       }
+      // rows past the block are zeros here: they leave the maxima unchanged
+#pragma unroll
+      for (int c = 0; c < 8; ++c) amax[c] = __builtin_fmaxf(amax[c], __builtin_fabsf(v[i][c]));
     }
     // column maxima: the 4 row groups of a wave share a channel group at lanes
-    // l, l + 16, l + 32, l + 48; then across the 4 waves through LDS
+    // l, l + 16, l + 32, l + 48; at gran_k 128 then across the 4 waves through LDS
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       amax[c] = __builtin_fmaxf(amax[c], __shfl_xor(amax[c], 16, 64));
       amax[c] = __builtin_fmaxf(amax[c], __shfl_xor(amax[c], 32, 64));
     }
-    if (lane < kQColGroups) {
+    if constexpr (GRAN == 128) {
+      if (lane < kQColGroups) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) red[w][cg * 8 + c] = amax[c];
+        for (int c = 0; c < 8; ++c) red[w][cg * 8 + c] = amax[c];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float m = red[0][cg * 8 + c];
+#pragma unroll
+        for (int ww = 1; ww < kQThreads / 64; ++ww) m = __builtin_fmaxf(m, red[ww][cg * 8 + c]);
+        amax[c] = m;
+      }
+      __syncthreads();  // red is rewritten by the next item
     }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float m = red[0][cg * 8 + c];
-#pragma unroll
-      for (int ww = 1; ww < kQThreads / 64; ++ww) m = __builtin_fmaxf(m, red[ww][cg * 8 + c]);
-      amax[c] = m;
-    }
-    __syncthreads();  // red is rewritten by the next item
     // scales and codes
-    float mul[8];   // UE8M0: 2^(127 - e)
+    float mul[8];   // UE8M0: 2^(127 - e); fp32 scales: 1 / s
     float sdiv[8];  // fp32 scales: s
     uint32_t eb[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if constexpr (SK == KG_E4M3_F32SCALE) {
         sdiv[c] = amax[c] == 0.0f ? 1.0f : amax[c] / 448.0f;
+        mul[c] = 1.0f / sdiv[c];
       } else {
         const int e = amax[c] == 0.0f ? 127 : e8m0_ceil(amax[c] / 448.0f);
         eb[c] = (uint32_t)e;
@@ -194,17 +235,16 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
     }
 #pragma unroll
     for (int i = 0; i < kMaxRows; ++i) {
-      const int r = rg + kQRowGroups * i;
+      const int r = rg + RG * i;
       if (r < rows) {
         uint32_t lo4 = 0, hi4 = 0;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          float y;
+          uint32_t q;
           if constexpr (SK == KG_E4M3_F32SCALE)
-            y = v[i][c] / sdiv[c];
+            q = e4m3_rne_quotient(v[i][c], sdiv[c], mul[c]);
           else
-            y = v[i][c] * mul[c];  // exact: a power of two
-          const uint32_t q = e4m3_rne(y);
+            q = e4m3_rne(v[i][c] * mul[c]);  // exact: a power of two
           if (c < 4)
             lo4 |= q << (8 * c);
           else
@@ -213,7 +253,7 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
         *(uint2*)(p.Q + (t0 + r) * p.H + h0) = uint2{lo4, hi4};
       }
     }
-    if (rg == 0) {
+    if (rg == 0 && h0 < p.H) {
       if constexpr (SK == KG_E4M3_F32SCALE) {
         float4* dst = (float4*)((float*)p.S + (int64_t)b * p.H + h0);
         dst[0] = float4{sdiv[0], sdiv[1], sdiv[2], sdiv[3]};
@@ -281,13 +321,21 @@ extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int
   p.gran = gran_k;
   // items are not known on the host (they depend on ks): enough persistent
   // workgroups for the largest case, eight per CU
-  const int64_t max_items = ((K_total + (int64_t)G * (gran_k - 1)) / gran_k) * (H / 128);
-  const int grid = (int)(max_items < (int64_t)cus * 8 ? (max_items > 0 ? max_items : 1) : (int64_t)cus * 8);
-  const void* fn = src == KG_SRC_BF16
-                       ? (scale_kind == KG_E4M3_F32SCALE ? (const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_F32SCALE>
-                                                         : (const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_UE8M0>)
-                       : (scale_kind == KG_E4M3_F32SCALE ? (const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_F32SCALE>
-                                                         : (const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_UE8M0>);
+  const int tile = gran_k == 32 ? 512 : 128;  // channels per item
+  const int64_t max_items = ((K_total + (int64_t)G * (gran_k - 1)) / gran_k) * ((H + tile - 1) / tile);
+  const int64_t wgs = (int64_t)cus * 32;
+  const int grid = (int)(max_items < wgs ? (max_items > 0 ? max_items : 1) : wgs);
+  const void* fns[2][2][2] = {
+      {{(const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_F32SCALE, 32>,
+        (const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_F32SCALE, 128>},
+       {(const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_UE8M0, 32>,
+        (const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_UE8M0, 128>}},
+      {{(const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_F32SCALE, 32>,
+        (const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_F32SCALE, 128>},
+       {(const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_UE8M0, 32>,
+        (const void*)kg_requant_kernel<KG_SRC_E4M3_1X128, KG_E4M3_UE8M0, 128>}}};
+  const void* fn = fns[src == KG_SRC_BF16 ? 0 : 1][scale_kind == KG_E4M3_F32SCALE ? 0 : 1]
+                      [gran_k == 32 ? 0 : 1];
   void* args[] = {&p};
   e = hipLaunchKernel(fn, dim3(grid), dim3(kQThreads), args, sched_bytes(G), (hipStream_t)stream);
   if (e != hipSuccess) return KG_ERR_HIP;
