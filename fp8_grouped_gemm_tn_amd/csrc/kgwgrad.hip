@@ -1058,7 +1058,6 @@ static Launch launch_of() {
                 CF::BN, CF::THREADS};
 }
 
-// small: half tiles for problems with few full tiles; split: stream-K (bf16 only)
 // small: half tiles (bf16) for problems with few full tiles; split: stream-K over the
 // full-size tiles
 static Launch pick(int kind, bool fast, bool small = false, bool split = false) {
