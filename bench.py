@@ -117,6 +117,24 @@ def ingest_counters(fetch_csv, write_csv, name):
     print(json.dumps(rec))
 
 
+def warm_up(step, warmup, seconds=1.0):
+    """Run `warmup` untimed steps; with None, as many as fit in `seconds` (at least
+    10). Returns the number run."""
+    import torch
+    if warmup is not None:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        return warmup
+    n, t0 = 0, time.perf_counter()
+    while n < 10 or time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The oracle as it is, on a bounded sample of the workload's rows."""
     from oracle import kgref
@@ -193,8 +211,7 @@ def requant_main(args):
         rc = kg.kg_requant_raw(X, xs, ksd, ks.size, H, K, gran, src, kind, Q, S)
         assert rc == kg.KG_OK, rc
 
-    for _ in range(args.warmup):
-        step()
+    args.warmup = warm_up(step, args.warmup)
     assert kg.kg_status() == kg.KG_OK
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -258,8 +275,10 @@ def requant_main(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: as many as fit in "
+                         "about one second, so that the GPU clocks have settled)")
     ap.add_argument("--workload", default="bf16", choices=list(DESCR))
     ap.add_argument("--fast", action="store_true", help="fp8 kinds: contract with the fp8 MFMA")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -317,8 +336,7 @@ def main():
         kg.kg_wgrad(A, sa, B, sb, C, D, ks, case.gran_k, dtype, K_total=case.K_total,
                     workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
+    args.warmup = warm_up(step, args.warmup)
     assert kg.kg_status() == kg.KG_OK
     torch.cuda.synchronize()
 

@@ -12,8 +12,11 @@
 // Design (MI355X-first, not the pages' TMA design):
 //  * One persistent launch. Every workgroup rebuilds the schedule in LDS
 //    (kg_sched.h) and walks work items (expert, m-tile, n-tile), longest experts
-//    first. Items are dealt so that the workgroups of one XCD take neighbouring
-//    tiles of one expert and share their operand rows in that XCD's L2.
+//    first. The hardware places workgroup b on XCD b % 8. When the items take
+//    several rounds of the grid, each XCD's workgroups take a contiguous run of
+//    neighbouring tiles of one expert and share their operand rows in that XCD's
+//    L2; a single round is dealt round-robin, so that GEMM and fill items spread
+//    over all eight L2s.
 //  * Empty experts become copy/fill items (D = C, or 0).
 //  * Operands move global -> LDS with buffer loads that write LDS directly; token
 //    rows past the expert's end are outside the buffer's range and read as zero,
@@ -888,10 +891,13 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   }
   const int T = p.tiles_m * p.tiles_n;
   const int grid = gridDim.x;
-  // XCD-aware deal: workgroup b runs on XCD b % 8; give each XCD a contiguous run
-  // of work so its workgroups share operand rows in its L2.
+  // Workgroup b runs on XCD b % 8. With several rounds of items, each XCD takes a
+  // contiguous run of every round (neighbouring tiles that share operand rows in
+  // its L2). A single round is dealt round-robin instead: all eight L2s then serve
+  // GEMM tiles (measured faster on MI355X when the round also holds fill items).
   const int b = blockIdx.x;
-  const int slot = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
+  const bool one_round = (int64_t)p.G * p.tiles_m * p.tiles_n <= grid;
+  const int slot = (grid % 8 == 0 && !one_round) ? (b % 8) * (grid / 8) + b / 8 : b;
   const LoadOffsets<CF> lo = load_offsets<CF>(p);
 
   if constexpr (SPLIT) {
