@@ -9,7 +9,8 @@ before the timed region. Prints one JSON line.
 
 Default workload: bf16, G = 4 experts, M = 1024, N = 2048, 16384 tokens routed
 uniformly over three experts (the second expert gets none), D accumulated onto
-C. The other workloads (worked, zipf_fp8, ue8m0_many, local_share) are
+C. The other workloads (worked, zipf_fp8, ue8m0_many, local_share, and the six
+non-grouped shapes single_m{m}_n{n}_k{k} of the issue page's 1D1D table) are
 selectable with --workload.
 
     python bench.py --requant NAME [--steps K] [--warmup W]
@@ -53,6 +54,11 @@ DESCR = {
     "ue8m0_many": "many experts UE8M0: G=256 (51 empty), M=2048, N=7168, 131072 tokens top-8, fp8 e4m3 + E8M0 per 32, no C",
     "local_share": "local expert share: G=8, M=7168, N=4096, 262144 tokens ~N(32768,8192), fp8 e4m3 + fp32 scales per 128, D += C",
 }
+for _m, _n, _k in ((4096, 2112, 7168), (4096, 24576, 1536), (4096, 32768, 512),
+                   (4096, 7168, 16384), (4096, 4096, 7168), (4096, 7168, 2048)):
+    DESCR[f"single_m{_m}_n{_n}_k{_k}"] = (
+        f"non-grouped 1D1D shape of the issue page's table: G=1, M={_m}, N={_n}, {_k} tokens, "
+        f"fp8 e4m3 + fp32 scales per 128, no C")
 
 
 def kernel_source_hash():

@@ -1205,15 +1205,21 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
   if (rc != KG_OK) return rc;
   // bf16 problems with fewer than two full 256 x 256 tiles per CU use half tiles.
   // When even then at most half of the CUs would get a tile, and a workspace is
-  // given, the tiles' token ranges are cut across all CUs instead (stream-K).
+  // given (and G <= 64), the tiles' token ranges are cut across all CUs instead
+  // (stream-K).
   auto tiles_of = [&](const Launch& l) {
     return (int64_t)G * ((M + l.bm - 1) / l.bm) * ((N + l.bn - 1) / l.bn);
   };
   const int64_t big_tiles = tiles_of(pick(BF16, false));
   const bool small = kind == BF16 && big_tiles < 2 * (int64_t)cus;
+  // Stream-K also when whole rounds of tiles would leave more than 30% of the
+  // grid idle (e.g. 272 tiles on 256 CUs); the default bf16 problem's 192 half
+  // tiles (75% of one round) stay whole: its partial-tile hand-off measured slower.
+  const int64_t T = tiles_of(pick(kind, fast, small));
+  const int64_t rounds = (T + cus - 1) / cus;
   const bool split = workspace != nullptr && G <= kMaxSplitGroups &&
                      (size_t)workspace_bytes >= split_ws_bytes(cus) &&
-                     2 * tiles_of(pick(kind, fast, small)) <= (int64_t)cus;
+                     (2 * T <= (int64_t)cus || 10 * T < 7 * rounds * (int64_t)cus);
   const Launch L = pick(kind, fast, small && !split, split);
   const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
   const int64_t total = (int64_t)G * tiles_m * tiles_n;

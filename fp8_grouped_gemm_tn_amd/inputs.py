@@ -18,6 +18,11 @@ Workloads (named by what they are):
                  power-of-two scales per 32 tokens, no C.
   local_share  - G = 8, M = 7168, N = 4096, 262144 tokens with per-expert counts drawn
                  from N(32768, 8192), clipped at 0 and rescaled, values as zipf_fp8.
+  single_m{m}_n{n}_k{k} - one group (G = 1): the six non-grouped fp8 GEMM shapes
+                 (m, n, k) of the GitHub issue page's 1D1D kernel table (thefacetakt,
+                 2025-03-20), mapped onto this operation as M = m, N = n and k
+                 contraction tokens; A, B ~ N(0,1), fp8 + fp32 scales per 128 tokens
+                 (the table's 1x128 scales on both operands), no C.
 
 Quantiser (input preparation, not part of the measured path): for each run of
 gran_k tokens of one expert (runs restart at each expert's first token) and each
@@ -211,11 +216,21 @@ def make_case(name, ks, M, N, dtype, gran_k=128, with_c=True, seed=0, device="cp
                 meta=dict(seed=seed, device=str(dev)))
 
 
-WORKLOADS = ("worked", "bf16", "zipf_fp8", "ue8m0_many", "local_share")
+# (m, n, k) of the issue page's non-grouped 1D1D fp8 GEMM table
+SINGLE_SHAPES = ((4096, 2112, 7168), (4096, 24576, 1536), (4096, 32768, 512),
+                 (4096, 7168, 16384), (4096, 4096, 7168), (4096, 7168, 2048))
+
+
+def single_name(m, n, k):
+    return f"single_m{m}_n{n}_k{k}"
+
+
+SINGLE = {single_name(*mnk): mnk for mnk in SINGLE_SHAPES}
+WORKLOADS = ("worked", "bf16", "zipf_fp8", "ue8m0_many", "local_share") + tuple(SINGLE)
 
 
 def workload(name, device="cpu", seed=0):
-    """The five named workloads (see the module docstring)."""
+    """The named workloads (see the module docstring)."""
     if name == "worked":
         return make_case(name, ks_worked(), 64, 128, E4M3_F32SCALE, 128, with_c=False,
                          seed=seed, device=device)
@@ -235,11 +250,17 @@ def workload(name, device="cpu", seed=0):
         ks = ks_normal(262144, 8, 32768.0, 8192.0, seed)
         return make_case(name, ks, 7168, 4096, E4M3_F32SCALE, 128, with_c=True, seed=seed,
                          device=device, b_std=1e-3, a_outlier_p=0.01)
+    if name in SINGLE:
+        m, n, k = SINGLE[name]
+        return make_case(name, np.array([k], np.int32), m, n, E4M3_F32SCALE, 128, with_c=False,
+                         seed=seed, device=device)
     raise KeyError(name)
 
 
 def workload_ks(name, seed=0):
     """Routing of a named workload without generating its values."""
+    if name in SINGLE:
+        return np.array([SINGLE[name][2]], np.int32)
     return {
         "worked": lambda: ks_worked(),
         "bf16": lambda: ks_uniform_with_empty(16384, 4, [1], seed),

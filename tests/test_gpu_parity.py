@@ -395,3 +395,24 @@ def test_full_size_workloads_sampled(name):
         sampled_check(case, t, D, fast=True)
     del D, t, case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", list(inputs.SINGLE))
+def test_single_group_issue_shapes_sampled(name):
+    """The issue page's non-grouped 1D1D shapes as one group (ragged N tiles for
+    n = 2112, 512-token and 16384-token contractions), in the launch configuration
+    bench.py times (with the stream-K workspace)."""
+    say("single group", name)
+    case = inputs.workload(name, device="cuda")
+    t = to_dev(case)
+    ws = kg.new_workspace(dev())
+    D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev())
+    for flags in (0, FAST):
+        kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], None, D, t["ks"], case.gran_k,
+                    case.dtype | flags, K_total=case.K_total, workspace=ws)
+        assert kg.kg_status() == kg.KG_OK
+        torch.cuda.synchronize()
+        assert torch.isfinite(D).all()
+        sampled_check(case, t, D, fast=bool(flags))
+    del D, t, case, ws
+    torch.cuda.empty_cache()
