@@ -81,6 +81,41 @@ double kgref_bf16(uint16_t bits) {
   return (double)f;
 }
 
+/* Nearest bf16 to v, from the format's definition (binary32's exponent range,
+ * 8 significant bits): with q the spacing of bf16 values at |v| (2^(e-7) for
+ * 2^e <= |v| < 2^(e+1), e >= -126; 2^-133 below 2^-126), |v| / q is rounded to
+ * the nearest integer, ties to the even one; results of 2^128 or more become
+ * infinity; the sign follows v; NaN gives the quiet NaN code 0x7FC0. This is
+ * the rounding of the bf16 output variant of the GEMM (the how-to page's FP8
+ * example allocates a bf16 D). The rounding is done once, from fp64, not through
+ * binary32. */
+uint16_t kgref_bf16_round(double v) {
+  if (isnan(v)) return 0x7FC0;
+  const uint16_t sign = signbit(v) ? 0x8000 : 0;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int x;
+  frexp(a, &x); /* a = f * 2^x, f in [0.5, 1): 2^(x-1) <= a < 2^x */
+  const int e = x - 1;
+  const double q = e < -126 ? ldexp(1.0, -133) : ldexp(1.0, e - 7);
+  const double n = a / q; /* exact: q is a power of two */
+  double r = floor(n);
+  const double frac = n - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  const double val = r * q;
+  if (val >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+  /* val has at most 8 significant bits inside binary32's range: the binary32
+   * conversion is exact and its low 16 bits are zero */
+  const float f = (float)val;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (u >> 16));
+}
+
+void kgref_bf16_round_array(const double* v, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kgref_bf16_round(v[i]);
+}
+
 /* ---------------------------------------------------------------- checks */
 
 int kgref_validate(const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k, int dtype) {

@@ -44,6 +44,12 @@ double kgref_e4m3(uint8_t byte);
 double kgref_e8m0(uint8_t byte);
 double kgref_bf16(uint16_t bits);
 
+/* Rounding of the bf16 output variant: the nearest bf16 code to v (ties to the
+ * even code, 2^128 and beyond to infinity, NaN to 0x7FC0), rounded once from
+ * fp64. The array form rounds n values. */
+uint16_t kgref_bf16_round(double v);
+void kgref_bf16_round_array(const double* v, uint16_t* out, int64_t n);
+
 /* Argument checks: shapes >= 0, known dtype, gran_k in {32,128} for fp8,
  * every ks[g] >= 0 and sum(ks) == K_total. */
 int kgref_validate(const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k, int dtype);

@@ -52,6 +52,10 @@ def lib():
         L.kgref_last_threads.argtypes = []
         L.kgref_e4m3_encode.restype = ctypes.c_uint8
         L.kgref_e4m3_encode.argtypes = [ctypes.c_double]
+        L.kgref_bf16_round.restype = ctypes.c_uint16
+        L.kgref_bf16_round.argtypes = [ctypes.c_double]
+        L.kgref_bf16_round_array.restype = None
+        L.kgref_bf16_round_array.argtypes = [vp, vp, i64]
         L.kgref_requant.restype = ctypes.c_int
         L.kgref_requant.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, vp, vp]
@@ -179,3 +183,17 @@ def requant(X, xs, ks, H, gran_k, src, scale_kind, K_total=None):
     rc = lib().kgref_requant(_ptr(X), _ptr(xs), _ptr(ks) if G > 0 else None, G, H, K_total,
                              gran_k, src, scale_kind, _ptr(Q), _ptr(S))
     return rc, Q, S
+
+
+def bf16_round(v):
+    """Nearest bf16 codes (uint16) to the fp64 values v (kgref_bf16_round)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().kgref_bf16_round_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def bf16_value(codes):
+    """fp64 values of bf16 codes (kgref_bf16, elementwise)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint16)
+    return (c.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

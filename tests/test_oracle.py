@@ -440,3 +440,73 @@ def test_sampled_equals_full_and_threads_do_not_matter():
                             g_range=(1, 3), m_range=(4, 9))
     assert rc == kgref.OK
     np.testing.assert_array_equal(Dp, D1[1:3, 4:9])
+
+
+# ---------------------------------------------------------------- bf16 output rounding
+
+# (value, code) from the bf16 format: 1 = 0x3F80 and the spacing just above 1 is
+# 2^-7; 1 + 2^-8 is the midpoint of 0x3F80 and 0x3F81 (tie -> even 0x3F80);
+# 1 + 3*2^-8 is the midpoint of 0x3F81 and 0x3F82 (tie -> even 0x3F82); the
+# smallest subnormal is 2^-133 (0x0001), its half is a tie with zero (-> 0x0000),
+# 1.5 * 2^-133 ties between 0x0001 and 0x0002 (-> 0x0002); the midpoint between the
+# largest finite value (2 - 2^-7) * 2^127 = 0x7F7F and 2^128 ties to the even
+# code, which is 2^128 itself, i.e. infinity (0x7F80).
+BF16_LANDMARKS = [
+    (1.0, 0x3F80), (-2.5, 0xC020), (1 + 2.0 ** -8, 0x3F80), (1 + 3 * 2.0 ** -8, 0x3F82),
+    (1 + 2.0 ** -8 + 2.0 ** -40, 0x3F81), (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000),
+    (1.5 * 2.0 ** -133, 0x0002), (2.0 ** 128 * (1 - 2.0 ** -9), 0x7F80),
+    ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F), (-0.0, 0x8000), (0.0, 0x0000),
+    (float("inf"), 0x7F80), (float("-inf"), 0xFF80),
+]
+
+
+@pytest.mark.parametrize("v,code", BF16_LANDMARKS)
+def test_bf16_round_landmarks(v, code):
+    assert kgref.lib().kgref_bf16_round(v) == code
+
+
+def test_bf16_round_nan():
+    c = kgref.lib().kgref_bf16_round(float("nan"))
+    assert (c & 0x7F80) == 0x7F80 and (c & 0x007F) != 0
+
+
+def test_bf16_round_matches_torch_on_binary32_inputs():
+    # binary32 inputs round once either way, so torch's float32 -> bfloat16
+    # conversion (round to nearest even) is an independent check
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(20000) * 1e-39).astype(np.float32),        # subnormals
+        (rng.standard_normal(20000) * 1e38).astype(np.float32),
+        # exact midpoints between neighbouring bf16 values
+        ((rng.integers(0x0001, 0x7F7F, 20000).astype(np.uint32) << 16) | 0x8000).view(np.float32),
+    ])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = kgref.bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_round_once_from_fp64_not_through_binary32():
+    # just above a midpoint by less than binary32's resolution: binary32 rounding
+    # first would land on the midpoint and then go to the even code
+    base = (np.arange(0x3F00, 0x4100, 2, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    spacing = 2.0 ** (np.floor(np.log2(base)) - 7)
+    v = base + spacing / 2 + spacing * 2.0 ** -30
+    got = kgref.bf16_round(v)
+    even = (base.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(got, even + 1)
+    assert np.array_equal(kgref.bf16_round(base + spacing / 2), even)
+
+
+def test_bf16_round_is_monotone_and_nearest():
+    rng = np.random.default_rng(3)
+    v = np.sort(rng.standard_normal(100000) * 10.0)
+    c = kgref.bf16_round(v)
+    val = kgref.bf16_value(c)
+    assert (np.diff(val) >= 0).all()
+    # nearest: no bf16 value lies strictly closer (neighbour codes one step away)
+    pos = v > 0
+    up = kgref.bf16_value(np.where(pos, c + 1, c - 1).astype(np.uint16))
+    dn = kgref.bf16_value(np.where(pos, c - 1, c + 1).astype(np.uint16))
+    err = np.abs(val - v)
+    assert (err <= np.abs(up - v)).all() and (err <= np.abs(dn - v)).all()
