@@ -70,9 +70,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def counters_for(workload, fast):
+def counters_for(workload, fast, bf16_out=False):
     """HBM bytes per launch measured with rocprofv3 counters for this kernel source."""
-    path = os.path.join(ROOT, "profiles", f"kg_wgrad_{workload}{'_fast' if fast else ''}_traffic.json")
+    name = f"{workload}{'_fast' if fast else ''}{'_bf16out' if bf16_out else ''}"
+    path = os.path.join(ROOT, "profiles", f"kg_wgrad_{name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -288,6 +289,8 @@ def main():
     ap.add_argument("--workload", default="bf16", choices=list(DESCR))
     ap.add_argument("--fast", action="store_true", help="fp8 kinds: contract with the fp8 MFMA")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--bf16-out", action="store_true",
+                    help="the bf16-output variant: C and D in bf16 (KG_FLAG_D_BF16)")
     ap.add_argument("--no-workspace", action="store_true",
                     help="call kg_wgrad without a workspace (no stream-K split of small problems)")
     ap.add_argument("--seed", type=int, default=0)
@@ -330,8 +333,11 @@ def main():
     case = inputs.workload(args.workload, device="cuda", seed=args.seed)
     A, B = case.A, case.B
     sa, sb, C = case.sa, case.sb, case.C
+    out_dtype = torch.bfloat16 if args.bf16_out else torch.float32
+    if C is not None and args.bf16_out:
+        C = C.to(torch.bfloat16)
     ks = torch.from_numpy(case.ks).to(dev)
-    D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev)
+    D = torch.empty((case.G, case.M, case.N), dtype=out_dtype, device=dev)
     flags = kg.KG_FLAG_FP8_MFMA if (args.fast and case.dtype != kg.KG_BF16) else 0
     dtype = case.dtype | flags
     # the library's workspace (zeroed once, left zeroed by every call), allocated
@@ -364,7 +370,7 @@ def main():
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
 
     flops = case.flops
-    nbytes = case.algorithmic_bytes()
+    nbytes = case.algorithmic_bytes(2 if args.bf16_out else 4)
     is_bf16 = case.dtype == kg.KG_BF16
     mfma_peak = PEAK["bf16"] if is_bf16 else PEAK["fp8"]
     t_mfma = flops / (mfma_peak * 1e12)
@@ -377,7 +383,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = counters_for(args.workload, bool(flags))
+    roof["traffic"] = counters_for(args.workload, bool(flags), args.bf16_out)
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     roof["roofline_ms"] = round(max(t_mfma, t_hbm) * 1e3, 4)
@@ -399,7 +405,8 @@ def main():
         "data": "synthetic (seeded generators, fp8 values quantised per 128/32-token block)",
         "config": {"workload": DESCR[args.workload], "G": case.G, "M": case.M, "N": case.N,
                    "tokens": case.K_total, "gran_k": case.gran_k if not is_bf16 else None,
-                   "fp8_mfma": bool(flags), "workspace": ws is not None},
+                   "fp8_mfma": bool(flags), "workspace": ws is not None,
+                   "d_dtype": "bf16" if args.bf16_out else "fp32"},
         "roofline": roof,
         "pct_fp8_peak": round(100.0 * value / PEAK["fp8"], 2),
         "hbm_gbs": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),

@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(PKG, "libkgwgrad.so")
 
 KG_E4M3_F32SCALE, KG_E4M3_UE8M0, KG_BF16 = 0, 1, 2
 KG_FLAG_FP8_MFMA = 0x100
+KG_FLAG_D_BF16 = 0x200
 KG_OK = 0
 KG_ERR_NULL, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_DTYPE = -1, -2, -3, -4
 KG_ERR_ALIGN, KG_ERR_ALIAS, KG_ERR_UNSUPPORTED, KG_ERR_HIP, KG_ERR_KSUM = -5, -6, -7, -8, -9
@@ -111,8 +112,14 @@ def new_workspace(device=None):
 def kg_wgrad(A, sa, B, sb, C, D, ks, gran_k, dtype, K_total=None, stream=None, workspace=None):
     """D = C + K-grouped A^T B. Shapes are read from the tensors:
     A [K_total, M], B [K_total, N], D [G, M, N], ks [G] int32 (all on the GPU).
-    `workspace` (from new_workspace) lets small bf16 problems use every CU."""
+    A bfloat16 D (and C) selects the bf16-output variant (KG_FLAG_D_BF16).
+    `workspace` (from new_workspace) lets problems with few tiles use every CU."""
+    import torch
     G, M, N = D.shape
+    if D.dtype == torch.bfloat16:
+        dtype |= KG_FLAG_D_BF16
+    if C is not None and C.dtype != D.dtype:
+        raise TypeError("C and D must have the same dtype")
     if K_total is None:
         K_total = A.shape[0]
     if workspace is None:

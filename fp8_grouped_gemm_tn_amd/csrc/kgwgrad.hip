@@ -64,10 +64,11 @@ struct Params {
   const unsigned char* sa;
   const unsigned char* B;
   const unsigned char* sb;
-  const float* C;
-  float* D;
+  const float* C;  // bf16 [G, M, N] in the bf16-output kernels
+  float* D;        // bf16 [G, M, N] in the bf16-output kernels
   const int32_t* ks;
   int G, M, N;
+
   int64_t K_total;
   int gran;  // tokens per scale row
   int tiles_m, tiles_n;
@@ -202,12 +203,65 @@ __device__ inline void wait_stages(int n) {
     wait_stages_n<CF::PER, CF::NS>(n);
 }
 
+// ---------------------------------------------------------------- bf16 output
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// four bf16 codes (two per dword, lower half first) -> fp32, exact
+__device__ inline v4f bf16x4_to_f32(v2u x) {
+  return v4f{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
+             __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u)};
+}
+
+// fp32 -> four bf16 codes, rounded to nearest, ties to even
+__device__ inline v2u f32x4_to_bf16(v4f v) {
+  return __builtin_bit_cast(v2u, __builtin_convertvector(v, v4bf));
+}
+
 // ---------------------------------------------------------------- fill
 
 // D tile = C tile (or 0) for an empty expert.
 template <class CF>
+__device__ void fill_tile_bf16(const Params& p, int g, int m0, int n0) {
+  const int t = threadIdx.x;
+  constexpr int kCols8 = CF::BN / 8;  // 16-byte runs of 8 bf16 per tile row
+  constexpr int kPer = CF::BM * kCols8 / CF::THREADS;
+  constexpr int kBatch = kPer < 16 ? kPer : 16;
+  static_assert(kPer % kBatch == 0, "fill batches");
+  const size_t base = (size_t)g * p.M * p.N;
+  const unsigned short* C = (const unsigned short*)p.C;
+  unsigned short* D = (unsigned short*)p.D;
+#pragma unroll
+  for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+    v4u v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int e = t + CF::THREADS * (b0 + k);
+      const int r = e / kCols8, c8 = e - r * kCols8;
+      const int m = m0 + r, n = n0 + 8 * c8;
+      v[k] = v4u{0u, 0u, 0u, 0u};
+      if (C && m < p.M && n < p.N)
+        v[k] = __builtin_nontemporal_load((const v4u*)(C + base + (size_t)m * p.N + n));
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int e = t + CF::THREADS * (b0 + k);
+      const int r = e / kCols8, c8 = e - r * kCols8;
+      const int m = m0 + r, n = n0 + 8 * c8;
+      if (m < p.M && n < p.N)
+        __builtin_nontemporal_store(v[k], (v4u*)(D + base + (size_t)m * p.N + n));
+    }
+  }
+}
+
+template <class CF, bool OUTB = false>
 __device__ void fill_tile(const Params& p, int g, int m0, int n0) {
   if (p.C == p.D) return;  // in place: D already holds C
+  if constexpr (OUTB) {
+    fill_tile_bf16<CF>(p, g, m0, n0);
+    return;
+  }
   const int t = threadIdx.x;
   constexpr int kCols4 = CF::BN / 4;
   constexpr int kPer = CF::BM * kCols4 / CF::THREADS;
@@ -354,7 +408,7 @@ __device__ inline void store_tile_parts(const Params& p, unsigned char* lds, int
 // the C tile goes global -> LDS by buffer loads (rows past M read as zero) while
 // the waves owning the pass's rows write their accumulators to LDS; then every
 // thread adds and stores whole float4 runs along N, non-temporally.
-template <class CF>
+template <class CF, bool OUTB>
 __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, int m0, int n0,
                                   const v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -363,21 +417,32 @@ __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, in
   float* e = (float*)lds;
   const float* cl = (const float*)(lds + CF::EPI_C_OFF);
   const size_t gbase = (size_t)g * p.M * p.N;
-  // C of this expert, from (m0, 0) to the expert's end
-  const v4i rc = make_rsrc(p.C + gbase + (size_t)m0 * p.N,
-                           (uint32_t)((size_t)(p.M - m0) * p.N * 4));
+  // C of this expert, from (m0, 0) to the expert's end (4- or 2-byte elements)
+  constexpr int osz = OUTB ? 2 : 4;
+  const v4i rc = make_rsrc((const unsigned char*)p.C + (gbase + (size_t)m0 * p.N) * osz,
+                           (uint32_t)((size_t)(p.M - m0) * p.N * osz));
   constexpr int kPH = CF::BM / CF::EPI_ROWS;
 #pragma unroll
   for (int ph = 0; ph < kPH; ++ph) {
 #pragma unroll
     for (int pc = 0; pc < CF::NJ / 2; ++pc) {
       __syncthreads();  // stage buffers / previous pass no longer read
-      if (p.C) {
+      if (p.C && !OUTB) {
         for (int k = w; k < CF::EPI_LOADS; k += CF::WAVES) {
           int row, lcol, m, n;
           epi_coords<CF>(64 * k + lane, ph, pc, m0, n0, row, lcol, m, n);
           load16_lds(rc, lds_addr(lds + CF::EPI_C_OFF) + 1024 * k,
                      (uint32_t)(((m - m0) * p.N + n) * 4));
+        }
+      } else if (p.C) {
+        // bf16 C: lane j of load k brings the 8 columns of float4 runs 2j and 2j+1
+        // (same row and wave strip); in LDS, bf16 element (row, lcol) sits at
+        // row * EPI_COLS + lcol
+        for (int k = w; k < CF::EPI_LOADS / 2; k += CF::WAVES) {
+          int row, lcol, m, n;
+          epi_coords<CF>(2 * (64 * k + lane), ph, pc, m0, n0, row, lcol, m, n);
+          load16_lds(rc, lds_addr(lds + CF::EPI_C_OFF) + 1024 * k,
+                     (uint32_t)(((m - m0) * p.N + n) * 2));
         }
       }
       const int wrow0 = wm * CF::WM - ph * CF::EPI_ROWS;  // this wave's first row in the pass
@@ -400,8 +465,15 @@ __device__ inline void store_tile(const Params& p, unsigned char* lds, int g, in
         epi_coords<CF>(threadIdx.x + CF::THREADS * k, ph, pc, m0, n0, row, lcol, m, n);
         if (m < p.M && n < p.N) {
           v4f v = *(const v4f*)(e + row * CF::EPI_STRIDE + lcol);
-          if (p.C) v += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
-          __builtin_nontemporal_store(v, (v4f*)(p.D + gbase + (size_t)m * p.N + n));
+          if constexpr (!OUTB) {
+            if (p.C) v += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
+            __builtin_nontemporal_store(v, (v4f*)(p.D + gbase + (size_t)m * p.N + n));
+          } else {
+            if (p.C)
+              v += bf16x4_to_f32(*(const v2u*)((const unsigned short*)cl + row * CF::EPI_COLS + lcol));
+            __builtin_nontemporal_store(
+                f32x4_to_bf16(v), (v2u*)((unsigned short*)p.D + gbase + (size_t)m * p.N + n));
+          }
         }
       }
     }
@@ -878,7 +950,7 @@ template <int KIND, bool FAST, class CF>
 __device__ void split_tiles(const Params& p, const Sched& s, unsigned char* smem,
                             const LoadOffsets<CF>& lo, int slot);
 
-template <int KIND, bool FAST, class CF, bool SPLIT = false>
+template <int KIND, bool FAST, class CF, bool SPLIT = false, bool OUTB = false>
 __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int64_t wsum_k[kMaxWaves];
@@ -915,7 +987,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
       const int Kg = uniform((int)(s.off[g + 1] - t_begin));
       __syncthreads();  // the previous item is done with the stage buffers
       if (Kg == 0) {
-        fill_tile<CF>(p, g, m0, n0);
+        fill_tile<CF, OUTB>(p, g, m0, n0);
         continue;
       }
       const int boff_g = uniform(s.boff[g]);
@@ -924,7 +996,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
       zero_acc<CF>(acc);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the previous item's stores
       item_gemm<KIND, FAST, CF>(p, lo, smem, t_begin, Kg, boff_g, m0, n0, nk, 0, nk, acc);
-      store_tile<CF>(p, smem, g, m0, n0, acc);
+      store_tile<CF, OUTB>(p, smem, g, m0, n0, acc);
     }
   }
 }
@@ -1058,15 +1130,29 @@ struct Launch {
   int bm, bn, threads;
 };
 
-template <int KIND, bool FAST, class CF, bool SPLIT = false>
+template <int KIND, bool FAST, class CF, bool SPLIT = false, bool OUTB = false>
 static Launch launch_of() {
-  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF, SPLIT>, CF::NS * CF::STAGE, CF::BM,
-                CF::BN, CF::THREADS};
+  return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF, SPLIT, OUTB>, CF::NS * CF::STAGE,
+                CF::BM, CF::BN, CF::THREADS};
+}
+
+// bf16 output (whole tiles only: stream-K is not taken with a bf16 D)
+static Launch pick_outb(int kind, bool fast, bool small) {
+  if (kind == BF16)
+    return small ? launch_of<BF16, false, CfgB16s, false, true>()
+                 : launch_of<BF16, false, CfgB16, false, true>();
+  if (kind == F32S)
+    return fast ? launch_of<F32S, true, CfgF8, false, true>()
+                : launch_of<F32S, false, CfgF8h, false, true>();
+  return fast ? launch_of<E8M0, true, CfgF8, false, true>()
+              : launch_of<E8M0, false, CfgF8h, false, true>();
 }
 
 // small: half tiles (bf16) for problems with few full tiles; split: stream-K over the
-// full-size tiles
-static Launch pick(int kind, bool fast, bool small = false, bool split = false) {
+// full-size tiles; outb: bf16 D
+static Launch pick(int kind, bool fast, bool small = false, bool split = false,
+                   bool outb = false) {
+  if (outb) return pick_outb(kind, fast, small);
   if (split) {
     if (kind == BF16) return launch_of<BF16, false, CfgB16, true>();
     if (kind == F32S)
@@ -1094,7 +1180,13 @@ static int device_setup(int dev) {
     int cus = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const Launch all[11] = {pick(BF16, false),
+    const Launch all[17] = {pick(BF16, false, false, false, true),
+                            pick(BF16, false, true, false, true),
+                            pick(F32S, false, false, false, true),
+                            pick(F32S, true, false, false, true),
+                            pick(E8M0, false, false, false, true),
+                            pick(E8M0, true, false, false, true),
+                            pick(BF16, false),
                             pick(BF16, false, true),
                             pick(F32S, false),
                             pick(F32S, true),
@@ -1162,15 +1254,16 @@ extern "C" int64_t kg_wgrad_workspace_flag_bytes(void) {
 }
 
 extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb,
-                           const float* C, float* D, const int32_t* ks, int G, int M, int N,
+                           const void* C, void* D, const int32_t* ks, int G, int M, int N,
                            int64_t K_total, int gran_k, int dtype_flags, void* workspace,
                            int64_t workspace_bytes, void* stream) {
   const int dtype = dtype_flags & 0xFF;
   const int flags = dtype_flags & ~0xFF;
   if (dtype != KG_E4M3_F32SCALE && dtype != KG_E4M3_UE8M0 && dtype != KG_BF16)
     return KG_ERR_DTYPE;
-  if (flags & ~KG_FLAG_FP8_MFMA) return KG_ERR_DTYPE;
+  if (flags & ~(KG_FLAG_FP8_MFMA | KG_FLAG_D_BF16)) return KG_ERR_DTYPE;
   const bool fast = (flags & KG_FLAG_FP8_MFMA) != 0;
+  const bool out_bf16 = (flags & KG_FLAG_D_BF16) != 0;
   if (fast && dtype == KG_BF16) return KG_ERR_DTYPE;
   if (G < 0 || M < 0 || N < 0 || K_total < 0 || workspace_bytes < 0) return KG_ERR_SHAPE;
   if (dtype != KG_BF16 && gran_k != 32 && gran_k != 128) return KG_ERR_GRAN;
@@ -1191,7 +1284,7 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
       misaligned(D) || ((uintptr_t)ks & 3) != 0 || ((uintptr_t)workspace & 255) != 0)
     return KG_ERR_ALIGN;
   const int elt = dtype == KG_BF16 ? 2 : 1;
-  const size_t dbytes = (size_t)G * M * N * 4;
+  const size_t dbytes = (size_t)G * M * N * (out_bf16 ? 2 : 4);
   if (C != nullptr && C != D && overlap(C, dbytes, D, dbytes)) return KG_ERR_ALIAS;
   if (overlap(A, (size_t)K_total * M * elt, D, dbytes) ||
       overlap(B, (size_t)K_total * N * elt, D, dbytes) || overlap(ks, (size_t)G * 4, D, dbytes) ||
@@ -1217,10 +1310,10 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
   // tiles (75% of one round) stay whole: its partial-tile hand-off measured slower.
   const int64_t T = tiles_of(pick(kind, fast, small));
   const int64_t rounds = (T + cus - 1) / cus;
-  const bool split = workspace != nullptr && G <= kMaxSplitGroups &&
+  const bool split = workspace != nullptr && G <= kMaxSplitGroups && !out_bf16 &&
                      (size_t)workspace_bytes >= split_ws_bytes(cus) &&
                      (2 * T <= (int64_t)cus || 10 * T < 7 * rounds * (int64_t)cus);
-  const Launch L = pick(kind, fast, small && !split, split);
+  const Launch L = pick(kind, fast, small && !split, split, out_bf16);
   const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
   const int64_t total = (int64_t)G * tiles_m * tiles_n;
   if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;
@@ -1230,8 +1323,8 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
   p.sa = (const unsigned char*)sa;
   p.B = (const unsigned char*)B;
   p.sb = (const unsigned char*)sb;
-  p.C = C;
-  p.D = D;
+  p.C = (const float*)C;
+  p.D = (float*)D;
   p.ks = ks;
   p.G = G;
   p.M = M;
@@ -1251,7 +1344,7 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
 }
 
 extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb,
-                        const float* C, float* D, const int32_t* ks, int G, int M, int N,
+                        const void* C, void* D, const int32_t* ks, int G, int M, int N,
                         int64_t K_total, int gran_k, int dtype_flags, void* stream) {
   return kg_wgrad_ws(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags, nullptr, 0,
                      stream);

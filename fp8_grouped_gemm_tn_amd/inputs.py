@@ -78,14 +78,15 @@ class Case:
         return dict(A=bits(self.A), B=bits(self.B), sa=bits(self.sa), sb=bits(self.sb),
                     C=bits(self.C), ks=self.ks.copy())
 
-    def algorithmic_bytes(self) -> int:
-        """Bytes the method must move once: A, B, scales, C (if given) and D."""
+    def algorithmic_bytes(self, out_bytes: int = 4) -> int:
+        """Bytes the method must move once: A, B, scales, C (if given) and D, with
+        `out_bytes` per element of C and D (4: fp32, 2: the bf16-output variant)."""
         elt = 2 if self.dtype == BF16 else 1
         nbytes = self.K_total * (self.M + self.N) * elt
         if self.sa is not None:
             nbytes += self.sa.numel() * self.sa.element_size()
             nbytes += self.sb.numel() * self.sb.element_size()
-        out = self.G * self.M * self.N * 4
+        out = self.G * self.M * self.N * out_bytes
         nbytes += out + (out if self.C is not None else 0)
         return nbytes
 

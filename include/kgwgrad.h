@@ -52,6 +52,15 @@ typedef enum {
  */
 #define KG_FLAG_FP8_MFMA 0x100
 
+/*
+ * Flag OR-ed into `dtype`: D (and C, when given) hold bf16 instead of fp32 (the
+ * how-to page's FP8 example allocates a bf16 D; its FAQ describes accumulation into
+ * a bf16 output). The sum C + sum_kb(...) is formed in fp32 as without the flag and
+ * rounded once to the nearest bf16, ties to even. Empty experts copy C bit for bit
+ * (or write +0.0). With a workspace, such calls never take the stream-K mode.
+ */
+#define KG_FLAG_D_BF16 0x200
+
 /* Return codes. */
 typedef enum {
   KG_OK = 0,
@@ -76,8 +85,9 @@ typedef enum {
  *   sa     [nblk, M]      fp32 (KG_E4M3_F32SCALE) or uint8 E8M0 (KG_E4M3_UE8M0); NULL for bf16
  *   B      [K_total, N]   same element type as A
  *   sb     [nblk, N]      same type as sa; NULL for bf16
- *   C      [G, M, N] fp32, may be NULL (treated as 0) or equal to D (in-place accumulate)
- *   D      [G, M, N] fp32, output
+ *   C      [G, M, N] fp32 (bf16 with KG_FLAG_D_BF16), may be NULL (treated as 0) or
+ *          equal to D (in-place accumulate)
+ *   D      [G, M, N] fp32 (bf16 with KG_FLAG_D_BF16), output
  *   ks     [G] int32, device memory: tokens per expert, in expert order
  *   nblk   = sum_g ceil(ks[g] / gran_k)
  *   gran_k tokens per scale block: 128 or 32 (fp8); ignored for bf16
@@ -93,16 +103,17 @@ typedef enum {
  * does not add up to K_total or holds a negative count is detected on the device:
  * the kernel then writes nothing and records KG_ERR_KSUM for kg_status.
  */
-int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb, const float* C,
-             float* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
+int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb, const void* C,
+             void* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
              int dtype, void* stream);
 
 /*
  * kg_wgrad_ws -- kg_wgrad with a caller-owned workspace that lets small bf16
  * problems use every compute unit.
  *
- * When the bf16 problem has fewer than two 256 x 256 output tiles per compute unit
- * and G <= 64, the token range of every tile is cut across all compute units
+ * When G <= 64, D is fp32, and the problem's output tiles would occupy at most
+ * half of the compute units, or whole rounds of tiles would leave more than 30%
+ * of them idle, the token range of every tile is cut across all compute units
  * (stream-K): the workgroup that holds a tile's first tokens adds the partial
  * tiles of the workgroups that hold its later tokens, in a fixed order, so results
  * do not depend on timing. Other problems, or a NULL / too small workspace, run
@@ -122,8 +133,8 @@ int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb, const
  * KG_ERR_SPLIT if a partial tile was never published (the kernel then gives up
  * after about 0.2 s instead of waiting forever).
  */
-int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, const float* C,
-                float* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
+int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, const void* C,
+                void* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
                 int dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*

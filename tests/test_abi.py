@@ -55,7 +55,14 @@ def call(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), B.KG_ERR_DTYPE),
     (dict(dtype=kg.KG_BF16 | kg.KG_FLAG_FP8_MFMA, sa=None, sb=None), B.KG_ERR_DTYPE),
-    (dict(dtype=kg.KG_E4M3_F32SCALE | 0x200), B.KG_ERR_DTYPE),
+    (dict(dtype=kg.KG_E4M3_F32SCALE | 0x400), B.KG_ERR_DTYPE),
+    # bf16 output: the same checks with 2-byte C and D
+    (dict(dtype=kg.KG_E4M3_F32SCALE | kg.KG_FLAG_D_BF16, C=FAKE + (1 << 30) + 32),
+     B.KG_ERR_ALIAS),
+    (dict(dtype=kg.KG_E4M3_F32SCALE | kg.KG_FLAG_D_BF16, D=FAKE + 4096), B.KG_ERR_ALIAS),
+    (dict(dtype=kg.KG_BF16 | kg.KG_FLAG_D_BF16, sa=None, sb=None, D=FAKE + (1 << 30) + 2),
+     B.KG_ERR_ALIGN),
+    (dict(dtype=kg.KG_E4M3_F32SCALE | kg.KG_FLAG_D_BF16, M=40), B.KG_ERR_ALIGN),
     (dict(G=-1), B.KG_ERR_SHAPE),
     (dict(M=-16), B.KG_ERR_SHAPE),
     (dict(K=-1), B.KG_ERR_SHAPE),

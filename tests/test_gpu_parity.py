@@ -416,3 +416,95 @@ def test_single_group_issue_shapes_sampled(name):
         sampled_check(case, t, D, fast=bool(flags))
     del D, t, case, ws
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- bf16 output
+
+def check_bf16_out(D_gpu, D_ref, bound, what="", fast=False):
+    """D_gpu (bf16) must lie between the oracle's bf16 roundings of D_ref -+ the fp32
+    tolerance: the kernel rounds its fp32 sum (within the tolerance of D_ref) once to
+    the nearest bf16, and rounding is monotone."""
+    tol = (FAST_RTOL if fast else RTOL) * bound + ATOL
+    got = kgref.bf16_value(D_gpu.view(torch.int16).cpu().numpy().view(np.uint16))
+    lo = kgref.bf16_value(kgref.bf16_round(D_ref - tol))
+    hi = kgref.bf16_value(kgref.bf16_round(D_ref + tol))
+    bad = (got < lo) | (got > hi)
+    assert not bad.any(), (f"{what}: {bad.sum()} bf16 outputs outside their rounding interval, "
+                           f"first at {np.unravel_index(np.argmax(bad), bad.shape)}")
+    if not fast:
+        # most intervals hold a single bf16 value, which the output then equals
+        assert (lo == hi).mean() > 0.5, f"{what}: tolerance interval too wide to be a check"
+
+
+@pytest.mark.parametrize("dtype,gran", [(F32, 128), (UE8, 32), (UE8, 128), (BF, 128)])
+@pytest.mark.parametrize("with_c", [False, True])
+@pytest.mark.parametrize("flags", [0, FAST])
+def test_bf16_output_variant(dtype, gran, with_c, flags):
+    if dtype == BF and flags:
+        pytest.skip("the fp8-MFMA flag applies to fp8 inputs")
+    ks = [300, 0, 129, 1, 517]
+    say("bf16 out", dtype, gran, with_c, flags)
+    case = small_case(dtype, gran, ks, 272, 400, with_c=with_c, seed=11)
+    t = to_dev(case)
+    Cb = None if case.C is None else t["C"].to(torch.bfloat16)
+    D = torch.full((case.G, case.M, case.N), float("nan"), dtype=torch.bfloat16, device=dev())
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], Cb, D, t["ks"], case.gran_k, case.dtype | flags,
+                K_total=case.K_total)
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    h = case.host()
+    C32 = None if Cb is None else Cb.float().cpu().numpy()
+    rc, D_ref, bound = kgref.wgrad(h["A"], h["sa"], h["B"], h["sb"], C32, h["ks"], case.M, case.N,
+                                   case.gran_k, case.dtype)
+    assert rc == kgref.OK
+    check_bf16_out(D, D_ref, bound, "bf16 out", fast=bool(flags))
+    # the empty expert: C bit for bit, or +0.0
+    want = Cb[1] if Cb is not None else torch.zeros_like(D[1])
+    assert torch.equal(D[1].view(torch.int16), want.view(torch.int16))
+
+
+def test_bf16_output_in_place_and_workspace():
+    ks = [640, 0, 200]
+    case = small_case(F32, 128, ks, 512, 256, with_c=True, seed=5)
+    t = to_dev(case)
+    Cb = t["C"].to(torch.bfloat16)
+    D = Cb.clone()
+    ws = kg.new_workspace(dev())
+    # in place (C == D), with a workspace that the bf16 output never uses for stream-K
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], D, D, t["ks"], case.gran_k, case.dtype,
+                K_total=case.K_total, workspace=ws)
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    h = case.host()
+    rc, D_ref, bound = kgref.wgrad(h["A"], h["sa"], h["B"], h["sb"], Cb.float().cpu().numpy(),
+                                   h["ks"], case.M, case.N, case.gran_k, case.dtype)
+    assert rc == kgref.OK
+    check_bf16_out(D, D_ref, bound, "bf16 in place")
+    assert torch.equal(D[1].view(torch.int16), Cb[1].view(torch.int16))
+    assert (ws[:kg.kg_wgrad_workspace_flag_bytes()] == 0).all()
+
+
+def test_bf16_output_full_size_default_workload_sampled():
+    say("bf16 out full size")
+    case = inputs.workload("bf16", device="cuda")
+    t = to_dev(case)
+    Cb = t["C"].to(torch.bfloat16)
+    D = torch.empty((case.G, case.M, case.N), dtype=torch.bfloat16, device=dev())
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], Cb, D, t["ks"], case.gran_k, case.dtype,
+                K_total=case.K_total, workspace=kg.new_workspace(dev()))
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    live = np.nonzero(case.ks > 0)[0]
+    n = 2000
+    sg, sm, sn = rng.choice(live, n), rng.integers(0, case.M, n), rng.integers(0, case.N, n)
+    h = case.host()
+    C32 = Cb.float().cpu().numpy()
+    rc, ref, bound = kgref.wgrad_sampled(h["A"], h["sa"], h["B"], h["sb"], C32, h["ks"], case.M,
+                                         case.N, case.gran_k, case.dtype, sg, sm, sn)
+    assert rc == kgref.OK
+    got = D[torch.from_numpy(sg).to(D.device), torch.from_numpy(sm).to(D.device),
+            torch.from_numpy(sn).to(D.device)]
+    check_bf16_out(got, ref, bound, "bf16 out full size")
+    g0 = int(np.nonzero(case.ks == 0)[0][0])
+    assert torch.equal(D[g0].view(torch.int16), Cb[g0].view(torch.int16))
