@@ -269,3 +269,99 @@ def workload_ks(name, seed=0):
         "ue8m0_many": lambda: ks_topk(16384, 256, 8, 51, seed),
         "local_share": lambda: ks_normal(262144, 8, 32768.0, 8192.0, seed),
     }[name]()
+
+
+# ----------------------------------------------------------------- M-grouped dgrad inputs
+
+@dataclass
+class DgradCase:
+    """Inputs of the M-grouped data-gradient GEMM: expert g owns token rows
+    [off[g], off[g+1]) of A = dy [M_total, K] (fp8, one fp32 scale per token per 128
+    channels, stored [K/128, M_total]); W [G, K, N] is each expert's weight as the
+    forward pass stores it (fp8, one fp32 scale per 128 x 128 block, [G, K/128, N/128])."""
+    name: str
+    G: int
+    N: int
+    K: int
+    ms: np.ndarray          # int32 [G]
+    A: torch.Tensor         # uint8 [M_total, K]
+    sa: torch.Tensor        # float32 [K/128, M_total]
+    W: torch.Tensor         # uint8 [G, K, N]
+    sw: torch.Tensor        # float32 [G, K/128, N/128]
+
+    @property
+    def M_total(self) -> int:
+        return int(self.ms.astype(np.int64).sum())
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M_total * self.N * self.K
+
+    def algorithmic_bytes(self, out_bytes: int = 2) -> int:
+        """A, W, their scales and D (out_bytes per element) once."""
+        return (self.M_total * self.K + self.G * self.K * self.N + self.sa.numel() * 4
+                + self.sw.numel() * 4 + self.M_total * self.N * out_bytes)
+
+    def host(self):
+        cpu = lambda t: t.detach().cpu().numpy()
+        return dict(A=cpu(self.A), sa=cpu(self.sa), W=cpu(self.W), sw=cpu(self.sw),
+                    ms=self.ms.copy())
+
+
+def quantize_rows_1x128(x: torch.Tensor):
+    """x fp32 [R, K] -> (uint8 [R, K], fp32 scales [K/128, R]): one scale per row per
+    128 columns, amax / 448 (1 for an all-zero run)."""
+    R, K = x.shape
+    xb = x.view(R, K // 128, 128)
+    amax = xb.abs().amax(dim=2)
+    scale = torch.where(amax == 0, torch.ones_like(amax), amax / FP8_MAX)
+    y = torch.clamp(xb / scale[:, :, None], -FP8_MAX, FP8_MAX)
+    q = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(R, K)
+    return q, scale.t().contiguous()
+
+
+def quantize_blocks_128x128(w: torch.Tensor):
+    """w fp32 [G, K, N] -> (uint8 [G, K, N], fp32 scales [G, K/128, N/128])."""
+    G, K, N = w.shape
+    wb = w.view(G, K // 128, 128, N // 128, 128)
+    amax = wb.abs().amax(dim=(2, 4))
+    scale = torch.where(amax == 0, torch.ones_like(amax), amax / FP8_MAX)
+    y = torch.clamp(wb / scale[:, :, None, :, None], -FP8_MAX, FP8_MAX)
+    q = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(G, K, N)
+    return q, scale
+
+
+def make_dgrad_case(name, ms, N, K, seed=0, device="cpu", a_std=1.0, w_std=1.0):
+    """Seeded dgrad inputs. Draw order: A (dy), then W."""
+    ms = np.asarray(ms, dtype=np.int32)
+    G = ms.size
+    M_total = int(ms.astype(np.int64).sum())
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    a = _normal(gen, (M_total, K), dev, a_std)
+    w = _normal(gen, (G, K, N), dev, w_std)
+    A, sa = quantize_rows_1x128(a)
+    del a
+    W, sw = quantize_blocks_128x128(w)
+    del w
+    return DgradCase(name=name, G=G, N=N, K=K, ms=ms, A=A.contiguous(), sa=sa, W=W.contiguous(),
+                     sw=sw.contiguous())
+
+
+DGRAD_WORKLOADS = ("dgrad_local_share", "dgrad_ue8m0_many_down")
+
+
+def dgrad_workload(name, device="cpu", seed=0):
+    """dgrad_local_share: the data gradient paired with the local_share weight
+    gradient (fused gate+up projection w [4096, 7168]: dx [262144, 7168] = dy
+    [262144, 4096] w), routing of local_share. dgrad_ue8m0_many_down: the
+    down projection of the many-expert layer (w [7168, 2048]: dx [131072, 2048] =
+    dy [131072, 7168] w), routing of ue8m0_many (51 empty experts)."""
+    if name == "dgrad_local_share":
+        return make_dgrad_case(name, workload_ks("local_share", seed), 7168, 4096, seed=seed,
+                               device=device)
+    if name == "dgrad_ue8m0_many_down":
+        return make_dgrad_case(name, workload_ks("ue8m0_many", seed), 2048, 7168, seed=seed,
+                               device=device)
+    raise KeyError(name)

@@ -524,3 +524,201 @@ int kgref_requant(const void* X, const float* xs, const int32_t* ks, int G, int 
   free(col);
   return KGREF_OK;
 }
+
+/* ---------------------------------------------------------------- M-grouped dgrad
+ *
+ * The other backward GEMM (GitHub issue "Is DeepGEMM directly applicable to
+ * backward in training?": the backward pass of a GEMM is two GEMMs, YouJiacheng
+ * 2025-02-26; the library shipped this one first, LyricZhao 2025-02-26; activations
+ * carry 1x128 scales and only weights carry 128x128 block scales, soundOfDestiny
+ * 2025-02-28). With y = x w^T in the forward pass, the data gradient is
+ * dx = dy w. Per expert g (token rows [off[g], off[g+1]) of dy, contiguous):
+ *
+ *   D[t][n] = sum over 128-channel blocks kb of the contraction axis of
+ *             SA[kb][t] * SW[g][kb][n/128] * sum_{k in kb} dec(A[t][k]) * dec(W[g][k][n])
+ *
+ * A = dy [M_total][K] (K contiguous), SA [K/128][M_total] fp32 (one scale per token
+ * per 128 channels, stored channel-block-major), W [G][K][N] (the expert's weight
+ * as the forward pass stores it, N contiguous), SW [G][K/128][N/128] fp32 (one scale
+ * per 128x128 block). K and N are multiples of 128. Each block partial is exact in
+ * fp64 (as for the K-grouped GEMM); the scales are applied to it once it is formed.
+ */
+
+typedef struct {
+  const uint8_t *A, *W;
+  const float *sa, *sw;
+  const int64_t* off;
+  int G, N, K;
+  int64_t M_total;
+} dgrad_t;
+
+static int dgrad_group_of(const dgrad_t* p, int64_t t) {
+  int lo = 0, hi = p->G; /* off[lo] <= t < off[hi] */
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (p->off[mid] <= t) lo = mid; else hi = mid;
+  }
+  while (lo < p->G && p->off[lo + 1] <= t) ++lo; /* skip empty experts */
+  return lo;
+}
+
+static void dgrad_elem(const dgrad_t* p, int64_t t, int n, double* d, double* bnd) {
+  const int g = dgrad_group_of(p, t);
+  const int nkb = p->K / 128;
+  const uint8_t* a = p->A + t * (int64_t)p->K;
+  const uint8_t* w = p->W + (int64_t)g * p->K * p->N;
+  double acc = 0.0, acc_abs = 0.0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    double part = 0.0, part_abs = 0.0;
+    for (int k = 128 * kb; k < 128 * kb + 128; ++k) {
+      const double x = g_e4m3[a[k]], y = g_e4m3[w[(int64_t)k * p->N + n]];
+      part += x * y;
+      part_abs += fabs(x) * fabs(y);
+    }
+    const double s = (double)p->sa[(int64_t)kb * p->M_total + t] *
+                     (double)p->sw[((int64_t)g * nkb + kb) * (p->N / 128) + n / 128];
+    acc += s * part;
+    acc_abs += fabs(s) * part_abs;
+  }
+  *d = acc;
+  *bnd = acc_abs;
+}
+
+typedef struct {
+  const dgrad_t* p;
+  int64_t t_lo, ns;
+  const int64_t* st;
+  const int32_t* sn;
+  double *D, *bound;
+  atomic_long next;
+  long nitems;
+} dgrad_job_t;
+
+static void* dgrad_rows_worker(void* arg) {
+  dgrad_job_t* j = (dgrad_job_t*)arg;
+  const int N = j->p->N;
+  for (;;) {
+    const long it = atomic_fetch_add(&j->next, 1);
+    if (it >= j->nitems) break;
+    for (int n = 0; n < N; ++n)
+      dgrad_elem(j->p, j->t_lo + it, n, j->D + (size_t)it * N + n, j->bound + (size_t)it * N + n);
+  }
+  return NULL;
+}
+
+static void* dgrad_sampled_worker(void* arg) {
+  dgrad_job_t* j = (dgrad_job_t*)arg;
+  for (;;) {
+    const long it = atomic_fetch_add(&j->next, 1);
+    if (it >= j->nitems) break;
+    dgrad_elem(j->p, j->st[it], j->sn[it], j->D + it, j->bound + it);
+  }
+  return NULL;
+}
+
+static int dgrad_run(dgrad_job_t* job, void* (*fn)(void*), int nthreads) {
+  int nt = pick_threads(nthreads);
+  if (nt > job->nitems) nt = (int)job->nitems;
+  if (nt < 1) nt = 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+  if (!th) return KGREF_ERR_SHAPE;
+  int started = 0;
+  for (int i = 0; i < nt; ++i) {
+    if (pthread_create(&th[i], NULL, fn, job) != 0) break;
+    ++started;
+  }
+  if (started == 0) fn(job);
+  for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  free(th);
+  g_last_threads = started > 0 ? started : 1;
+  return KGREF_OK;
+}
+
+int kgref_dgrad_validate(const int32_t* ms, int G, int N, int K, int64_t M_total) {
+  if (G < 0 || N < 0 || K < 0 || M_total < 0) return KGREF_ERR_SHAPE;
+  if (K % 128 != 0 || N % 128 != 0) return KGREF_ERR_SHAPE;
+  if (G > 0 && ms == NULL) return KGREF_ERR_NULL;
+  int64_t sum = 0;
+  for (int g = 0; g < G; ++g) {
+    if (ms[g] < 0) return KGREF_ERR_KSUM;
+    sum += ms[g];
+  }
+  return sum == M_total ? KGREF_OK : KGREF_ERR_KSUM;
+}
+
+static int dgrad_setup(dgrad_t* p, int64_t** off, const uint8_t* A, const float* sa,
+                       const uint8_t* W, const float* sw, const int32_t* ms, int G, int N, int K,
+                       int64_t M_total) {
+  pthread_once(&g_once, build_tables);
+  int rc = kgref_dgrad_validate(ms, G, N, K, M_total);
+  if (rc != KGREF_OK) return rc;
+  if (M_total > 0 && K > 0 && (!A || !sa || !W || !sw)) return KGREF_ERR_NULL;
+  *off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(G + 1));
+  if (!*off) return KGREF_ERR_SHAPE;
+  (*off)[0] = 0;
+  for (int g = 0; g < G; ++g) (*off)[g + 1] = (*off)[g] + ms[g];
+  p->A = A;
+  p->W = W;
+  p->sa = sa;
+  p->sw = sw;
+  p->off = *off;
+  p->G = G;
+  p->N = N;
+  p->K = K;
+  p->M_total = M_total;
+  return KGREF_OK;
+}
+
+int kgref_dgrad(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                const int32_t* ms, int G, int N, int K, int64_t M_total, int64_t t_lo,
+                int64_t t_hi, double* D_out, double* bound_out, int nthreads) {
+  dgrad_t p;
+  int64_t* off = NULL;
+  int rc = dgrad_setup(&p, &off, A, sa, W, sw, ms, G, N, K, M_total);
+  if (rc == KGREF_OK && (t_lo < 0 || t_hi > M_total || t_lo > t_hi)) rc = KGREF_ERR_SHAPE;
+  if (rc == KGREF_OK && t_hi > t_lo && N > 0) {
+    if (!D_out || !bound_out) {
+      rc = KGREF_ERR_NULL;
+    } else {
+      dgrad_job_t job;
+      memset(&job, 0, sizeof job);
+      job.p = &p;
+      job.t_lo = t_lo;
+      job.D = D_out;
+      job.bound = bound_out;
+      atomic_init(&job.next, 0);
+      job.nitems = (long)(t_hi - t_lo);
+      rc = dgrad_run(&job, dgrad_rows_worker, nthreads);
+    }
+  }
+  free(off);
+  return rc;
+}
+
+int kgref_dgrad_sampled(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                        const int32_t* ms, int G, int N, int K, int64_t M_total, int64_t ns,
+                        const int64_t* st, const int32_t* sn, double* out, double* bound_out,
+                        int nthreads) {
+  dgrad_t p;
+  int64_t* off = NULL;
+  int rc = dgrad_setup(&p, &off, A, sa, W, sw, ms, G, N, K, M_total);
+  if (rc == KGREF_OK && ns > 0) {
+    if (!st || !sn || !out || !bound_out) rc = KGREF_ERR_NULL;
+    for (int64_t i = 0; rc == KGREF_OK && i < ns; ++i)
+      if (st[i] < 0 || st[i] >= M_total || sn[i] < 0 || sn[i] >= N) rc = KGREF_ERR_SHAPE;
+    if (rc == KGREF_OK) {
+      dgrad_job_t job;
+      memset(&job, 0, sizeof job);
+      job.p = &p;
+      job.st = st;
+      job.sn = sn;
+      job.D = out;
+      job.bound = bound_out;
+      atomic_init(&job.next, 0);
+      job.nitems = (long)ns;
+      rc = dgrad_run(&job, dgrad_sampled_worker, nthreads);
+    }
+  }
+  free(off);
+  return rc;
+}

@@ -97,6 +97,26 @@ uint8_t kgref_e4m3_encode(double v);
 int kgref_requant(const void* X, const float* xs, const int32_t* ks, int G, int H,
                   int64_t K_total, int gran_k, int src, int scale_kind, uint8_t* Q, void* S);
 
+/* ---- M-grouped GEMM of the data gradient (dgrad), 1x128 x 128x128 scales ----
+ *
+ * Expert g owns the token rows [off[g], off[g+1]) (off from ms like the K-grouped
+ * offsets). For such a token t and output column n:
+ *   D[t][n] = sum over kb of SA[kb][t] * SW[g][kb][n/128] *
+ *             sum_{k = 128 kb}^{128 kb + 127} dec(A[t][k]) * dec(W[g][k][n])
+ * A: uint8 e4m3fn [M_total][K]; SA: float [K/128][M_total]; W: uint8 e4m3fn [G][K][N];
+ * SW: float [G][K/128][N/128]; K and N multiples of 128 (KGREF_ERR_SHAPE otherwise),
+ * ms[g] >= 0 adding up to M_total (KGREF_ERR_KSUM otherwise).
+ * kgref_dgrad writes rows [t_lo, t_hi) of D and of the bound sum_k |a||w| (double
+ * [(t_hi - t_lo)][N]); kgref_dgrad_sampled the elements (st[i], sn[i]). */
+int kgref_dgrad_validate(const int32_t* ms, int G, int N, int K, int64_t M_total);
+int kgref_dgrad(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                const int32_t* ms, int G, int N, int K, int64_t M_total, int64_t t_lo,
+                int64_t t_hi, double* D_out, double* bound_out, int nthreads);
+int kgref_dgrad_sampled(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                        const int32_t* ms, int G, int N, int K, int64_t M_total, int64_t ns,
+                        const int64_t* st, const int32_t* sn, double* out, double* bound_out,
+                        int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

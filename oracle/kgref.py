@@ -56,6 +56,14 @@ def lib():
         L.kgref_bf16_round.argtypes = [ctypes.c_double]
         L.kgref_bf16_round_array.restype = None
         L.kgref_bf16_round_array.argtypes = [vp, vp, i64]
+        L.kgref_dgrad_validate.restype = ctypes.c_int
+        L.kgref_dgrad_validate.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64]
+        L.kgref_dgrad.restype = ctypes.c_int
+        L.kgref_dgrad.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  i64, i64, i64, vp, vp, ctypes.c_int]
+        L.kgref_dgrad_sampled.restype = ctypes.c_int
+        L.kgref_dgrad_sampled.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int]
         L.kgref_requant.restype = ctypes.c_int
         L.kgref_requant.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, vp, vp]
@@ -197,3 +205,39 @@ def bf16_value(codes):
     """fp64 values of bf16 codes (kgref_bf16, elementwise)."""
     c = np.ascontiguousarray(codes, dtype=np.uint16)
     return (c.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dgrad(A, sa, W, sw, ms, N, K, rows=None, threads=0):
+    """M-grouped dgrad reference: (rc, D [rows, N] fp64, bound [rows, N]) for token
+    rows `rows` = (t_lo, t_hi) (default: all). A uint8 [M_total, K], sa float32
+    [K/128, M_total], W uint8 [G, K, N], sw float32 [G, K/128, N/128], ms int32 [G]."""
+    A = _c(A, np.uint8)
+    sa = _c(sa, np.float32)
+    W = _c(W, np.uint8)
+    sw = _c(sw, np.float32)
+    ms = _c(ms, np.int32)
+    M_total = int(ms.astype(np.int64).sum())
+    t_lo, t_hi = (0, M_total) if rows is None else rows
+    D = np.zeros((max(t_hi - t_lo, 0), N), np.float64)
+    bound = np.zeros_like(D)
+    rc = lib().kgref_dgrad(_ptr(A), _ptr(sa), _ptr(W), _ptr(sw), _ptr(ms), ms.size, N, K,
+                           M_total, t_lo, t_hi, _ptr(D), _ptr(bound), threads)
+    return rc, D, bound
+
+
+def dgrad_sampled(A, sa, W, sw, ms, N, K, st, sn, threads=0):
+    """The dgrad reference for the elements (st[i], sn[i])."""
+    A = _c(A, np.uint8)
+    sa = _c(sa, np.float32)
+    W = _c(W, np.uint8)
+    sw = _c(sw, np.float32)
+    ms = _c(ms, np.int32)
+    M_total = int(ms.astype(np.int64).sum())
+    st = np.ascontiguousarray(st, dtype=np.int64)
+    sn = np.ascontiguousarray(sn, dtype=np.int32)
+    out = np.zeros(st.size, np.float64)
+    bound = np.zeros(st.size, np.float64)
+    rc = lib().kgref_dgrad_sampled(_ptr(A), _ptr(sa), _ptr(W), _ptr(sw), _ptr(ms), ms.size, N, K,
+                                   M_total, st.size, _ptr(st), _ptr(sn), _ptr(out), _ptr(bound),
+                                   threads)
+    return rc, out, bound
