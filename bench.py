@@ -13,6 +13,12 @@ C. The other workloads (worked, zipf_fp8, ue8m0_many, local_share, and the six
 non-grouped shapes single_m{m}_n{n}_k{k} of the issue page's 1D1D table) are
 selectable with --workload.
 
+    python bench.py --dgrad NAME [--fast] [--fp32-out]
+
+times the M-grouped data-gradient GEMM (kg_dgrad) on dgrad_local_share or
+dgrad_ue8m0_many_down (bf16 output unless --fp32-out), with its roofline and the
+CPU oracle timed on a row sample.
+
     python bench.py --requant NAME [--steps K] [--warmup W]
 
 times the requantiser (kg_requant) that produces a workload's fp8 operand instead:
@@ -279,6 +285,103 @@ def requant_main(args):
     print(json.dumps(line), flush=True)
 
 
+def dgrad_main(args):
+    """Time kg_dgrad on one dgrad workload; print one JSON line."""
+    import numpy as np
+    import torch
+    import fp8_grouped_gemm_tn_amd as kg
+    from fp8_grouped_gemm_tn_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    c = inputs.dgrad_workload(args.dgrad, device="cuda", seed=args.seed)
+    ms = torch.from_numpy(c.ms).to(dev)
+    out = torch.float32 if args.fp32_out else torch.bfloat16
+    D = torch.empty((c.M_total, c.N), dtype=out, device=dev)
+    flags = kg.KG_FLAG_FP8_MFMA if args.fast else 0
+
+    def step():
+        kg.kg_dgrad(c.A, c.sa, c.W, c.sw, D, ms, flags)
+
+    args.warmup = warm_up(step, args.warmup)
+    assert kg.kg_status() == kg.KG_OK
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert kg.kg_status() == kg.KG_OK
+    avg_ms = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev)
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    flops = c.flops
+    nbytes = c.algorithmic_bytes(4 if args.fp32_out else 2)
+    mfma_peak = PEAK["fp8"]
+    t_mfma, t_hbm = flops / (mfma_peak * 1e12), nbytes / (HBM_GBS * 1e9)
+    secs = avg_ms / 1e3
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(flops / secs / 1e12, 3), "peak": mfma_peak,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+    line = {
+        "metric": "M-grouped dgrad TFLOP/s (2*M_total*N*K) + % of FP8 MFMA / HBM roofline, 1 GPU",
+        "value": round(flops / (ms_per_step / 1e3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 e4m3 (fp8 MFMA)" if args.fast else "fp8 e4m3 (bf16 MFMA)",
+        "data": "synthetic (seeded N(0,1), 1x128 activation and 128x128 weight quantisation)",
+        "config": {"workload": DGRAD_DESCR[args.dgrad], "G": c.G, "N": c.N, "K": c.K,
+                   "tokens": c.M_total, "fp8_mfma": bool(args.fast),
+                   "d_dtype": "fp32" if args.fp32_out else "bf16"},
+        "roofline": roof,
+        "wall_s": round(wall, 4),
+    }
+    if not args.no_cpu:
+        from oracle import kgref
+        h = {k: v.cpu().numpy() for k, v in dict(A=c.A, sa=c.sa, W=c.W, sw=c.sw).items()}
+        rows = 16
+        while True:
+            tt = time.perf_counter()
+            rc, _, _ = kgref.dgrad(h["A"], h["sa"], h["W"], h["sw"], c.ms, c.N, c.K, rows=(0, rows))
+            dt = time.perf_counter() - tt
+            assert rc == kgref.OK
+            if dt > 3.0 or rows >= 4096:
+                break
+            rows = min(4096, int(rows * max(2.0, 10.0 / max(dt, 1e-3))))
+        f = 2.0 * rows * c.N * c.K
+        line["cpu_baseline"] = {"value": round(f / dt / 1e12, 6), "unit": "TFLOP/s",
+                                "cores": kgref.last_threads(), "kind": "oracle",
+                                "sample": f"token rows 0..{rows - 1}, all {c.N} columns: "
+                                          f"{f / 1e9:.2f} GFLOP in {dt:.2f} s (fp64)"}
+    print(json.dumps(line), flush=True)
+
+
+DGRAD_DESCR = {
+    "dgrad_local_share": "dgrad paired with the local-share wgrad: G=8, 262144 tokens ~N(32768,8192), "
+                         "dx [262144, 7168] = dy [262144, 4096] . w, fp8 e4m3 1x128 / 128x128 scales",
+    "dgrad_ue8m0_many_down": "dgrad of the many-expert down projection: G=256 (51 empty), 131072 "
+                             "tokens top-8, dx [131072, 2048] = dy [131072, 7168] . w, fp8 e4m3 "
+                             "1x128 / 128x128 scales",
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,7 +405,16 @@ def main():
                          "profiles/kg_wgrad_NAME_traffic.json")
     ap.add_argument("--requant", choices=list(REQUANT),
                     help="time the requantiser on this operand instead of the GEMM")
+    ap.add_argument("--dgrad", choices=list(DGRAD_DESCR),
+                    help="time the M-grouped dgrad GEMM (kg_dgrad, bf16 output) instead")
+    ap.add_argument("--fp32-out", action="store_true", help="--dgrad: fp32 output")
     args = ap.parse_args()
+    if args.dgrad:
+        if args.gpus != 1:
+            print("bench.py measures one GPU; run with --gpus 1.", file=sys.stderr)
+            sys.exit(2)
+        dgrad_main(args)
+        return
     if args.requant:
         if args.gpus != 1:
             print("bench.py measures one GPU; run with --gpus 1.", file=sys.stderr)

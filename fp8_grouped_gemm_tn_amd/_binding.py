@@ -36,6 +36,7 @@ SIGNATURES = {
     "kg_debug_offsets": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "kg_max_groups": (_i32, []),
     "kg_requant": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "kg_dgrad": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp]),
 }
 
 _lib = None
@@ -171,3 +172,23 @@ def kg_requant(X, xs, ks, gran_k, scale_kind, nblk, Q=None, S=None, stream=None)
     if rc != KG_OK:
         raise KgError(rc, "kg_requant")
     return Q, S
+
+
+def kg_dgrad_raw(A, sa, W, sw, D, ms, G, N, K, M_total, flags, stream=None):
+    """Call kg_dgrad with torch device tensors (or None); returns the status code."""
+    return lib().kg_dgrad(_ptr(A), _ptr(sa), _ptr(W), _ptr(sw), _ptr(D), _ptr(ms), int(G), int(N),
+                          int(K), int(M_total), int(flags), _stream(stream))
+
+
+def kg_dgrad(A, sa, W, sw, D, ms, flags=0, stream=None):
+    """D = M-grouped dy . w: A (dy) [M_total, K] fp8 bytes, sa [K/128, M_total] fp32,
+    W [G, K, N] fp8 bytes, sw [G, K/128, N/128] fp32, ms [G] int32, D [M_total, N]
+    (float32, or bfloat16 for the bf16 output). All on the GPU."""
+    import torch
+    G, K, N = W.shape
+    if D.dtype == torch.bfloat16:
+        flags |= KG_FLAG_D_BF16
+    rc = kg_dgrad_raw(A, sa, W, sw, D, ms, G, N, K, A.shape[0], flags, stream)
+    if rc != KG_OK:
+        raise KgError(rc, "kg_dgrad")
+    return D

@@ -315,10 +315,13 @@ __device__ inline void epi_coords(int idx, int ph, int pc, int m0, int n0, int& 
 // LDS while the addend goes global -> LDS by buffer loads; every thread adds the
 // addend to its float4 runs, then each partial in turn through the same LDS
 // buffer, and stores whole float4 runs along N, non-temporally.
-template <class CF, bool SYS_STORE = false>
+// With OUTB, dst holds bf16 (the sums are rounded to nearest even; no addend or
+// partials are allowed then).
+template <class CF, bool SYS_STORE = false, bool OUTB = false>
 __device__ inline void store_tile_gen(unsigned char* lds, const v4f (&acc)[CF::NI][CF::NJ],
                                       float* dst, int ld, int rows, int cols, const float* add,
                                       uint32_t add_bytes, const float* parts, int nparts) {
+  static_assert(!(OUTB && SYS_STORE), "bf16 output is stored with ordinary stores");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
@@ -384,6 +387,9 @@ __device__ inline void store_tile_gen(unsigned char* lds, const v4f (&acc)[CF::N
           if (addl) v += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
           if constexpr (SYS_STORE)
             store16_sys(dst, (uint32_t)((size_t)rows * ld * 4), (uint32_t)((m * ld + n) * 4), v);
+          else if constexpr (OUTB)
+            __builtin_nontemporal_store(
+                f32x4_to_bf16(v), (v2u*)((unsigned short*)dst + (size_t)m * ld + n));
           else
             __builtin_nontemporal_store(v, (v4f*)(dst + (size_t)m * ld + n));
         }
@@ -1377,5 +1383,7 @@ extern "C" int kg_debug_offsets(const int32_t* ks, int G, int gran_k, int64_t* o
   return KG_OK;
 }
 
-// The requantiser shares this translation unit (and the device status word).
+// The requantiser and the M-grouped dgrad GEMM share this translation unit (and the
+// device status word).
 #include "kg_requant.h"
+#include "kg_dgrad.h"

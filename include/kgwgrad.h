@@ -209,6 +209,42 @@ int kg_max_groups(void);
 int kg_requant(const void* X, const float* xs, const int32_t* ks, int G, int H, int64_t K_total,
                int gran_k, int src, int scale_kind, void* Q, void* S, void* stream);
 
+/*
+ * kg_dgrad -- enqueue the M-grouped GEMM of the data gradient, dx = dy . w per expert
+ * (GitHub issue "Is DeepGEMM directly applicable to backward in training?": the
+ * backward pass of a GEMM is two GEMMs, YouJiacheng 2025-02-26; activations carry
+ * 1x128 scales and only weights carry 128x128 block scales, soundOfDestiny
+ * 2025-02-28). Expert g owns the contiguous token rows [off[g], off[g+1]) of A,
+ * off[g+1] = off[g] + ms[g]; for such a row t and output column n
+ *
+ *   D[t][n] = sum over kb of sa[kb][t] * sw[g][kb][n/128] *
+ *             sum_{k = 128 kb}^{128 kb + 127} A[t][k] * W[g][k][n]
+ *
+ *   A   [M_total, K]      fp8 e4m3fn bytes (dy, K contiguous)
+ *   sa  [K/128, M_total]  fp32, one scale per token per 128 channels
+ *   W   [G, K, N]         fp8 e4m3fn bytes (each expert's w as the forward pass
+ *                         stores it, N contiguous)
+ *   sw  [G, K/128, N/128] fp32, one scale per 128 x 128 block of W
+ *   D   [M_total, N]      fp32 output (bf16 with KG_FLAG_D_BF16, rounded to
+ *                         nearest even from the fp32 sum)
+ *   ms  [G] int32, device memory: tokens per expert, in expert order
+ *   flags  KG_FLAG_FP8_MFMA (contract with the fp8 MFMA, accuracy as for kg_wgrad)
+ *          and/or KG_FLAG_D_BF16
+ *
+ * Each block's partial sum is formed exactly from the fp8 products (bf16 MFMA on
+ * widened values; see KG_FLAG_FP8_MFMA for the fast mode) and multiplied by its two
+ * scales before it is added in fp32. K and N must be multiples of 128 and every
+ * pointer 16-byte aligned except sw and ms (4 bytes) (KG_ERR_ALIGN). Errors before
+ * any launch: KG_ERR_DTYPE (unknown flag), KG_ERR_SHAPE (negative sizes), KG_ERR_NULL,
+ * KG_ERR_ALIGN, KG_ERR_ALIAS (D overlapping an input), KG_ERR_UNSUPPORTED (G > 1024,
+ * N or K > 2^24, M_total > 2^31 - 1, or a tile's offsets past 32 bits), KG_ERR_HIP.
+ * A ms that holds a negative count or does not add up to M_total is reported by
+ * kg_status (KG_ERR_KSUM) and nothing is written. G, N or M_total == 0: KG_OK, no
+ * launch. Rows of D are written exactly once (by the tile that owns them).
+ */
+int kg_dgrad(const void* A, const float* sa, const void* W, const float* sw, void* D,
+             const int32_t* ms, int G, int N, int K, int64_t M_total, int flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -184,3 +184,36 @@ def test_quantizer_blocks_restart_per_group_and_fit_e4m3():
     rows = torch.tensor([0] * 32 + [1] * 32 + [2] * 32 + [3] * 32 + [4] * 2 + [5] * 5)
     assert (q2.view(torch.float8_e4m3fn).float().abs() <= 448).all()
     assert ((q2.view(torch.float8_e4m3fn).float() * sc[rows] - x).abs() <= x.abs() * 2 ** -3 + sc[rows] * 2 ** -9).all()
+
+
+def dcall(A=FAKE, sa=FAKE, W=FAKE + (1 << 28), sw=FAKE, D=FAKE + (1 << 30), ms=FAKE + (1 << 31),
+          G=3, N=256, K=384, M=100, flags=0):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return B.lib().kg_dgrad(v(A), v(sa), v(W), v(sw), v(D), v(ms), G, N, K, M, flags, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=0x400), B.KG_ERR_DTYPE),
+    (dict(G=-1), B.KG_ERR_SHAPE),
+    (dict(K=-128), B.KG_ERR_SHAPE),
+    (dict(M=-1), B.KG_ERR_SHAPE),
+    (dict(G=1025), B.KG_ERR_UNSUPPORTED),
+    (dict(K=200), B.KG_ERR_ALIGN),
+    (dict(N=64), B.KG_ERR_ALIGN),
+    (dict(D=None), B.KG_ERR_NULL),
+    (dict(ms=None), B.KG_ERR_NULL),
+    (dict(W=None), B.KG_ERR_NULL),
+    (dict(sa=None), B.KG_ERR_NULL),
+    (dict(A=FAKE + 8), B.KG_ERR_ALIGN),
+    (dict(D=FAKE + (1 << 30) + 4), B.KG_ERR_ALIGN),
+    (dict(D=FAKE + 4096), B.KG_ERR_ALIAS),                 # D overlaps A
+    (dict(D=FAKE + (1 << 28), flags=kg.KG_FLAG_D_BF16), B.KG_ERR_ALIAS),  # D on W
+])
+def test_dgrad_synchronous_errors(kw, code):
+    assert dcall(**kw) == code
+
+
+def test_dgrad_empty_problems_launch_nothing():
+    assert dcall(G=0) == B.KG_OK
+    assert dcall(N=0) == B.KG_OK
+    assert dcall(M=0) == B.KG_OK

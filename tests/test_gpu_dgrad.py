@@ -1,0 +1,147 @@
+"""GPU parity of the M-grouped dgrad GEMM (kg_dgrad, through the C ABI) against the
+CPU oracle.
+
+Precise mode: |D - D_ref| <= 1e-5 * sum_k |a w| + 1e-6 element-wise and Frobenius
+1e-5 (fp32 accumulation of exact fp8 products, as for the K-grouped GEMM); fp8-MFMA
+mode: 2^-10 * sum|a w| + 1e-6 and Frobenius 1e-4 (the fp8 MFMA's accumulation, see
+kgwgrad.h). bf16 output: between the oracle's bf16 roundings of D_ref -+ the
+tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_grouped_gemm_tn_amd as kg
+from fp8_grouped_gemm_tn_amd import inputs
+from oracle import kgref
+
+pytestmark = pytest.mark.gpu
+
+FAST = kg.KG_FLAG_FP8_MFMA
+RTOL, ATOL, FROB = 1e-5, 1e-6, 1e-5
+FAST_RTOL, FAST_FROB = 2.0 ** -10, 1e-4
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def to_dev(c):
+    d = dev()
+    return dict(A=c.A.to(d), sa=c.sa.to(d), W=c.W.to(d), sw=c.sw.to(d),
+                ms=torch.from_numpy(c.ms).to(d))
+
+
+def run(c, t, flags=0, out=torch.float32, D=None):
+    if D is None:
+        D = torch.full((c.M_total, c.N), float("nan"), dtype=out, device=dev())
+    kg.kg_dgrad(t["A"], t["sa"], t["W"], t["sw"], D, t["ms"], flags)
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    return D
+
+
+def check(D, ref, bound, fast=False, what=""):
+    tol = (FAST_RTOL if fast else RTOL) * bound + ATOL
+    if D.dtype == torch.bfloat16:
+        got = kgref.bf16_value(D.view(torch.int16).cpu().numpy().view(np.uint16))
+        lo = kgref.bf16_value(kgref.bf16_round(ref - tol))
+        hi = kgref.bf16_value(kgref.bf16_round(ref + tol))
+        bad = (got < lo) | (got > hi)
+        assert not bad.any(), f"{what}: {bad.sum()} bf16 outputs outside their rounding interval"
+        return
+    got = D.double().cpu().numpy()
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} out of tolerance, worst {(err - tol).max():.3e} "
+                           f"at {np.unravel_index(np.argmax(err - tol), err.shape)}")
+    nrm = np.linalg.norm(ref)
+    if nrm > 0:
+        assert np.linalg.norm(got - ref) <= (FAST_FROB if fast else FROB) * nrm
+
+
+@pytest.mark.parametrize("ms,N,K", [
+    ([300, 0, 1, 517, 256], 384, 512),   # ragged experts, an empty one, several m-tiles
+    ([40], 128, 128),                    # one partial tile, one stage
+    ([0, 257, 0], 256, 1024),            # 257 rows: a full tile and a one-row tile
+])
+@pytest.mark.parametrize("flags", [0, FAST])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_dgrad_matches_oracle(ms, N, K, flags, out):
+    say("dgrad", ms, N, K, flags, out)
+    c = inputs.make_dgrad_case("t", ms, N, K, seed=3)
+    t = to_dev(c)
+    D = run(c, t, flags, out)
+    h = c.host()
+    rc, ref, bound = kgref.dgrad(h["A"], h["sa"], h["W"], h["sw"], h["ms"], c.N, c.K)
+    assert rc == kgref.OK
+    check(D, ref, bound, fast=bool(flags), what="dgrad")
+
+
+def test_dgrad_writes_only_its_rows_and_is_deterministic():
+    c = inputs.make_dgrad_case("t", [129, 0, 300], 256, 384, seed=5)
+    t = to_dev(c)
+    guard = 64
+    big = torch.full((c.M_total + 2 * guard, c.N), float("nan"), device=dev())
+    D = big[guard:guard + c.M_total]
+    run(c, t, D=D)
+    assert torch.isnan(big[:guard]).all() and torch.isnan(big[guard + c.M_total:]).all()
+    assert torch.isfinite(D).all()
+    D2 = run(c, t)
+    assert torch.equal(D.view(torch.int32), D2.view(torch.int32))
+
+
+def test_dgrad_ms_mismatch_is_reported_and_writes_nothing():
+    c = inputs.make_dgrad_case("t", [100, 60], 128, 256, seed=1)
+    t = to_dev(c)
+    bad = torch.tensor([100, 61], dtype=torch.int32, device=dev())
+    D = torch.full((c.M_total, c.N), float("nan"), device=dev())
+    rc = kg.kg_dgrad_raw(t["A"], t["sa"], t["W"], t["sw"], D, bad, 2, c.N, c.K, c.M_total, 0)
+    assert rc == kg.KG_OK
+    assert kg.kg_status() == kg.KG_ERR_KSUM
+    assert torch.isnan(D).all()
+    assert kg.kg_status() == kg.KG_OK
+
+
+def test_dgrad_power_of_two_scales_bit_exact():
+    c = inputs.make_dgrad_case("t", [200, 77], 256, 512, seed=9)
+    t = to_dev(c)
+    D = run(c, t)
+    t2 = dict(t, sa=t["sa"] * 4.0, sw=t["sw"] * 0.5)
+    D2 = run(c, t2)
+    assert torch.equal(D2, D * 2.0)
+
+
+@pytest.mark.parametrize("name", inputs.DGRAD_WORKLOADS)
+def test_dgrad_full_size_sampled(name):
+    say("dgrad full size", name)
+    c = inputs.dgrad_workload(name, device="cuda")
+    t = to_dev(c)
+    h = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in
+         dict(A=c.A, sa=c.sa, W=c.W, sw=c.sw, ms=c.ms).items()}
+    rng = np.random.default_rng(0)
+    n = 1500
+    st = rng.integers(0, c.M_total, n)
+    sn = rng.integers(0, c.N, n)
+    # the first and last row of every non-empty expert, first and last column
+    off = np.concatenate([[0], np.cumsum(c.ms)])
+    edges = [r for g in range(c.G) if c.ms[g] > 0 for r in (off[g], off[g + 1] - 1)]
+    st = np.concatenate([st, edges, edges])
+    sn = np.concatenate([sn, np.zeros(len(edges), np.int64), np.full(len(edges), c.N - 1)])
+    rc, ref, bound = kgref.dgrad_sampled(h["A"], h["sa"], h["W"], h["sw"], h["ms"], c.N, c.K,
+                                         st, sn)
+    assert rc == kgref.OK
+    for flags, out in ((0, torch.float32), (0, torch.bfloat16), (FAST, torch.bfloat16)):
+        say("dgrad full size", name, flags, out)
+        D = torch.empty((c.M_total, c.N), dtype=out, device=dev())
+        run(c, t, flags, D=D)
+        got = D[torch.from_numpy(st).to(D.device), torch.from_numpy(sn).to(D.device)]
+        check(got, ref, bound, fast=bool(flags), what=name)
+        del D
+    torch.cuda.empty_cache()
