@@ -392,6 +392,8 @@ def main():
     ap.add_argument("--workload", default="bf16", choices=list(DESCR))
     ap.add_argument("--fast", action="store_true", help="fp8 kinds: contract with the fp8 MFMA")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--gran-k", type=int, default=None, choices=[32, 128],
+                    help="replace an fp8 workload's scale granularity (tokens per scale)")
     ap.add_argument("--bf16-out", action="store_true",
                     help="the bf16-output variant: C and D in bf16 (KG_FLAG_D_BF16)")
     ap.add_argument("--no-workspace", action="store_true",
@@ -442,7 +444,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    case = inputs.workload(args.workload, device="cuda", seed=args.seed)
+    case = inputs.workload(args.workload, device="cuda", seed=args.seed, gran_k=args.gran_k)
     A, B = case.A, case.B
     sa, sb, C = case.sa, case.sb, case.C
     out_dtype = torch.bfloat16 if args.bf16_out else torch.float32
@@ -495,7 +497,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = counters_for(args.workload, bool(flags), args.bf16_out)
+    roof["traffic"] = (counters_for(args.workload, bool(flags), args.bf16_out)
+                       if args.gran_k is None else None)
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     roof["roofline_ms"] = round(max(t_mfma, t_hbm) * 1e3, 4)
@@ -515,7 +518,9 @@ def main():
         "vs_baseline": None,
         "dtype": dname,
         "data": "synthetic (seeded generators, fp8 values quantised per 128/32-token block)",
-        "config": {"workload": DESCR[args.workload], "G": case.G, "M": case.M, "N": case.N,
+        "config": {"workload": DESCR[args.workload] + (f" (scales per {args.gran_k} tokens)"
+                                                        if args.gran_k else ""),
+                   "G": case.G, "M": case.M, "N": case.N,
                    "tokens": case.K_total, "gran_k": case.gran_k if not is_bf16 else None,
                    "fp8_mfma": bool(flags), "workspace": ws is not None,
                    "d_dtype": "bf16" if args.bf16_out else "fp32"},

@@ -57,7 +57,8 @@ __device__ int kgwgrad_status_word;
 
 namespace kg {
 
-enum Kind { F32S = 0, E8M0 = 1, BF16 = 2 };
+// F32S32: fp32 scales per 32 tokens (a scale row per 32-token block).
+enum Kind { F32S = 0, E8M0 = 1, BF16 = 2, F32S32 = 3 };
 
 struct Params {
   const unsigned char* A;
@@ -103,7 +104,9 @@ struct Cfg {
   // with scales, one scale tile per operand. Load k of a stage is issued by wave
   // k % WAVES, so the first HEAVY waves issue PER + 1 loads and the others PER.
   static constexpr int LOADS_A = TK * CHA / 64, LOADS_B = TK * CHB / 64;
-  static constexpr int LOADS = LOADS_A + LOADS_B + (SCALE_BYTES_ > 0 ? 2 : 0);
+  // scale tiles of more than 1 KB take SCALE_LOADS wave loads per operand
+  static constexpr int SCALE_LOADS = SCALE_BYTES_ > 1024 ? SCALE_BYTES_ / 1024 : 1;
+  static constexpr int LOADS = LOADS_A + LOADS_B + (SCALE_BYTES_ > 0 ? 2 * SCALE_LOADS : 0);
   static constexpr int SLOTS = (LOADS + WAVES - 1) / WAVES;  // per wave
   static constexpr int PER = LOADS / WAVES, HEAVY = LOADS % WAVES;
   static constexpr int OPA = TK * ROWA, OPB = TK * ROWB;
@@ -130,7 +133,7 @@ struct Cfg {
   static_assert(EPI_ROWS * EPI_CPR % THREADS == 0, "epilogue work must split evenly");
   static_assert(!PIPE || (TK == 32 && NS >= 3 && ELT == 2), "pipelined stages: bf16, 32 tokens");
   static_assert(EPI_ROWS % WM == 0, "epilogue row blocks hold whole wave rows");
-  static_assert(SCALE_BYTES <= 1024, "one wave load per scale tile");
+  static_assert(SCALE_BYTES <= 1024 || SCALE_BYTES % 1024 == 0, "whole wave loads per scale tile");
   static_assert((PER + 1) * (NS - 1) <= 63, "stage loads in flight fit the wait counter");
 };
 
@@ -140,6 +143,9 @@ using CfgF8 = Cfg<256, 256, 4, 128, 2, 1, 1024>;
 // fp8 widened to bf16: 256 x 128 per workgroup, 64 x 64 per wave (the widened
 // fragments need the registers a wider wave tile would take); two stages of 128
 using CfgF8h = Cfg<256, 128, 4, 128, 2, 1, 1024>;
+// fp8 with fp32 scales per 32 tokens: the 256 x 128 tile of CfgF8h, four scale rows
+// per 128-token stage (4 KB of scale tile per operand)
+using CfgF8h32 = Cfg<256, 128, 4, 128, 2, 1, 4096>;
 // bf16: 256 x 256 per workgroup, 8 waves of 64 x 128 (two per SIMD), a ring of four
 // 32-token stages; each wave reads stage kb+1's fragments while it runs stage kb's
 // MFMAs
@@ -514,23 +520,28 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
       const bool is_a = k < CF::LOADS_A;
       load16_lds(is_a ? ra : rb, is_a ? sA + 1024 * k : sB + 1024 * (k - CF::LOADS_A), lo.off[s]);
     } else if (KIND != BF16 && k < CF::LOADS) {
-      // scale tiles: fp32 -> one row of BM (BN) floats; E8M0 -> TK/gran rows of BM
-      // (BN) bytes. Scale rows per stage: fp32 -> the block's row (blocks of 128
-      // span 128/TK stages); E8M0 -> TK/gran rows, or the one row of the block when
-      // gran > TK.
-      constexpr int esz = KIND == F32S ? 4 : 1;
-      const int per = KIND == F32S || p.gran >= CF::TK ? 1 : CF::TK / p.gran;
-      const int nb_g = (Kg + p.gran - 1) / p.gran;
-      const int r0 = (CF::TK * kb) / p.gran;
+      // scale tiles: TK/gran rows of BM (BN) scales (fp32 or E8M0), or the one row of
+      // the block when gran >= TK; rows are stored one after the other in LDS. Load q
+      // of an operand's SCALE_LOADS brings its q-th kilobyte.
+      constexpr int esz = KIND == F32S || KIND == F32S32 ? 4 : 1;
+      // rows per stage: compile-time for the fp32 kinds (gran 128 and 32)
+      const int per = KIND == F32S ? 1 : KIND == F32S32 ? CF::TK / 32
+                      : p.gran >= CF::TK ? 1 : CF::TK / p.gran;
+      const int gran = KIND == F32S ? 128 : KIND == F32S32 ? 32 : p.gran;
+      const int nb_g = (Kg + gran - 1) / gran;
+      const int r0 = (CF::TK * kb) / gran;
       const int nrows = uniform(min(per, nb_g - r0));
       const int64_t r = (int64_t)boff_g + r0;
-      const bool is_a = k == CF::LOADS_A + CF::LOADS_B;
+      const int qs = k - (CF::LOADS_A + CF::LOADS_B);
+      const bool is_a = CF::SCALE_LOADS == 1 ? qs == 0 : qs < CF::SCALE_LOADS;
+      const int part = CF::SCALE_LOADS == 1 ? 0 : (is_a ? qs : qs - CF::SCALE_LOADS);
       const int ext = is_a ? p.M : p.N, c0 = is_a ? m0 : n0;
       const int width = is_a ? CF::BM : CF::BN;
       const int cpr = width * esz / 16;  // 16-byte chunks per scale row
-      const int sr = lane / cpr, c = lane - sr * cpr;
+      const int idx = 64 * part + lane;
+      const int sr = idx / cpr, c = idx - sr * cpr;
       const v4i rs = make_rsrc((is_a ? p.sa : p.sb) + r * ext * esz, (uint32_t)(nrows * ext * esz));
-      load16_lds(rs, sA + (is_a ? CF::SA_OFF : CF::SB_OFF),
+      load16_lds(rs, sA + (is_a ? CF::SA_OFF : CF::SB_OFF) + 1024 * part,
                  sr < per ? (uint32_t)(sr * ext * esz + c0 * esz + 16 * c) : kOobOffset);
     }
   }
@@ -706,6 +717,69 @@ __device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[
   if constexpr (PROMOTE) rescale(CF::NI - 1, CF::NJ - 1, prev);
 }
 
+// fp32 scales per 32 tokens: every 32-token step kk of a stage is its own block
+// (scale row kk). Each step's MFMA gives the block partial of sub-tile (i, jn), which
+// is rescaled by sa (x) sb on the VALU one MFMA behind. Precise: bf16 MFMA on widened
+// fp8; fast: the 16x16x32 fp8 MFMA, whose operand is this lane's 8 tokens as they
+// come from the transposing read.
+template <class CF, bool FAST>
+__device__ inline void compute_f32s32(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
+  constexpr int KK = CF::TK / 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  const int lrow = 8 * q + (j >> 1);
+  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const float* sSa = (const float*)(st + CF::SA_OFF);
+  const float* sSb = (const float*)(st + CF::SB_OFF);
+  v2i ar[CF::NI][KK];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) ar[i][kk] = tr8(aBase + 32 * kk * CF::ROWA + 16 * i);
+  auto rescale = [&](int pi, int pj, int pk, const v4f& x) {
+    const v4f sa = *(const v4f*)(sSa + pk * CF::BM + wm * CF::WM + 16 * pi + 4 * q);
+    const float sb = sSb[pk * CF::BN + wn * CF::WN + 16 * pj + j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[r] * sb, x[r], acc[pi][pj][r]);
+  };
+  v2i rnext[KK], bcur[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+  v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
+  constexpr int S = CF::NI * CF::NJ;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int jn = s / CF::NI, i = s % CF::NI;
+    if (i == 0) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) bcur[kk] = rnext[kk];
+      if (jn + 1 < CF::NJ) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      v4f x;
+      if constexpr (FAST)
+        x = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, ar[i][kk]),
+                                                       __builtin_bit_cast(long, bcur[kk]),
+                                                       v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      else
+        x = mfma_bf16(widen8(ar[i][kk], 1.0f), widen8(bcur[kk], 1.0f), v4f{0.f, 0.f, 0.f, 0.f});
+      const int t = s * KK + kk;  // step index; rescale step t - 1
+      if (t > 0) {
+        const int tp = t - 1, sp = tp / KK;
+        rescale(sp % CF::NI, sp / CF::NI, tp % KK, prev);
+      }
+      prev = x;
+    }
+  }
+  rescale(CF::NI - 1, CF::NJ - 1, KK - 1, prev);
+}
+
 // precise fp8 + E8M0: every fragment is widened with its power-of-two scale
 // (exact), then the bf16 MFMAs accumulate straight into acc.
 template <class CF>
@@ -815,6 +889,8 @@ __device__ inline void compute_stage(const unsigned char* st, int gran, bool pro
                                      v4f (&acc)[CF::NI][CF::NJ], v4f (&part)[CF::NI][CF::NJ]) {
   if constexpr (KIND == BF16) {
     compute_bf16<CF>(st, acc);
+  } else if constexpr (KIND == F32S32) {
+    compute_f32s32<CF, FAST>(st, acc);
   } else if constexpr (KIND == F32S && FAST) {
     compute_fast_f32s<CF>(st, acc);
   } else if constexpr (KIND == F32S) {
@@ -1144,6 +1220,9 @@ static Launch launch_of() {
 
 // bf16 output (whole tiles only: stream-K is not taken with a bf16 D)
 static Launch pick_outb(int kind, bool fast, bool small) {
+  if (kind == F32S32)
+    return fast ? launch_of<F32S32, true, CfgF8h32, false, true>()
+                : launch_of<F32S32, false, CfgF8h32, false, true>();
   if (kind == BF16)
     return small ? launch_of<BF16, false, CfgB16s, false, true>()
                  : launch_of<BF16, false, CfgB16, false, true>();
@@ -1159,6 +1238,11 @@ static Launch pick_outb(int kind, bool fast, bool small) {
 static Launch pick(int kind, bool fast, bool small = false, bool split = false,
                    bool outb = false) {
   if (outb) return pick_outb(kind, fast, small);
+  if (kind == F32S32)
+    return fast ? (split ? launch_of<F32S32, true, CfgF8h32, true>()
+                         : launch_of<F32S32, true, CfgF8h32>())
+                : (split ? launch_of<F32S32, false, CfgF8h32, true>()
+                         : launch_of<F32S32, false, CfgF8h32>());
   if (split) {
     if (kind == BF16) return launch_of<BF16, false, CfgB16, true>();
     if (kind == F32S)
@@ -1186,7 +1270,11 @@ static int device_setup(int dev) {
     int cus = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const Launch all[17] = {pick(BF16, false, false, false, true),
+    const Launch all[23] = {pick(F32S32, false), pick(F32S32, true),
+                            pick(F32S32, false, false, true), pick(F32S32, true, false, true),
+                            pick(F32S32, false, false, false, true),
+                            pick(F32S32, true, false, false, true),
+                            pick(BF16, false, false, false, true),
                             pick(BF16, false, true, false, true),
                             pick(F32S, false, false, false, true),
                             pick(F32S, true, false, false, true),
@@ -1273,7 +1361,6 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
   if (fast && dtype == KG_BF16) return KG_ERR_DTYPE;
   if (G < 0 || M < 0 || N < 0 || K_total < 0 || workspace_bytes < 0) return KG_ERR_SHAPE;
   if (dtype != KG_BF16 && gran_k != 32 && gran_k != 128) return KG_ERR_GRAN;
-  if (dtype == KG_E4M3_F32SCALE && gran_k != 128) return KG_ERR_UNSUPPORTED;
   if (G > kMaxGroups) return KG_ERR_UNSUPPORTED;
   if (M > (1 << 24) || N > (1 << 24) || K_total > INT32_MAX) return KG_ERR_UNSUPPORTED;
   if ((int64_t)M * N > (int64_t)1 << 29) return KG_ERR_UNSUPPORTED;  // 32-bit byte offsets in one expert's C
@@ -1298,7 +1385,9 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
       (C != nullptr && overlap(workspace, (size_t)workspace_bytes, C, dbytes)))
     return KG_ERR_ALIAS;
 
-  const int kind = dtype == KG_E4M3_F32SCALE ? F32S : dtype == KG_E4M3_UE8M0 ? E8M0 : BF16;
+  const int kind = dtype == KG_E4M3_F32SCALE ? (gran_k == 32 ? F32S32 : F32S)
+                   : dtype == KG_E4M3_UE8M0  ? E8M0
+                                             : BF16;
   int cus = 0;
   const int rc = current_cus(&cus);
   if (rc != KG_OK) return rc;

@@ -230,8 +230,11 @@ SINGLE = {single_name(*mnk): mnk for mnk in SINGLE_SHAPES}
 WORKLOADS = ("worked", "bf16", "zipf_fp8", "ue8m0_many", "local_share") + tuple(SINGLE)
 
 
-def workload(name, device="cpu", seed=0):
-    """The named workloads (see the module docstring)."""
+def workload(name, device="cpu", seed=0, gran_k=None):
+    """The named workloads (see the module docstring). `gran_k` replaces an fp8
+    workload's scale granularity (e.g. 32 for fp32 scales per 32 tokens)."""
+    if gran_k is not None:
+        return _regran(name, device, seed, gran_k)
     if name == "worked":
         return make_case(name, ks_worked(), 64, 128, E4M3_F32SCALE, 128, with_c=False,
                          seed=seed, device=device)
@@ -256,6 +259,21 @@ def workload(name, device="cpu", seed=0):
         return make_case(name, np.array([k], np.int32), m, n, E4M3_F32SCALE, 128, with_c=False,
                          seed=seed, device=device)
     raise KeyError(name)
+
+
+def _regran(name, device, seed, gran_k):
+    spec = {"zipf_fp8": (7168, 4096, E4M3_F32SCALE, True, dict(b_std=1e-3, a_outlier_p=0.01)),
+            "local_share": (7168, 4096, E4M3_F32SCALE, True, dict(b_std=1e-3, a_outlier_p=0.01)),
+            "ue8m0_many": (2048, 7168, E4M3_UE8M0, False, {})}
+    if name not in spec and name not in SINGLE:
+        raise KeyError(f"{name}: no scale granularity to replace")
+    if name in SINGLE:
+        m, n, k = SINGLE[name]
+        return make_case(name, np.array([k], np.int32), m, n, E4M3_F32SCALE, gran_k,
+                         with_c=False, seed=seed, device=device)
+    M, N, dt, with_c, kw = spec[name]
+    return make_case(name, workload_ks(name, seed), M, N, dt, gran_k, with_c=with_c, seed=seed,
+                     device=device, **kw)
 
 
 def workload_ks(name, seed=0):

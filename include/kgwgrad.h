@@ -93,10 +93,10 @@ typedef enum {
  *   gran_k tokens per scale block: 128 or 32 (fp8); ignored for bf16
  *   stream a hipStream_t (NULL: the default stream)
  *
- * Implemented combinations: (KG_E4M3_F32SCALE, 128), (KG_E4M3_UE8M0, 32),
- * (KG_E4M3_UE8M0, 128) and KG_BF16. (KG_E4M3_F32SCALE, 32) returns
- * KG_ERR_UNSUPPORTED. G is limited to 1024 (kg_max_groups), M and N to 2^24, M * N to
- * 2^29 and K_total to 2^31 - 1 (KG_ERR_UNSUPPORTED beyond).
+ * Implemented combinations: (KG_E4M3_F32SCALE, 128), (KG_E4M3_F32SCALE, 32),
+ * (KG_E4M3_UE8M0, 32), (KG_E4M3_UE8M0, 128) and KG_BF16. G is limited to 1024
+ * (kg_max_groups), M and N to 2^24, M * N to 2^29 and K_total to 2^31 - 1
+ * (KG_ERR_UNSUPPORTED beyond).
  *
  * Returns KG_OK after enqueueing, or an error code before enqueueing anything (D
  * untouched). G == 0, M == 0 or N == 0 return KG_OK without a launch. A ks that

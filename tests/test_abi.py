@@ -67,7 +67,6 @@ def call(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE 
     (dict(M=-16), B.KG_ERR_SHAPE),
     (dict(K=-1), B.KG_ERR_SHAPE),
     (dict(gran=64), B.KG_ERR_GRAN),
-    (dict(gran=32), B.KG_ERR_UNSUPPORTED),  # fp32 scales at 32 tokens: not built
     (dict(G=1025), B.KG_ERR_UNSUPPORTED),
     (dict(D=None), B.KG_ERR_NULL),
     (dict(ks=None), B.KG_ERR_NULL),

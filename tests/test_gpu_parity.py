@@ -114,7 +114,7 @@ def test_worked_shape_full():
 # ---------------------------------------------------------------- multi-tile ragged
 
 RAGGED = [300, 0, 129, 1, 513, 64]
-PATHS = [(F32, 128), (UE8, 32), (UE8, 128), (BF, 128)]
+PATHS = [(F32, 128), (F32, 32), (UE8, 32), (UE8, 128), (BF, 128)]
 
 
 @pytest.mark.parametrize("dtype,gran", PATHS)
@@ -147,7 +147,7 @@ def test_outliers_and_small_gradients(dtype, gran):
     check_close(D, D_ref, bound, "outliers")
 
 
-FAST_PATHS = [(F32, 128), (UE8, 32), (UE8, 128)]
+FAST_PATHS = [(F32, 128), (F32, 32), (UE8, 32), (UE8, 128)]
 
 
 @pytest.mark.parametrize("dtype,gran", FAST_PATHS)
@@ -195,7 +195,8 @@ SPLIT_SHAPES = [
 
 
 @pytest.mark.parametrize("dtype,gran,flags", [(BF, 128, 0), (F32, 128, 0), (UE8, 32, 0),
-                                              (UE8, 128, 0), (F32, 128, FAST), (UE8, 32, FAST)])
+                                              (UE8, 128, 0), (F32, 128, FAST), (UE8, 32, FAST),
+                                              (F32, 32, 0), (F32, 32, FAST)])
 @pytest.mark.parametrize("ks,M,N,with_c", SPLIT_SHAPES)
 def test_stream_k_workspace(ks, M, N, with_c, dtype, gran, flags):
     say("stream-K", dtype, gran, flags, ks, M, N, with_c)
@@ -436,7 +437,7 @@ def check_bf16_out(D_gpu, D_ref, bound, what="", fast=False):
         assert (lo == hi).mean() > 0.5, f"{what}: tolerance interval too wide to be a check"
 
 
-@pytest.mark.parametrize("dtype,gran", [(F32, 128), (UE8, 32), (UE8, 128), (BF, 128)])
+@pytest.mark.parametrize("dtype,gran", [(F32, 128), (F32, 32), (UE8, 32), (UE8, 128), (BF, 128)])
 @pytest.mark.parametrize("with_c", [False, True])
 @pytest.mark.parametrize("flags", [0, FAST])
 def test_bf16_output_variant(dtype, gran, with_c, flags):
@@ -508,3 +509,20 @@ def test_bf16_output_full_size_default_workload_sampled():
     check_bf16_out(got, ref, bound, "bf16 out full size")
     g0 = int(np.nonzero(case.ks == 0)[0][0])
     assert torch.equal(D[g0].view(torch.int16), Cb[g0].view(torch.int16))
+
+
+def test_f32_scales_per_32_tokens_full_size_sampled():
+    """fp32 scales per 32 tokens on the Zipf-routed shape (G = 32, M = 7168, N = 4096,
+    65536 tokens), both modes, sampled against the oracle."""
+    say("full size f32/32")
+    ks = inputs.workload_ks("zipf_fp8")
+    case = inputs.make_case("zipf_f32_32", ks, 7168, 4096, F32, 32, with_c=True, seed=0,
+                            device="cuda", b_std=1e-3, a_outlier_p=0.01)
+    t = to_dev(case)
+    D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev())
+    run_gpu(case, t, D=D)
+    sampled_check(case, t, D)
+    run_gpu(case, t, D=D, flags=FAST)
+    sampled_check(case, t, D, fast=True)
+    del D, t, case
+    torch.cuda.empty_cache()
