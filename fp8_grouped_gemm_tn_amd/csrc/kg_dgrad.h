@@ -187,27 +187,35 @@ __device__ inline void dgrad_compute(const unsigned char* st, float swv,
     v2i rnext[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * DCfg::ROWB);
+    // one column of sub-tiles at a time, its NI MFMA chains advanced together; the
+    // previous column is rescaled between this column's first MFMAs
     v8bf bf[KK];
-    v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f xprev[DCfg::NI];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int jn = s / DCfg::NI, i = s % DCfg::NI;
-      if (i == 0) {
+    for (int jn = 0; jn < DCfg::NJ; ++jn) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
-        if (jn + 1 < DCfg::NJ) {
+      for (int kk = 0; kk < KK; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
+      if (jn + 1 < DCfg::NJ) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            rnext[kk] = tr8(bBase + 32 * kk * DCfg::ROWB + 16 * (jn + 1));
+        for (int kk = 0; kk < KK; ++kk)
+          rnext[kk] = tr8(bBase + 32 * kk * DCfg::ROWB + 16 * (jn + 1));
+      }
+      v4f x[DCfg::NI];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int i = 0; i < DCfg::NI; ++i)
+          x[i] = mfma_bf16(af[i][kk], bf[kk], kk == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : x[i]);
+        if (kk == 0 && jn > 0) {
+#pragma unroll
+          for (int i = 0; i < DCfg::NI; ++i) rescale(i, jn - 1, xprev[i]);
         }
       }
-      v4f x = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) x = mfma_bf16(af[i][kk], bf[kk], x);
-      if (s > 0) rescale((s - 1) % DCfg::NI, (s - 1) / DCfg::NI, prev);
-      prev = x;
+      for (int i = 0; i < DCfg::NI; ++i) xprev[i] = x[i];
     }
-    rescale(DCfg::NI - 1, DCfg::NJ - 1, prev);
+#pragma unroll
+    for (int i = 0; i < DCfg::NI; ++i) rescale(i, DCfg::NJ - 1, xprev[i]);
   }
 }
 

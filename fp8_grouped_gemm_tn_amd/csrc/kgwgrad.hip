@@ -686,35 +686,48 @@ __device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[pi][pj][r] = fmaf(sa[r] * sb, x[r], acc[pi][pj][r]);
   };
-  constexpr int S = CF::NI * CF::NJ;
+  // One column jn of sub-tiles at a time: its NI partial sums are NI independent MFMA
+  // chains advanced together (step kk of every chain before step kk + 1 of any), so
+  // no MFMA waits for the result of the one before it; the previous column's
+  // rescale runs between this column's first MFMAs.
   v2i rnext[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
   v8bf bf[KK];
-  v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
+  v4f xprev[CF::NI];
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int jn = s / CF::NI, i = s % CF::NI;
-    if (i == 0) {
+  for (int jn = 0; jn < CF::NJ; ++jn) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
-      if (jn + 1 < CF::NJ) {
+    for (int kk = 0; kk < KK; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
+    if (jn + 1 < CF::NJ) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+      for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+    }
+    v4f x[CF::NI];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < CF::NI; ++i)
+        x[i] = mfma_bf16(af[i][kk], bf[kk], kk == 0 ? part[i][jn] : x[i]);
+      if (PROMOTE && kk == 0 && jn > 0) {
+#pragma unroll
+        for (int i = 0; i < CF::NI; ++i) rescale(i, jn - 1, xprev[i]);
       }
     }
-    v4f x = part[i][jn];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) x = mfma_bf16(af[i][kk], bf[kk], x);
-    if constexpr (PROMOTE) {
-      if (s > 0) rescale((s - 1) % CF::NI, (s - 1) / CF::NI, prev);
-      prev = x;
-      part[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
-    } else {
-      part[i][jn] = x;
+    for (int i = 0; i < CF::NI; ++i) {
+      if constexpr (PROMOTE) {
+        xprev[i] = x[i];
+        part[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
+      } else {
+        part[i][jn] = x[i];
+      }
     }
   }
-  if constexpr (PROMOTE) rescale(CF::NI - 1, CF::NJ - 1, prev);
+  if constexpr (PROMOTE) {
+#pragma unroll
+    for (int i = 0; i < CF::NI; ++i) rescale(i, CF::NJ - 1, xprev[i]);
+  }
 }
 
 // fp32 scales per 32 tokens: every 32-token step kk of a stage is its own block
