@@ -76,10 +76,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def counters_for(workload, fast, bf16_out=False):
+def counters_for(workload, fast, bf16_out=False, kernel="kg_wgrad"):
     """HBM bytes per launch measured with rocprofv3 counters for this kernel source."""
     name = f"{workload}{'_fast' if fast else ''}{'_bf16out' if bf16_out else ''}"
-    path = os.path.join(ROOT, "profiles", f"kg_wgrad_{name}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -104,17 +104,26 @@ def _counter_rows(path):
 
 
 def ingest_counters(fetch_csv, write_csv, name):
-    """HBM bytes per launch of kg_wgrad from FETCH_SIZE / WRITE_SIZE (KiB per
+    """HBM bytes per launch of a kernel from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB plain copy
-    recorded in the same CSV (run the profiled bench.py with --copy-calib)."""
+    recorded in the same CSV (run the profiled bench.py with --copy-calib). `name` is
+    the record's name, prefixed "dgrad:" or "requant:" for those kernels (kg_wgrad
+    otherwise)."""
+    kern = "kg_wgrad"
+    for prefix in ("dgrad", "requant"):
+        if name.startswith(prefix + ":"):
+            kern, name = "kg_" + prefix, name[len(prefix) + 1:]
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path)
-        mine = [v[counter] for (d, k), v in rows.items() if "kg_wgrad_kernel" in k]
-        copy = [v[counter] for (d, k), v in rows.items()
-                if "copy" in k.lower() and "kg_" not in k
-                and COPY_BYTES / 1024 / 4 < v[counter] < COPY_BYTES / 1024 * 4]
-        assert mine, f"no kg_wgrad dispatch in {path}"
+        mine = [v[counter] for (d, k), v in rows.items() if kern + "_kernel" in k]
+        # the calibration copy is the run's first copy dispatch (bench.py issues it
+        # before it generates any input, which may copy too)
+        copies = sorted((int(d), v[counter]) for (d, k), v in rows.items()
+                        if "copy" in k.lower() and "kg_" not in k)
+        copy = [copies[0][1]] if copies and \
+            COPY_BYTES / 1024 / 4 < copies[0][1] < COPY_BYTES / 1024 * 4 else []
+        assert mine, f"no {kern} dispatch in {path}"
         assert copy, f"no 1 GiB copy dispatch in {path}"
         factor = (COPY_BYTES / 1024) / max(copy)   # true KiB per counted KiB
         per_launch = sorted(mine)[len(mine) // 2] * factor * 1024
@@ -124,10 +133,24 @@ def ingest_counters(fetch_csv, write_csv, name):
            "traffic_bytes": int(res["FETCH_SIZE"]["bytes_per_launch"] +
                                 res["WRITE_SIZE"]["bytes_per_launch"]),
            "counters": res}
-    path = os.path.join(ROOT, "profiles", f"kg_wgrad_{name}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kern}_{name}_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def copy_calibration(args, dev):
+    """With --copy-calib: one plain 1 GiB device copy (untimed), so that a counter run
+    sees it beside the kernel (HBM counter calibration)."""
+    if not args.copy_calib:
+        return
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def warm_up(step, warmup, seconds=1.0):
@@ -201,6 +224,7 @@ def requant_main(args):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl, H, gran, kind, src, descr = REQUANT[args.requant]
     dev = torch.device("cuda:0")
+    copy_calibration(args, dev)
     ks = inputs.workload_ks(wl, args.seed)
     K = int(ks.astype(np.int64).sum())
     nblk = int(sum((int(k) + gran - 1) // gran for k in ks))
@@ -257,7 +281,8 @@ def requant_main(args):
         "data": "synthetic (seeded N(0,1) values, the workload's seeded routing)",
         "config": {"workload": descr, "tokens": K, "H": H, "G": int(ks.size), "gran_k": gran},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
+                     "traffic": counters_for(args.requant, False, False, "kg_requant"),
                      "algorithmic_bytes": nbytes},
     }
     if not args.no_cpu:
@@ -294,6 +319,7 @@ def dgrad_main(args):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    copy_calibration(args, dev)
     c = inputs.dgrad_workload(args.dgrad, device="cuda", seed=args.seed)
     ms = torch.from_numpy(c.ms).to(dev)
     out = torch.float32 if args.fp32_out else torch.bfloat16
@@ -331,7 +357,8 @@ def dgrad_main(args):
         roof = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = counters_for(args.dgrad[len("dgrad_"):], bool(args.fast), not args.fp32_out,
+                                   "kg_dgrad")
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     line = {
@@ -437,13 +464,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    if args.copy_calib:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args, dev)
     case = inputs.workload(args.workload, device="cuda", seed=args.seed, gran_k=args.gran_k)
     A, B = case.A, case.B
     sa, sb, C = case.sa, case.sb, case.C

@@ -316,9 +316,11 @@ class DgradCase:
         return 2 * self.M_total * self.N * self.K
 
     def algorithmic_bytes(self, out_bytes: int = 2) -> int:
-        """A, W, their scales and D (out_bytes per element) once."""
-        return (self.M_total * self.K + self.G * self.K * self.N + self.sa.numel() * 4
-                + self.sw.numel() * 4 + self.M_total * self.N * out_bytes)
+        """A, the weights of experts that have tokens, their scales and D (out_bytes per
+        element) once."""
+        live = int((self.ms > 0).sum())
+        return (self.M_total * self.K + live * self.K * self.N + self.sa.numel() * 4
+                + live * (self.K // 128) * (self.N // 128) * 4 + self.M_total * self.N * out_bytes)
 
     def host(self):
         cpu = lambda t: t.detach().cpu().numpy()
