@@ -91,6 +91,23 @@ class Case:
         return nbytes
 
 
+def k_major(X: torch.Tensor, extra: int = 0) -> torch.Tensor:
+    """K-major (NT) copy of a token-major operand X [K_total, C]: a [C, K_total] view
+    (stride ld) of a [C, ld] buffer whose rows are whole 16-byte units with at least
+    `extra` columns of padding; the padding holds NaN codes (e4m3 0x7F, bf16 0x7FC0),
+    so a kernel that reads it shows NaN."""
+    K, Cn = X.shape
+    elt = X.element_size()
+    unit = 16 // elt
+    ld = (K + extra + unit - 1) // unit * unit
+    if X.dtype == torch.bfloat16:
+        buf = torch.full((Cn, ld), 0x7FC0, dtype=torch.int16, device=X.device).view(torch.bfloat16)
+    else:
+        buf = torch.full((Cn, ld), 0x7F, dtype=X.dtype, device=X.device)
+    buf[:, :K] = X.t()
+    return buf[:, :K]
+
+
 # ----------------------------------------------------------------- routing
 
 def ks_worked():

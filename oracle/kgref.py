@@ -241,3 +241,33 @@ def dgrad_sampled(A, sa, W, sw, ms, N, K, st, sn, threads=0):
                                    M_total, st.size, _ptr(st), _ptr(sn), _ptr(out), _ptr(bound),
                                    threads)
     return rc, out, bound
+
+
+def token_major(Xt, K_total):
+    """The K-major (NT) operand layout: channel m's K_total token values are
+    contiguous, Xt[m, t] (rows may be longer than K_total; the rest is padding and
+    is never read). Returns the same matrix token-major, X[t, m] = Xt[m, t] (issue
+    page: dw = dy^t x with dy^t as A [M, K] and x^t as B [N, K], K = tokens)."""
+    Xt = np.asarray(Xt)
+    if Xt.ndim != 2 or Xt.shape[1] < K_total:
+        raise ValueError("K-major operand must be [channels, >= K_total]")
+    return np.ascontiguousarray(Xt[:, :K_total].T)
+
+
+def wgrad_nt(At, sa, Bt, sb, C, ks, M, N, gran_k, dtype, K_total=None, **kw):
+    """wgrad with K-major operands At [M, >= K_total] and Bt [N, >= K_total]: the
+    same D as wgrad on their token-major forms; scales keep their [blocks, M] and
+    [blocks, N] layout."""
+    if K_total is None:
+        K_total = int(np.asarray(ks, np.int64).sum())
+    return wgrad(token_major(At, K_total), sa, token_major(Bt, K_total), sb, C, ks, M, N,
+                 gran_k, dtype, K_total=K_total, **kw)
+
+
+def wgrad_sampled_nt(At, sa, Bt, sb, C, ks, M, N, gran_k, dtype, sg, sm, sn, K_total=None,
+                     **kw):
+    """wgrad_sampled with K-major operands (see wgrad_nt)."""
+    if K_total is None:
+        K_total = int(np.asarray(ks, np.int64).sum())
+    return wgrad_sampled(token_major(At, K_total), sa, token_major(Bt, K_total), sb, C, ks, M,
+                         N, gran_k, dtype, sg, sm, sn, K_total=K_total, **kw)
