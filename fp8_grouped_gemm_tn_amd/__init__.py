@@ -11,4 +11,5 @@ from ._binding import (KG_BF16, KG_E4M3_F32SCALE, KG_E4M3_UE8M0, KG_ERR_ALIAS,  
                        kg_status, kg_wgrad, kg_wgrad_raw, kg_wgrad_workspace_bytes,
                        kg_wgrad_workspace_flag_bytes,
                        kg_wgrad_ws_raw, new_workspace, KG_SRC_BF16, KG_SRC_E4M3_1X128,
-                       kg_requant, kg_requant_raw, kg_dgrad, kg_dgrad_raw)
+                       kg_requant, kg_requant_raw, kg_dgrad, kg_dgrad_raw,
+                       kg_wgrad_nt, kg_wgrad_nt_raw)

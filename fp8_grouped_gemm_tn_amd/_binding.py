@@ -30,6 +30,10 @@ SIGNATURES = {
                         _vp]),
     "kg_wgrad_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32,
                            _vp, _i64, _vp]),
+    "kg_wgrad_nt": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64,
+                           _i32, _i32, _vp]),
+    "kg_wgrad_nt_ws": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                              _i64, _i32, _i32, _vp, _i64, _vp]),
     "kg_wgrad_workspace_bytes": (_i64, []),
     "kg_wgrad_workspace_flag_bytes": (_i64, []),
     "kg_status": (_i32, [_vp]),
@@ -130,6 +134,40 @@ def kg_wgrad(A, sa, B, sb, C, D, ks, gran_k, dtype, K_total=None, stream=None, w
                              workspace.numel() * workspace.element_size(), stream)
     if rc != KG_OK:
         raise KgError(rc, "kg_wgrad")
+    return D
+
+
+def kg_wgrad_nt_raw(At, lda, sa, Bt, ldb, sb, C, D, ks, G, M, N, K_total, gran_k, dtype,
+                    ws=None, ws_bytes=0, stream=None):
+    """Call kg_wgrad_nt (or kg_wgrad_nt_ws when `ws` is given); returns the status."""
+    if ws is None:
+        return lib().kg_wgrad_nt(_ptr(At), int(lda), _ptr(sa), _ptr(Bt), int(ldb), _ptr(sb),
+                                 _ptr(C), _ptr(D), _ptr(ks), int(G), int(M), int(N), int(K_total),
+                                 int(gran_k), int(dtype), _stream(stream))
+    return lib().kg_wgrad_nt_ws(_ptr(At), int(lda), _ptr(sa), _ptr(Bt), int(ldb), _ptr(sb),
+                                _ptr(C), _ptr(D), _ptr(ks), int(G), int(M), int(N), int(K_total),
+                                int(gran_k), int(dtype), _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def kg_wgrad_nt(At, sa, Bt, sb, C, D, ks, gran_k, dtype, stream=None, workspace=None):
+    """kg_wgrad with K-major operands: At [M, K_total] and Bt [N, K_total] with unit
+    stride along tokens (row strides, e.g. of a padded buffer, are passed as lda and
+    ldb). D [G, M, N]; a bfloat16 D selects the bf16-output variant."""
+    import torch
+    G, M, N = D.shape
+    if At.dim() != 2 or Bt.dim() != 2 or At.stride(1) != 1 or Bt.stride(1) != 1:
+        raise ValueError("At and Bt must be 2-D with unit stride along tokens")
+    if At.shape[1] != Bt.shape[1]:
+        raise ValueError("At and Bt must have the same number of tokens")
+    if D.dtype == torch.bfloat16:
+        dtype |= KG_FLAG_D_BF16
+    if C is not None and C.dtype != D.dtype:
+        raise TypeError("C and D must have the same dtype")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = kg_wgrad_nt_raw(At, At.stride(0), sa, Bt, Bt.stride(0), sb, C, D, ks, G, M, N,
+                         At.shape[1], gran_k, dtype, workspace, ws_bytes, stream)
+    if rc != KG_OK:
+        raise KgError(rc, "kg_wgrad_nt")
     return D
 
 

@@ -71,6 +71,7 @@ struct Params {
   int G, M, N;
 
   int64_t K_total;
+  uint32_t lda_b, ldb_b;  // K-major kernels: row strides of A and B in bytes
   int gran;  // tokens per scale row
   int tiles_m, tiles_n;
   // stream-K mode when ws != nullptr: per-workgroup partial tiles and ready flags
@@ -84,32 +85,44 @@ struct Params {
 // each wave reads stage kb+1's fragments into registers before it issues stage kb's
 // MFMAs (bf16 only).
 template <int BM_, int BN_, int WAVES_M_, int TK_, int NS_, int ELT_, int SCALE_BYTES_,
-          int THREADS_ = 512, bool PIPE_ = false>
+          int THREADS_ = 512, bool PIPE_ = false, bool NT_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, TK = TK_, NS = NS_, ELT = ELT_;
   static constexpr int THREADS = THREADS_, WAVES = THREADS_ / 64;
   static constexpr bool PIPE = PIPE_;
+  // NT: K-major operands (token index contiguous in memory)
+  static constexpr bool NT = NT_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES / WAVES_M_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int NI = WM / 16, NJ = WN / 16;
-  // LDS rows: one token each, BM (BN) elements + PAD bytes. With the lane-to-row
-  // maps of the compute policies, the rows one half-wave reads then start in
-  // distinct bank windows (fp8: 16-byte reads, row stride = 17 x 16 B; bf16: 32-byte
-  // reads, row stride = 34 x 16 B).
-  static constexpr int PAD = ELT == 2 ? 32 : 16;
-  static constexpr int ROWA = BM * ELT + PAD, ROWB = BN * ELT + PAD;
-  static constexpr int CHA = ROWA / 16, CHB = ROWB / 16;        // 16-byte chunks per row
-  static constexpr int DCA = BM * ELT / 16, DCB = BN * ELT / 16;  // of which data
+  // Token-major operands: LDS rows of one token each, BM (BN) elements + PAD bytes.
+  // With the lane-to-row maps of the compute policies, the rows one half-wave reads
+  // then start in distinct bank windows (fp8: 16-byte reads, row stride = 17 x 16 B;
+  // bf16: 32-byte reads, row stride = 34 x 16 B).
+  // K-major operands: LDS rows of one channel each, the stage's TK tokens (128
+  // bytes); every pair of rows is followed by 16 bytes of padding, so that the 16
+  // rows of a sub-tile, read at one byte offset, start in 16 distinct 4-bank groups.
+  // The load layout's "row" is then a pair of channels (ROW = 272 bytes).
+  static constexpr int PAD = NT ? 16 : ELT == 2 ? 32 : 16;
+  static constexpr int ROWA = NT ? 2 * TK * ELT + PAD : BM * ELT + PAD;
+  static constexpr int ROWB = NT ? 2 * TK * ELT + PAD : BN * ELT + PAD;
+  static constexpr int CHA = ROWA / 16, CHB = ROWB / 16;  // 16-byte chunks per row
+  static constexpr int DCA = (ROWA - PAD) / 16;           // of which data
+  static constexpr int DCB = (ROWB - PAD) / 16;
+  static constexpr int RA = NT ? BM / 2 : TK, RB = NT ? BN / 2 : TK;  // LDS rows per operand
+  // K-major: byte offset of channel row r within its operand, and of 16 channels
+  static __host__ __device__ constexpr int nt_row(int r) { return (r >> 1) * ROWA + (r & 1) * TK * ELT; }
+  static constexpr int NT_SUB = 8 * ROWA;
   // A stage is LOADS wave loads of 1 KB: LOADS_A of A rows, LOADS_B of B rows and,
   // with scales, one scale tile per operand. Load k of a stage is issued by wave
   // k % WAVES, so the first HEAVY waves issue PER + 1 loads and the others PER.
-  static constexpr int LOADS_A = TK * CHA / 64, LOADS_B = TK * CHB / 64;
+  static constexpr int LOADS_A = RA * CHA / 64, LOADS_B = RB * CHB / 64;
   // scale tiles of more than 1 KB take SCALE_LOADS wave loads per operand
   static constexpr int SCALE_LOADS = SCALE_BYTES_ > 1024 ? SCALE_BYTES_ / 1024 : 1;
   static constexpr int LOADS = LOADS_A + LOADS_B + (SCALE_BYTES_ > 0 ? 2 * SCALE_LOADS : 0);
   static constexpr int SLOTS = (LOADS + WAVES - 1) / WAVES;  // per wave
   static constexpr int PER = LOADS / WAVES, HEAVY = LOADS % WAVES;
-  static constexpr int OPA = TK * ROWA, OPB = TK * ROWB;
+  static constexpr int OPA = RA * ROWA, OPB = RB * ROWB;
   static constexpr int SCALE_BYTES = SCALE_BYTES_;
   static constexpr int SA_OFF = OPA + OPB, SB_OFF = SA_OFF + SCALE_BYTES;
   static constexpr int STAGE = SB_OFF + SCALE_BYTES;
@@ -127,7 +140,8 @@ struct Cfg {
   static constexpr int EPI_PER = EPI_ROWS * EPI_CPR / THREADS;    // float4 per thread
   static constexpr int EPI_LOADS = EPI_ROWS * EPI_CPR / 64;       // wave loads of C
   static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile must be whole sub-tile pairs");
-  static_assert(TK * CHA % 64 == 0 && TK * CHB % 64 == 0, "stage must be whole wave loads");
+  static_assert(RA * CHA % 64 == 0 && RB * CHB % 64 == 0, "stage must be whole wave loads");
+  static_assert(!NT || (TK * ELT == 128 && !PIPE), "K-major rows: 128 bytes, plain stages");
   static_assert(EPI_BYTES <= NS * STAGE, "epilogue must fit the stages");
   static_assert(NS >= 2, "at least two stages");
   static_assert(EPI_ROWS * EPI_CPR % THREADS == 0, "epilogue work must split evenly");
@@ -153,6 +167,32 @@ using CfgB16 = Cfg<256, 256, 4, 32, 4, 2, 0, 512, true>;
 // bf16, 128 x 256 per workgroup (64 x 64 per wave) for problems with few tiles
 using CfgB16s = Cfg<128, 256, 2, 64, 2, 2, 0>;
 
+// K-major operands: the same tiles with 128-byte channel rows per stage (fp8: 128
+// tokens; bf16: 64 tokens in two plain stages instead of the pipelined ring)
+using CfgF8N = Cfg<256, 256, 4, 128, 2, 1, 1024, 512, false, true>;
+using CfgF8hN = Cfg<256, 128, 4, 128, 2, 1, 1024, 512, false, true>;
+using CfgF8h32N = Cfg<256, 128, 4, 128, 2, 1, 4096, 512, false, true>;
+using CfgB16N = Cfg<256, 256, 4, 64, 2, 2, 0, 512, false, true>;
+using CfgB16sN = Cfg<128, 256, 2, 64, 2, 2, 0, 512, false, true>;
+
+// the configurations of one operand layout
+template <bool NT>
+struct Cfgs {
+  using F8 = CfgF8;
+  using F8h = CfgF8h;
+  using F8h32 = CfgF8h32;
+  using B16 = CfgB16;
+  using B16s = CfgB16s;
+};
+template <>
+struct Cfgs<true> {
+  using F8 = CfgF8N;
+  using F8h = CfgF8hN;
+  using F8h32 = CfgF8h32N;
+  using B16 = CfgB16N;
+  using B16s = CfgB16sN;
+};
+
 // This lane's global byte offsets for its loads of a stage (slot s: load
 // k = w + WAVES * s), relative to the stage's first byte (row 0, column m0 or n0) of
 // the operand the load belongs to; the same for every stage and item of a launch.
@@ -172,7 +212,16 @@ __device__ inline LoadOffsets<CF> load_offsets(const Params& p) {
   for (int s = 0; s < CF::SLOTS; ++s) {
     const int k = w + CF::WAVES * s;
     o.off[s] = kOobOffset;
-    if (k < CF::LOADS_A) {
+    if constexpr (CF::NT) {
+      // chunk ch of channel pair `pair`: chunk ch & 7 of channel 2 pair + ch / 8
+      if (k < CF::LOADS_A + CF::LOADS_B) {
+        const bool is_a = k < CF::LOADS_A;
+        const int idx = 64 * (is_a ? k : k - CF::LOADS_A) + lane;
+        const int pair = idx / CF::CHA, ch = idx - pair * CF::CHA;
+        if (ch < CF::DCA)
+          o.off[s] = (2 * pair + (ch >> 3)) * (is_a ? p.lda_b : p.ldb_b) + 16 * (ch & 7);
+      }
+    } else if (k < CF::LOADS_A) {
       const int idx = 64 * k + lane;
       const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
       if (ch < CF::DCA) o.off[s] = row * eM + 16 * ch;
@@ -505,11 +554,26 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
   const int rows = uniform(min(CF::TK, Kg - CF::TK * kb));
   const int64_t t0 = t_begin + (int64_t)CF::TK * kb;
   const int eM = p.M * CF::ELT, eN = p.N * CF::ELT;
-  // the resource starts at (row 0, column m0) and ends with the expert's last row
-  // of this stage: rows past it, and columns past the row end of the last row,
-  // read as zero
-  const v4i ra = make_rsrc(p.A + t0 * eM + m0 * CF::ELT, (uint32_t)(rows * eM - m0 * CF::ELT));
-  const v4i rb = make_rsrc(p.B + t0 * eN + n0 * CF::ELT, (uint32_t)(rows * eN - n0 * CF::ELT));
+  v4i ra, rb;
+  // K-major: chunks of the stage's last 16-byte unit that hold no token of the
+  // expert load as zero (one partial chunk per row remains, see nt_tail_zero)
+  const bool nt_tail = CF::NT && rows < CF::TK;
+  if constexpr (CF::NT) {
+    // the resource starts at (channel m0, token t0) and ends with the operand: rows
+    // past the last channel read as zero. The host keeps the offsets of 256 rows
+    // below 0xFFFFFF80; a longer range is cut at kOobOffset, so that the masked
+    // chunks (offset kOobOffset) stay out of range.
+    const int64_t ta = t0 * CF::ELT;
+    const int64_t na = (int64_t)(p.M - m0) * p.lda_b - ta, nb = (int64_t)(p.N - n0) * p.ldb_b - ta;
+    ra = make_rsrc(p.A + (int64_t)m0 * p.lda_b + ta, (uint32_t)min(na, (int64_t)kOobOffset));
+    rb = make_rsrc(p.B + (int64_t)n0 * p.ldb_b + ta, (uint32_t)min(nb, (int64_t)kOobOffset));
+  } else {
+    // the resource starts at (row 0, column m0) and ends with the expert's last row
+    // of this stage: rows past it, and columns past the row end of the last row,
+    // read as zero
+    ra = make_rsrc(p.A + t0 * eM + m0 * CF::ELT, (uint32_t)(rows * eM - m0 * CF::ELT));
+    rb = make_rsrc(p.B + t0 * eN + n0 * CF::ELT, (uint32_t)(rows * eN - n0 * CF::ELT));
+  }
   const uint32_t sA = lds_addr(st), sB = sA + CF::OPA;
 #pragma unroll
   for (int s = 0; s < CF::SLOTS; ++s) {
@@ -518,7 +582,25 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
       // one load instruction per slot; the operand (resource and LDS base) is a
       // scalar select, not a branch
       const bool is_a = k < CF::LOADS_A;
-      load16_lds(is_a ? ra : rb, is_a ? sA + 1024 * k : sB + 1024 * (k - CF::LOADS_A), lo.off[s]);
+      uint32_t off = lo.off[s];
+      if (nt_tail) {
+        // chunks past the expert's tokens load zeros. The partial chunk of the
+        // operand's last channel could run past the end of the buffer: it loads
+        // the 16 bytes that end there instead (nt_tail_zero moves its bytes into
+        // place).
+        const int idx = 64 * (is_a ? k : k - CF::LOADS_A) + lane;
+        const int pair = idx / CF::CHA, ch = idx - pair * CF::CHA;
+        const int c = ch & 7, nbytes = rows * CF::ELT;
+        if (ch < CF::DCA) {
+          if (16 * c >= nbytes) {
+            off = kOobOffset;
+          } else if (16 * c + 16 > nbytes && 2 * pair + (ch >> 3) == (is_a ? p.M - m0 : p.N - n0) - 1) {
+            const int64_t d = t0 * CF::ELT + 16 * c + 16 - (is_a ? p.lda_b : p.ldb_b);
+            if (d > 0) off -= (uint32_t)d;
+          }
+        }
+      }
+      load16_lds(is_a ? ra : rb, is_a ? sA + 1024 * k : sB + 1024 * (k - CF::LOADS_A), off);
     } else if (KIND != BF16 && k < CF::LOADS) {
       // scale tiles: TK/gran rows of BM (BN) scales (fp32 or E8M0), or the one row of
       // the block when gran >= TK; rows are stored one after the other in LDS. Load q
@@ -544,6 +626,38 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
       load16_lds(rs, sA + (is_a ? CF::SA_OFF : CF::SB_OFF) + 1024 * part,
                  sr < per ? (uint32_t)(sr * ext * esz + c0 * esz + 16 * c) : kOobOffset);
     }
+  }
+}
+
+// K-major stage whose last 16-byte unit is partial (the expert's token count times
+// the element size is not a multiple of 16): that chunk of every row of both
+// operands also holds the next bytes of the row (another expert's tokens, or
+// padding). Zero its bytes past the expert's last token. In the operand's last
+// channel, whose chunk was loaded d bytes early when it would have run past the end
+// of the buffer (load_stage), first move the valid bytes down by d. The stage's
+// loads must be complete and visible; the caller barriers afterwards.
+template <class CF>
+__device__ inline void nt_tail_zero(const Params& p, unsigned char* st, int rows, int64_t t0,
+                                    int m0, int n0) {
+  const int nbytes = rows * CF::ELT;
+  const int c = nbytes >> 4, rem = nbytes & 15;
+  for (int r = threadIdx.x; r < CF::BM + CF::BN; r += CF::THREADS) {
+    const bool is_a = r < CF::BM;
+    const int rr = is_a ? r : r - CF::BM;
+    unsigned char* chp = st + (is_a ? 0 : CF::OPA) + CF::nt_row(rr) + 16 * c;
+    if (rr == (is_a ? p.M - m0 : p.N - n0) - 1) {
+      const int d = (int)(t0 * CF::ELT + 16 * c + 16 - (is_a ? p.lda_b : p.ldb_b));
+      if (d > 0)
+        for (int x = 0; x < rem; ++x) chp[x] = chp[x + d];  // rem + d <= 16
+    }
+    v4i v = *(v4i*)chp;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int keep = rem - 4 * w;  // bytes of dword w to keep
+      const unsigned m = keep >= 4 ? 0xFFFFFFFFu : keep <= 0 ? 0u : (1u << (8 * keep)) - 1u;
+      v[w] &= (int)m;
+    }
+    *(v4i*)chp = v;
   }
 }
 
@@ -580,6 +694,44 @@ __device__ inline float e8m0_scale(int e) {
   return e == 255 ? __builtin_nanf("") : __builtin_ldexpf(1.0f, e - 127);
 }
 
+// Fragment readers. `base` is this lane's base in the operand: token-major, its row
+// of the transposing read; K-major, its channel row of the wave's first sub-tile
+// plus its first token byte (the K-major offsets below are then immediates). Both
+// layouts give a lane the same tokens, so the MFMAs see the same operands.
+// fp8, tokens 32kk + 8q .. +7 of sub-tile row (column) i (K-major base: + 8q):
+template <class CF, int ROW>
+__device__ inline v2i rd8(const unsigned char* base, int i, int kk) {
+  if constexpr (CF::NT)
+    return *(const v2i*)(base + i * CF::NT_SUB + 32 * kk);
+  else
+    return tr8(base + 32 * kk * ROW + 16 * i);
+}
+
+// fast fp8, the 32 bytes of frag_f8: token runs 32(q>>1) + 8(q&1) + {0, 16, 64, 80}
+// (K-major base: + 32(q>>1) + 8(q&1))
+template <class CF, int ROW>
+__device__ inline v8i rdf8(const unsigned char* base, int i) {
+  if constexpr (CF::NT) {
+    const unsigned char* r = base + i * CF::NT_SUB;
+    const v2i x0 = *(const v2i*)(r);
+    const v2i x1 = *(const v2i*)(r + 16);
+    const v2i x2 = *(const v2i*)(r + 64);
+    const v2i x3 = *(const v2i*)(r + 80);
+    return v8i{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+  } else {
+    return frag_f8<ROW>(base + 16 * i);
+  }
+}
+
+// bf16, tokens 32kk + 16h + 4q .. +3 of sub-tile row (column) i (K-major base: + 8q)
+template <class CF, int ROW>
+__device__ inline v4bf rd16(const unsigned char* base, int i, int kk, int h) {
+  if constexpr (CF::NT)
+    return *(const v4bf*)(base + i * CF::NT_SUB + 64 * kk + 32 * h);
+  else
+    return tr16(base + (32 * kk + 16 * h) * ROW + 32 * i);
+}
+
 // ---------------------------------------------------------------- compute policies
 
 // All policies: wave (wm, wn) owns rows [wm*WM, +WM) and cols [wn*WN, +WN) of the
@@ -594,15 +746,18 @@ __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF:
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = fast_row(q, j);
-  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
-  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const int lbyte = 32 * (q >> 1) + 8 * (q & 1);  // K-major: first token byte
+  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + lbyte
+                                      : st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + lbyte
+                                      : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const float* sSa = (const float*)(st + CF::SA_OFF);
   const float* sSb = (const float*)(st + CF::SB_OFF);
   v8i af[CF::NI];
 #pragma unroll
-  for (int i = 0; i < CF::NI; ++i) af[i] = frag_f8<CF::ROWA>(aBase + 16 * i);
+  for (int i = 0; i < CF::NI; ++i) af[i] = rdf8<CF, CF::ROWA>(aBase, i);
   constexpr int S = CF::NI * CF::NJ;
-  v8i bcur = frag_f8<CF::ROWB>(bBase), bnext = bcur;
+  v8i bcur = rdf8<CF, CF::ROWB>(bBase, 0), bnext = bcur;
   v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
   // rescale of sub-tile (pi, pj): acc += (sa[rows] * sb[col]) * partial
   auto rescale = [&](int pi, int pj, const v4f& part) {
@@ -614,7 +769,7 @@ __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF:
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int jn = s / CF::NI, i = s % CF::NI;
-    if (i == 0 && jn + 1 < CF::NJ) bnext = frag_f8<CF::ROWB>(bBase + 16 * (jn + 1));
+    if (i == 0 && jn + 1 < CF::NJ) bnext = rdf8<CF, CF::ROWB>(bBase, jn + 1);
     const v4f part = mfma_fp8(af[i], bcur, v4f{0.f, 0.f, 0.f, 0.f});
     if (s > 0) rescale((s - 1) % CF::NI, (s - 1) / CF::NI, prev);
     prev = part;
@@ -632,8 +787,11 @@ __device__ inline void compute_fast_e8m0(const unsigned char* st, int gran,
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = fast_row(q, j);
-  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
-  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const int lbyte = 32 * (q >> 1) + 8 * (q & 1);  // K-major: first token byte
+  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + lbyte
+                                      : st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + lbyte
+                                      : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const unsigned char* sSa = st + CF::SA_OFF;
   const unsigned char* sSb = st + CF::SB_OFF;
   const int srow = gran == 32 ? q : 0;
@@ -641,13 +799,13 @@ __device__ inline void compute_fast_e8m0(const unsigned char* st, int gran,
   int ea[CF::NI];
 #pragma unroll
   for (int i = 0; i < CF::NI; ++i) {
-    af[i] = frag_f8<CF::ROWA>(aBase + 16 * i);
+    af[i] = rdf8<CF, CF::ROWA>(aBase, i);
     ea[i] = sSa[srow * CF::BM + wm * CF::WM + 16 * i + j];
   }
-  v8i bcur = frag_f8<CF::ROWB>(bBase);
+  v8i bcur = rdf8<CF, CF::ROWB>(bBase, 0);
 #pragma unroll
   for (int jn = 0; jn < CF::NJ; ++jn) {
-    const v8i bnext = jn + 1 < CF::NJ ? frag_f8<CF::ROWB>(bBase + 16 * (jn + 1)) : bcur;
+    const v8i bnext = jn + 1 < CF::NJ ? rdf8<CF, CF::ROWB>(bBase, jn + 1) : bcur;
     const int eb = sSb[srow * CF::BN + wn * CF::WN + 16 * jn + j];
 #pragma unroll
     for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_fp8_e8m0(af[i], bcur, acc[i][jn], ea[i], eb);
@@ -670,8 +828,11 @@ __device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = 8 * q + (j >> 1);
-  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
-  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const int lbyte = 8 * q;  // K-major: first token byte
+  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + lbyte
+                                      : st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + lbyte
+                                      : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const float* sSa = (const float*)(st + CF::SA_OFF);
   const float* sSb = (const float*)(st + CF::SB_OFF);
   v8bf af[CF::NI][KK];
@@ -679,7 +840,7 @@ __device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[
   for (int i = 0; i < CF::NI; ++i)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      af[i][kk] = widen8(tr8(aBase + 32 * kk * CF::ROWA + 16 * i), 1.0f);
+      af[i][kk] = widen8(rd8<CF, CF::ROWA>(aBase, i, kk), 1.0f);
   auto rescale = [&](int pi, int pj, const v4f& x) {
     const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * pi + 4 * q);
     const float sb = sSb[wn * CF::WN + 16 * pj + j];
@@ -692,7 +853,7 @@ __device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[
   // rescale runs between this column's first MFMAs.
   v2i rnext[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, 0, kk);
   v8bf bf[KK];
   v4f xprev[CF::NI];
 #pragma unroll
@@ -701,7 +862,7 @@ __device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[
     for (int kk = 0; kk < KK; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
     if (jn + 1 < CF::NJ) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+      for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, jn + 1, kk);
     }
     v4f x[CF::NI];
 #pragma unroll
@@ -742,15 +903,18 @@ __device__ inline void compute_f32s32(const unsigned char* st, v4f (&acc)[CF::NI
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = 8 * q + (j >> 1);
-  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
-  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const int lbyte = 8 * q;  // K-major: first token byte
+  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + lbyte
+                                      : st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + lbyte
+                                      : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const float* sSa = (const float*)(st + CF::SA_OFF);
   const float* sSb = (const float*)(st + CF::SB_OFF);
   v2i ar[CF::NI][KK];
 #pragma unroll
   for (int i = 0; i < CF::NI; ++i)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) ar[i][kk] = tr8(aBase + 32 * kk * CF::ROWA + 16 * i);
+    for (int kk = 0; kk < KK; ++kk) ar[i][kk] = rd8<CF, CF::ROWA>(aBase, i, kk);
   auto rescale = [&](int pi, int pj, int pk, const v4f& x) {
     const v4f sa = *(const v4f*)(sSa + pk * CF::BM + wm * CF::WM + 16 * pi + 4 * q);
     const float sb = sSb[pk * CF::BN + wn * CF::WN + 16 * pj + j];
@@ -759,7 +923,7 @@ __device__ inline void compute_f32s32(const unsigned char* st, v4f (&acc)[CF::NI
   };
   v2i rnext[KK], bcur[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, 0, kk);
   v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
   constexpr int S = CF::NI * CF::NJ;
 #pragma unroll
@@ -770,7 +934,7 @@ __device__ inline void compute_f32s32(const unsigned char* st, v4f (&acc)[CF::NI
       for (int kk = 0; kk < KK; ++kk) bcur[kk] = rnext[kk];
       if (jn + 1 < CF::NJ) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+        for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, jn + 1, kk);
       }
     }
 #pragma unroll
@@ -802,8 +966,11 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = 8 * q + (j >> 1);
-  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
-  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
+  const int lbyte = 8 * q;  // K-major: first token byte
+  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + lbyte
+                                      : st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
+  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + lbyte
+                                      : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const unsigned char* sSa = st + CF::SA_OFF;
   const unsigned char* sSb = st + CF::SB_OFF;
   // 32-token run kk of the stage uses scale row kk (gran 32) or row 0 (gran 128)
@@ -815,11 +982,11 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const float s = e8m0_scale(sSa[g32 * kk * CF::BM + wm * CF::WM + 16 * i + j]);
-      af[i][kk] = widen8(tr8(aBase + 32 * kk * CF::ROWA + 16 * i), s);
+      af[i][kk] = widen8(rd8<CF, CF::ROWA>(aBase, i, kk), s);
     }
   v2i rnext[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB);
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, 0, kk);
 #pragma unroll
   for (int jn = 0; jn < CF::NJ; ++jn) {
     v8bf bf[KK];
@@ -830,7 +997,7 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
     }
     if (jn + 1 < CF::NJ) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) rnext[kk] = tr8(bBase + 32 * kk * CF::ROWB + 16 * (jn + 1));
+      for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, jn + 1, kk);
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -848,21 +1015,24 @@ __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = 4 * q + (j >> 2);
-  const unsigned char* aBase = st + lrow * CF::ROWA + 8 * (j & 3) + 2 * (wm * CF::WM);
-  const unsigned char* bBase = st + CF::OPA + lrow * CF::ROWB + 8 * (j & 3) + 2 * (wn * CF::WN);
+  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + 8 * q
+                                      : st + lrow * CF::ROWA + 8 * (j & 3) + 2 * (wm * CF::WM);
+  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + 8 * q
+                                      : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 3) +
+                                            2 * (wn * CF::WN);
 #pragma unroll
   for (int kk = 0; kk < CF::TK / 32; ++kk) {
     v8bf af[CF::NI];
 #pragma unroll
     for (int i = 0; i < CF::NI; ++i) {
-      const v4bf x0 = tr16(aBase + (32 * kk + 0) * CF::ROWA + 32 * i);
-      const v4bf x1 = tr16(aBase + (32 * kk + 16) * CF::ROWA + 32 * i);
+      const v4bf x0 = rd16<CF, CF::ROWA>(aBase, i, kk, 0);
+      const v4bf x1 = rd16<CF, CF::ROWA>(aBase, i, kk, 1);
       af[i] = v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
 #pragma unroll
     for (int jn = 0; jn < CF::NJ; ++jn) {
-      const v4bf y0 = tr16(bBase + (32 * kk + 0) * CF::ROWB + 32 * jn);
-      const v4bf y1 = tr16(bBase + (32 * kk + 16) * CF::ROWB + 32 * jn);
+      const v4bf y0 = rd16<CF, CF::ROWB>(bBase, jn, kk, 0);
+      const v4bf y1 = rd16<CF, CF::ROWB>(bBase, jn, kk, 1);
       const v8bf b = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
 #pragma unroll
       for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i], b, acc[i][jn]);
@@ -1010,6 +1180,13 @@ __device__ inline void item_gemm(const Params& p, const LoadOffsets<CF>& lo, uns
     const int ahead = min(CF::NS - 2, n - 1 - j);
     wait_stages<CF>(ahead);
     __syncthreads();
+    if constexpr (CF::NT) {
+      if (kb0 + j == nk - 1 && (Kg * CF::ELT) % 16 != 0) {
+        nt_tail_zero<CF>(p, smem + buf * CF::STAGE, Kg - CF::TK * (nk - 1),
+                         t_begin + (int64_t)CF::TK * (nk - 1), m0, n0);
+        __syncthreads();
+      }
+    }
     if (j + CF::NS - 1 < n) {
       const int nb = buf == 0 ? CF::NS - 1 : buf - 1;  // (j + NS - 1) % NS
       load_stage<KIND, CF>(p, lo, smem + nb * CF::STAGE, t_begin, Kg, boff_g, kb0 + j + CF::NS - 1,
@@ -1232,40 +1409,53 @@ static Launch launch_of() {
 }
 
 // bf16 output (whole tiles only: stream-K is not taken with a bf16 D)
+template <bool NT>
 static Launch pick_outb(int kind, bool fast, bool small) {
+  using S = Cfgs<NT>;
   if (kind == F32S32)
-    return fast ? launch_of<F32S32, true, CfgF8h32, false, true>()
-                : launch_of<F32S32, false, CfgF8h32, false, true>();
+    return fast ? launch_of<F32S32, true, typename S::F8h32, false, true>()
+                : launch_of<F32S32, false, typename S::F8h32, false, true>();
   if (kind == BF16)
-    return small ? launch_of<BF16, false, CfgB16s, false, true>()
-                 : launch_of<BF16, false, CfgB16, false, true>();
+    return small ? launch_of<BF16, false, typename S::B16s, false, true>()
+                 : launch_of<BF16, false, typename S::B16, false, true>();
   if (kind == F32S)
-    return fast ? launch_of<F32S, true, CfgF8, false, true>()
-                : launch_of<F32S, false, CfgF8h, false, true>();
-  return fast ? launch_of<E8M0, true, CfgF8, false, true>()
-              : launch_of<E8M0, false, CfgF8h, false, true>();
+    return fast ? launch_of<F32S, true, typename S::F8, false, true>()
+                : launch_of<F32S, false, typename S::F8h, false, true>();
+  return fast ? launch_of<E8M0, true, typename S::F8, false, true>()
+              : launch_of<E8M0, false, typename S::F8h, false, true>();
+}
+
+template <bool NT>
+static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb) {
+  using S = Cfgs<NT>;
+  if (outb) return pick_outb<NT>(kind, fast, small);
+  if (kind == F32S32)
+    return fast ? (split ? launch_of<F32S32, true, typename S::F8h32, true>()
+                         : launch_of<F32S32, true, typename S::F8h32>())
+                : (split ? launch_of<F32S32, false, typename S::F8h32, true>()
+                         : launch_of<F32S32, false, typename S::F8h32>());
+  if (split) {
+    if (kind == BF16) return launch_of<BF16, false, typename S::B16, true>();
+    if (kind == F32S)
+      return fast ? launch_of<F32S, true, typename S::F8, true>()
+                  : launch_of<F32S, false, typename S::F8h, true>();
+    return fast ? launch_of<E8M0, true, typename S::F8, true>()
+                : launch_of<E8M0, false, typename S::F8h, true>();
+  }
+  if (kind == BF16)
+    return small ? launch_of<BF16, false, typename S::B16s>()
+                 : launch_of<BF16, false, typename S::B16>();
+  if (kind == F32S)
+    return fast ? launch_of<F32S, true, typename S::F8>() : launch_of<F32S, false, typename S::F8h>();
+  return fast ? launch_of<E8M0, true, typename S::F8>() : launch_of<E8M0, false, typename S::F8h>();
 }
 
 // small: half tiles (bf16) for problems with few full tiles; split: stream-K over the
-// full-size tiles; outb: bf16 D
+// full-size tiles; outb: bf16 D; nt: K-major operands
 static Launch pick(int kind, bool fast, bool small = false, bool split = false,
-                   bool outb = false) {
-  if (outb) return pick_outb(kind, fast, small);
-  if (kind == F32S32)
-    return fast ? (split ? launch_of<F32S32, true, CfgF8h32, true>()
-                         : launch_of<F32S32, true, CfgF8h32>())
-                : (split ? launch_of<F32S32, false, CfgF8h32, true>()
-                         : launch_of<F32S32, false, CfgF8h32>());
-  if (split) {
-    if (kind == BF16) return launch_of<BF16, false, CfgB16, true>();
-    if (kind == F32S)
-      return fast ? launch_of<F32S, true, CfgF8, true>() : launch_of<F32S, false, CfgF8h, true>();
-    return fast ? launch_of<E8M0, true, CfgF8, true>() : launch_of<E8M0, false, CfgF8h, true>();
-  }
-  if (kind == BF16)
-    return small ? launch_of<BF16, false, CfgB16s>() : launch_of<BF16, false, CfgB16>();
-  if (kind == F32S) return fast ? launch_of<F32S, true, CfgF8>() : launch_of<F32S, false, CfgF8h>();
-  return fast ? launch_of<E8M0, true, CfgF8>() : launch_of<E8M0, false, CfgF8h>();
+                   bool outb = false, bool nt = false) {
+  return nt ? pick_t<true>(kind, fast, small, split, outb)
+            : pick_t<false>(kind, fast, small, split, outb);
 }
 
 struct DeviceInfo {
@@ -1283,28 +1473,14 @@ static int device_setup(int dev) {
     int cus = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const Launch all[23] = {pick(F32S32, false), pick(F32S32, true),
-                            pick(F32S32, false, false, true), pick(F32S32, true, false, true),
-                            pick(F32S32, false, false, false, true),
-                            pick(F32S32, true, false, false, true),
-                            pick(BF16, false, false, false, true),
-                            pick(BF16, false, true, false, true),
-                            pick(F32S, false, false, false, true),
-                            pick(F32S, true, false, false, true),
-                            pick(E8M0, false, false, false, true),
-                            pick(E8M0, true, false, false, true),
-                            pick(BF16, false),
-                            pick(BF16, false, true),
-                            pick(F32S, false),
-                            pick(F32S, true),
-                            pick(E8M0, false),
-                            pick(E8M0, true),
-                            pick(BF16, false, false, true),
-                            pick(F32S, false, false, true),
-                            pick(F32S, true, false, true),
-                            pick(E8M0, false, false, true),
-                            pick(E8M0, true, false, true)};
-    for (const Launch& l : all) {
+    // every kernel the launches can pick: layouts x kinds x modes
+    const int kinds[4] = {F32S, E8M0, BF16, F32S32};
+    for (int v = 0; v < 2 * 4 * 2 * 2 * 2 * 2; ++v) {
+      const bool nt = v & 1, fast = (v >> 3) & 1, small = (v >> 4) & 1;
+      const bool split = (v >> 5) & 1, outb = (v >> 6) & 1;
+      const int kind = kinds[(v >> 1) & 3];
+      if ((fast && kind == BF16) || (split && outb)) continue;
+      const Launch l = pick(kind, fast, small, split, outb, nt);
       e = hipFuncSetAttribute(l.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                               l.stage_bytes + sched_bytes(kMaxGroups));
       if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
@@ -1360,10 +1536,12 @@ extern "C" int64_t kg_wgrad_workspace_flag_bytes(void) {
   return (int64_t)split_flag_bytes(cus);
 }
 
-extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb,
-                           const void* C, void* D, const int32_t* ks, int G, int M, int N,
-                           int64_t K_total, int gran_k, int dtype_flags, void* workspace,
-                           int64_t workspace_bytes, void* stream) {
+// nt: K-major operands A [M, lda] and B [N, ldb] (elements), else token-major
+// A [K_total, M] and B [K_total, N]
+static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const void* B,
+                     int64_t ldb, const void* sb, const void* C, void* D, const int32_t* ks, int G,
+                     int M, int N, int64_t K_total, int gran_k, int dtype_flags, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
   const int dtype = dtype_flags & 0xFF;
   const int flags = dtype_flags & ~0xFF;
   if (dtype != KG_E4M3_F32SCALE && dtype != KG_E4M3_UE8M0 && dtype != KG_BF16)
@@ -1373,6 +1551,7 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
   const bool out_bf16 = (flags & KG_FLAG_D_BF16) != 0;
   if (fast && dtype == KG_BF16) return KG_ERR_DTYPE;
   if (G < 0 || M < 0 || N < 0 || K_total < 0 || workspace_bytes < 0) return KG_ERR_SHAPE;
+  if (nt && (lda < K_total || ldb < K_total)) return KG_ERR_SHAPE;
   if (dtype != KG_BF16 && gran_k != 32 && gran_k != 128) return KG_ERR_GRAN;
   if (G > kMaxGroups) return KG_ERR_UNSUPPORTED;
   if (M > (1 << 24) || N > (1 << 24) || K_total > INT32_MAX) return KG_ERR_UNSUPPORTED;
@@ -1390,10 +1569,19 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
       misaligned(D) || ((uintptr_t)ks & 3) != 0 || ((uintptr_t)workspace & 255) != 0)
     return KG_ERR_ALIGN;
   const int elt = dtype == KG_BF16 ? 2 : 1;
+  if (nt) {
+    // whole 16-byte units per K-major row; offsets within 256 rows of one load stay
+    // below 2^32
+    if ((lda * elt) % 16 != 0 || (ldb * elt) % 16 != 0) return KG_ERR_ALIGN;
+    if (256 * lda * elt > (int64_t)0xFFFFFF00 || 256 * ldb * elt > (int64_t)0xFFFFFF00)
+      return KG_ERR_UNSUPPORTED;
+  }
+  const size_t abytes = nt ? (size_t)M * lda * elt : (size_t)K_total * M * elt;
+  const size_t bbytes = nt ? (size_t)N * ldb * elt : (size_t)K_total * N * elt;
   const size_t dbytes = (size_t)G * M * N * (out_bf16 ? 2 : 4);
   if (C != nullptr && C != D && overlap(C, dbytes, D, dbytes)) return KG_ERR_ALIAS;
-  if (overlap(A, (size_t)K_total * M * elt, D, dbytes) ||
-      overlap(B, (size_t)K_total * N * elt, D, dbytes) || overlap(ks, (size_t)G * 4, D, dbytes) ||
+  if (overlap(A, abytes, D, dbytes) ||
+      overlap(B, bbytes, D, dbytes) || overlap(ks, (size_t)G * 4, D, dbytes) ||
       overlap(workspace, (size_t)workspace_bytes, D, dbytes) ||
       (C != nullptr && overlap(workspace, (size_t)workspace_bytes, C, dbytes)))
     return KG_ERR_ALIAS;
@@ -1411,17 +1599,17 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
   auto tiles_of = [&](const Launch& l) {
     return (int64_t)G * ((M + l.bm - 1) / l.bm) * ((N + l.bn - 1) / l.bn);
   };
-  const int64_t big_tiles = tiles_of(pick(BF16, false));
+  const int64_t big_tiles = tiles_of(pick(BF16, false, false, false, false, nt));
   const bool small = kind == BF16 && big_tiles < 2 * (int64_t)cus;
   // Stream-K also when whole rounds of tiles would leave more than 30% of the
   // grid idle (e.g. 272 tiles on 256 CUs); the default bf16 problem's 192 half
   // tiles (75% of one round) stay whole: its partial-tile hand-off measured slower.
-  const int64_t T = tiles_of(pick(kind, fast, small));
+  const int64_t T = tiles_of(pick(kind, fast, small, false, false, nt));
   const int64_t rounds = (T + cus - 1) / cus;
   const bool split = workspace != nullptr && G <= kMaxSplitGroups && !out_bf16 &&
                      (size_t)workspace_bytes >= split_ws_bytes(cus) &&
                      (2 * T <= (int64_t)cus || 10 * T < 7 * rounds * (int64_t)cus);
-  const Launch L = pick(kind, fast, small && !split, split, out_bf16);
+  const Launch L = pick(kind, fast, small && !split, split, out_bf16, nt);
   const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
   const int64_t total = (int64_t)G * tiles_m * tiles_n;
   if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;
@@ -1438,6 +1626,8 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
   p.M = M;
   p.N = N;
   p.K_total = K_total;
+  p.lda_b = nt ? (uint32_t)(lda * elt) : 0;
+  p.ldb_b = nt ? (uint32_t)(ldb * elt) : 0;
   p.gran = dtype == KG_BF16 ? 0 : gran_k;
   p.tiles_m = tiles_m;
   p.tiles_n = tiles_n;
@@ -1449,6 +1639,30 @@ extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const v
                                        L.stage_bytes + sched_bytes(G), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return KG_OK;
+}
+
+extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb,
+                           const void* C, void* D, const int32_t* ks, int G, int M, int N,
+                           int64_t K_total, int gran_k, int dtype_flags, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  return wgrad_run(false, A, 0, sa, B, 0, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags,
+                   workspace, workspace_bytes, stream);
+}
+
+extern "C" int kg_wgrad_nt_ws(const void* A, int64_t lda, const void* sa, const void* B,
+                              int64_t ldb, const void* sb, const void* C, void* D,
+                              const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
+                              int dtype_flags, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  return wgrad_run(true, A, lda, sa, B, ldb, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags,
+                   workspace, workspace_bytes, stream);
+}
+
+extern "C" int kg_wgrad_nt(const void* A, int64_t lda, const void* sa, const void* B, int64_t ldb,
+                           const void* sb, const void* C, void* D, const int32_t* ks, int G, int M,
+                           int N, int64_t K_total, int gran_k, int dtype_flags, void* stream) {
+  return wgrad_run(true, A, lda, sa, B, ldb, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags,
+                   nullptr, 0, stream);
 }
 
 extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb,

@@ -138,6 +138,37 @@ int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, co
                 int dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * kg_wgrad_nt, kg_wgrad_nt_ws -- kg_wgrad and kg_wgrad_ws with K-major (NT)
+ * operands: the token index is the contiguous one. The GitHub issue page
+ * (qijiaxing, 2025-04-03) writes dw = dy^t x as a GEMM of dy^t [h_out, tokens] and
+ * x^t [h_in, tokens]; the how-to page's SM90 entry point k_grouped_fp8_gemm_nt_contiguous
+ * takes this layout ("API Entry Points", FAQ on the NT and TN variants).
+ *
+ *   A    [M, lda]  element (t, m) of kg_wgrad's A at A[m * lda + t]; expert g's tokens
+ *                  are columns [off[g], off[g+1]) of every row; columns >= K_total
+ *                  are never read (padding)
+ *   lda  row stride of A in elements: >= K_total, lda * element size a multiple of
+ *        16 bytes, and 256 * lda * element size at most 2^32 - 256
+ *   B    [N, ldb]  the same for B
+ *   ldb  row stride of B in elements, as lda
+ *
+ * Everything else (scales sa [nblk, M] and sb [nblk, N], C, D, ks, gran_k, dtype and
+ * flags, workspace) is as for kg_wgrad / kg_wgrad_ws, and so is the result: with
+ * whole tiles (no stream-K), bit for bit what kg_wgrad returns on the token-major
+ * operands.
+ * Expert starts need no alignment. Extra errors, returned before anything is
+ * enqueued: KG_ERR_SHAPE if lda or ldb < K_total, KG_ERR_ALIGN if a row is not a
+ * whole number of 16-byte units, KG_ERR_UNSUPPORTED for a stride beyond the limit.
+ */
+int kg_wgrad_nt(const void* A, int64_t lda, const void* sa, const void* B, int64_t ldb,
+                const void* sb, const void* C, void* D, const int32_t* ks, int G, int M, int N,
+                int64_t K_total, int gran_k, int dtype, void* stream);
+int kg_wgrad_nt_ws(const void* A, int64_t lda, const void* sa, const void* B, int64_t ldb,
+                   const void* sb, const void* C, void* D, const int32_t* ks, int G, int M,
+                   int N, int64_t K_total, int gran_k, int dtype, void* workspace,
+                   int64_t workspace_bytes, void* stream);
+
+/*
  * kg_wgrad_workspace_bytes -- workspace size that kg_wgrad_ws needs on the current
  * device (one 256 KB partial tile per compute unit plus flags), or -1 if the HIP
  * runtime reports an error.

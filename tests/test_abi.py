@@ -105,6 +105,35 @@ def test_workspace_entry_point_errors(kw, code):
     assert call_ws(**kw) == code
 
 
+def call_nt(ws=None, ws_bytes=0, **kw):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    a = dict(A=FAKE, lda=112, sa=FAKE, Bp=FAKE, ldb=112, sb=FAKE, C=None, D=FAKE + (1 << 30),
+             ks=FAKE + (1 << 31), G=3, M=64, N=128, K=104, gran=128, dtype=kg.KG_E4M3_F32SCALE)
+    a.update(kw)
+    args = (v(a["A"]), a["lda"], v(a["sa"]), v(a["Bp"]), a["ldb"], v(a["sb"]), v(a["C"]),
+            v(a["D"]), v(a["ks"]), a["G"], a["M"], a["N"], a["K"], a["gran"], a["dtype"])
+    if ws is None:
+        return B.lib().kg_wgrad_nt(*args, None)
+    return B.lib().kg_wgrad_nt_ws(*args, v(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lda=100), B.KG_ERR_SHAPE),                         # row shorter than K_total
+    (dict(ldb=96), B.KG_ERR_SHAPE),
+    (dict(lda=104), B.KG_ERR_ALIGN),                         # 104 fp8 bytes: not whole 16 B
+    (dict(ldb=120), B.KG_ERR_ALIGN),
+    (dict(lda=(1 << 24) + 16), B.KG_ERR_UNSUPPORTED),        # 256 rows of offsets >= 2^32
+    (dict(ldb=(1 << 23) + 8, dtype=kg.KG_BF16, sa=None, sb=None), B.KG_ERR_UNSUPPORTED),
+    (dict(D=FAKE + 4096), B.KG_ERR_ALIAS),                   # D inside A's 64 rows of 112
+    (dict(gran=64), B.KG_ERR_GRAN),
+    (dict(A=FAKE + 8), B.KG_ERR_ALIGN),
+    (dict(dtype=kg.KG_BF16, sa=None, sb=None, lda=108), B.KG_ERR_ALIGN),  # 216 bytes
+    (dict(ws=FAKE + (1 << 32) + 16, ws_bytes=1 << 26), B.KG_ERR_ALIGN),
+])
+def test_nt_synchronous_errors(kw, code):
+    assert call_nt(**kw) == code
+
+
 def call_rq(X=FAKE, xs=None, ks=FAKE + (1 << 31), G=2, H=256, K=300, gran=128,
             src=B.KG_SRC_BF16, kind=kg.KG_E4M3_F32SCALE, Q=FAKE + (1 << 32), S=FAKE + (1 << 33)):
     v = lambda x: None if x is None else ctypes.c_void_p(x)

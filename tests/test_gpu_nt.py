@@ -1,0 +1,194 @@
+"""GPU parity of the K-major (NT) entry points (kg_wgrad_nt, kg_wgrad_nt_ws) against
+the CPU oracle (kgref.wgrad_nt), with the tolerances of the token-major path
+(precise: 1e-5 * sum|ab| + 1e-6 per element, Frobenius 1e-5; fp8-MFMA mode:
+2^-10 * sum|ab| + 1e-6, Frobenius 1e-4). The K-major operands sit in row buffers
+padded with NaN codes, so a read past an expert's tokens or into the padding shows.
+Both layouts hand every MFMA the same operands, so in whole-tile mode the K-major
+result also equals the token-major kernel's bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_grouped_gemm_tn_amd as kg
+from fp8_grouped_gemm_tn_amd import inputs
+from oracle import kgref
+from tests.test_gpu_parity import (FAST, FAST_FROB, FAST_RTOL, FROB, RTOL, ATOL, BF, F32, UE8,
+                                   check_bf16_out, check_close, dev, say, small_case, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [(F32, 128, 0), (F32, 128, FAST), (F32, 32, 0), (F32, 32, FAST), (UE8, 32, 0),
+         (UE8, 32, FAST), (UE8, 128, 0), (UE8, 128, FAST), (BF, 128, 0)]
+
+
+def nt_dev(case, t, extra=5):
+    """K-major copies of A and B on the device (NaN-padded rows)."""
+    return inputs.k_major(t["A"], extra), inputs.k_major(t["B"], extra + 11)
+
+
+def nt_oracle(case, At, Bt, C="default"):
+    h = case.host()
+    bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16) \
+        if x.dtype == torch.bfloat16 else x.cpu().numpy()
+    Ch = h["C"] if isinstance(C, str) else C
+    rc, D, bound = kgref.wgrad_nt(bits(At), h["sa"], bits(Bt), h["sb"], Ch, h["ks"], case.M,
+                                  case.N, case.gran_k, case.dtype)
+    assert rc == kgref.OK
+    return D, bound
+
+
+def run_nt(case, t, At, Bt, flags=0, out=torch.float32, C="default", workspace=None):
+    D = torch.full((case.G, case.M, case.N), float("nan"), dtype=out, device=dev())
+    Cp = t["C"] if isinstance(C, str) else C
+    if Cp is not None and out == torch.bfloat16:
+        Cp = Cp.to(torch.bfloat16)
+    kg.kg_wgrad_nt(At, t["sa"], Bt, t["sb"], Cp, D, t["ks"], case.gran_k, case.dtype | flags,
+                   workspace=workspace)
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    return D
+
+
+# unaligned expert starts (45, 176, 179, ...), an empty expert, 1- and 3-token experts,
+# tails of every length mod 16, M and N with partial tiles
+NT_KS = [45, 0, 131, 3, 300, 1, 17, 128, 143]
+
+
+@pytest.mark.parametrize("dtype,gran,flags", PATHS)
+def test_nt_ragged_matches_oracle_and_token_major(dtype, gran, flags):
+    say("nt ragged", dtype, gran, flags)
+    case = small_case(dtype, gran, NT_KS, 320, 272, with_c=True, seed=21)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    D = run_nt(case, t, At, Bt, flags)
+    D_ref, bound = nt_oracle(case, At, Bt)
+    check_close(D, D_ref, bound, f"nt {dtype} {gran} {flags}", fast=bool(flags))
+    g = NT_KS.index(0)
+    assert torch.equal(D[g].cpu().view(torch.int32), case.C[g].view(torch.int32))
+    # the token-major kernel on the same matrices: the same bits
+    D_tn = torch.full_like(D, float("nan"))
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], gran, dtype | flags)
+    torch.cuda.synchronize()
+    assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype,gran,flags", [(F32, 128, 0), (UE8, 32, FAST), (BF, 128, 0)])
+def test_nt_every_tail_length(dtype, gran, flags):
+    # one expert per tail length 1..16 (mod 16) after an unaligned start, no C
+    ks = [7] + [16 * (i % 3) + i for i in range(1, 17)]
+    say("nt tails", dtype, gran, flags, ks)
+    case = small_case(dtype, gran, ks, 64, 128, with_c=False, seed=23)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t, extra=0)
+    D = run_nt(case, t, At, Bt, flags, C=None)
+    D_ref, bound = nt_oracle(case, At, Bt, C=None)
+    check_close(D, D_ref, bound, "nt tails", fast=bool(flags))
+
+
+@pytest.mark.parametrize("dtype,gran,flags", PATHS)
+def test_nt_bf16_output(dtype, gran, flags):
+    say("nt bf16 out", dtype, gran, flags)
+    case = small_case(dtype, gran, NT_KS, 256, 144, with_c=True, seed=25)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    D = run_nt(case, t, At, Bt, flags, out=torch.bfloat16)
+    # the oracle's C is the bf16 C the kernel read
+    Cb = t["C"].to(torch.bfloat16).float().cpu().numpy()
+    D_ref, bound = nt_oracle(case, At, Bt, C=Cb)
+    check_bf16_out(D, D_ref, bound, "nt bf16 out", fast=bool(flags))
+
+
+SPLIT = [([300, 0, 517], 256, 256), ([4001, 1237], 512, 1024), ([0, 1, 33, 0], 256, 512)]
+
+
+@pytest.mark.parametrize("dtype,gran,flags", [(BF, 128, 0), (F32, 128, 0), (F32, 128, FAST),
+                                              (UE8, 32, 0), (F32, 32, 0)])
+@pytest.mark.parametrize("ks,M,N", SPLIT)
+def test_nt_stream_k(ks, M, N, dtype, gran, flags):
+    say("nt stream-K", dtype, gran, flags, ks, M, N)
+    case = small_case(dtype, gran, ks, M, N, with_c=True, seed=27)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    ws = kg.new_workspace()
+    D = run_nt(case, t, At, Bt, flags, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:kg.kg_wgrad_workspace_flag_bytes()].count_nonzero()) == 0
+    D_ref, bound = nt_oracle(case, At, Bt)
+    check_close(D, D_ref, bound, "nt stream-K", fast=bool(flags))
+    D2 = run_nt(case, t, At, Bt, flags, workspace=ws)
+    assert torch.equal(D.view(torch.int32), D2.view(torch.int32))
+
+
+def test_nt_worked_example_and_in_place():
+    # the how-to page's example shape, accumulated in place (C == D)
+    case = inputs.workload("worked")
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    D = run_nt(case, t, At, Bt, C=None)
+    D_ref, bound = nt_oracle(case, At, Bt, C=None)
+    check_close(D, D_ref, bound, "nt worked")
+    C0 = torch.randn_like(D)
+    Di = C0.clone()
+    kg.kg_wgrad_nt(At, t["sa"], Bt, t["sb"], Di, Di, t["ks"], 128, case.dtype)
+    torch.cuda.synchronize()
+    D_ref2, bound2 = nt_oracle(case, At, Bt, C=C0.cpu().numpy())
+    check_close(Di, D_ref2, bound2, "nt in place")
+
+
+def test_nt_ksum_mismatch_is_reported_and_writes_nothing():
+    case = small_case(F32, 128, [100, 60], 64, 128, with_c=False, seed=29)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    bad = torch.tensor([100, 61], dtype=torch.int32, device=dev())
+    D = torch.full((2, 64, 128), float("nan"), device=dev())
+    rc = kg.kg_wgrad_nt_raw(At, At.stride(0), t["sa"], Bt, Bt.stride(0), t["sb"], None, D, bad,
+                            2, 64, 128, case.K_total, 128, F32)
+    assert rc == kg.KG_OK
+    assert kg.kg_status() == kg.KG_ERR_KSUM
+    assert torch.isnan(D).all()
+
+
+@pytest.mark.parametrize("name", ["bf16", "zipf_fp8", "ue8m0_many"])
+def test_nt_full_size_sampled(name):
+    """Full-size workloads with K-major operands (the layout transposed on the GPU),
+    in the configuration bench.py --nt times, sampled against the oracle on the
+    token-major host copies (the K-major arrays are checked to be their transposes)."""
+    say("nt full size", name)
+    case = inputs.workload(name, device="cuda")
+    t = to_dev(case)
+    At, Bt = inputs.k_major(t["A"]), inputs.k_major(t["B"])
+    assert torch.equal(At, t["A"].t()) and torch.equal(Bt, t["B"].t())
+    ws = kg.new_workspace(dev())
+    rng = np.random.default_rng(3)
+    live = np.nonzero(case.ks > 0)[0]
+    n = 1200
+    sg = rng.choice(live, n)
+    sm = rng.integers(0, case.M, n)
+    sn = rng.integers(0, case.N, n)
+    sm[:4], sn[:4] = [0, case.M - 1, 255, 256], [0, case.N - 1, 256, 255]
+    h = case.host()
+    rc, ref, bound = kgref.wgrad_sampled(h["A"], h["sa"], h["B"], h["sb"], h["C"], h["ks"],
+                                         case.M, case.N, case.gran_k, case.dtype, sg, sm, sn)
+    assert rc == kgref.OK
+    idx = [torch.from_numpy(x).to(dev()) for x in (sg, sm, sn)]
+    for flags in ((0, FAST) if case.dtype != BF else (0,)):
+        say("nt full size", name, flags)
+        D = torch.empty((case.G, case.M, case.N), dtype=torch.float32, device=dev())
+        kg.kg_wgrad_nt(At, t["sa"], Bt, t["sb"], t["C"], D, t["ks"], case.gran_k,
+                       case.dtype | flags, workspace=ws)
+        assert kg.kg_status() == kg.KG_OK
+        torch.cuda.synchronize()
+        assert torch.isfinite(D).all()
+        got = D[idx[0], idx[1], idx[2]].double().cpu().numpy()
+        lim = (FAST_RTOL if flags else RTOL) * bound + ATOL
+        assert (np.abs(got - ref) <= lim).all()
+        assert np.linalg.norm(got - ref) <= (FAST_FROB if flags else FROB) * np.linalg.norm(ref)
+        for g in np.nonzero(case.ks == 0)[0]:
+            if case.C is not None:
+                assert torch.equal(D[g].view(torch.int32), t["C"][g].view(torch.int32))
+            else:
+                assert (D[g].view(torch.int32) == 0).all()
+        del D
+    del At, Bt, t, case, ws
+    torch.cuda.empty_cache()
