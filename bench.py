@@ -76,9 +76,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def counters_for(workload, fast, bf16_out=False, kernel="kg_wgrad"):
+def counters_for(workload, fast, bf16_out=False, kernel="kg_wgrad", nt=False):
     """HBM bytes per launch measured with rocprofv3 counters for this kernel source."""
-    name = f"{workload}{'_fast' if fast else ''}{'_bf16out' if bf16_out else ''}"
+    name = f"{workload}{'_nt' if nt else ''}{'_fast' if fast else ''}{'_bf16out' if bf16_out else ''}"
     path = os.path.join(ROOT, "profiles", f"{kernel}_{name}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -423,6 +423,8 @@ def main():
                     help="replace an fp8 workload's scale granularity (tokens per scale)")
     ap.add_argument("--bf16-out", action="store_true",
                     help="the bf16-output variant: C and D in bf16 (KG_FLAG_D_BF16)")
+    ap.add_argument("--nt", action="store_true",
+                    help="K-major (NT) operands: A [M, tokens] and B [N, tokens], kg_wgrad_nt")
     ap.add_argument("--no-workspace", action="store_true",
                     help="call kg_wgrad without a workspace (no stream-K split of small problems)")
     ap.add_argument("--seed", type=int, default=0)
@@ -478,10 +480,17 @@ def main():
     # the library's workspace (zeroed once, left zeroed by every call), allocated
     # before the timed region; it lets small bf16 problems spread over every CU
     ws = None if args.no_workspace else kg.new_workspace(dev)
+    if args.nt:
+        # K-major copies of the operands, made before the timed region
+        At, Bt = inputs.k_major(A), inputs.k_major(B)
+        assert torch.equal(At, A.t()) and torch.equal(Bt, B.t())
 
-    def step():
-        kg.kg_wgrad(A, sa, B, sb, C, D, ks, case.gran_k, dtype, K_total=case.K_total,
-                    workspace=ws)
+        def step():
+            kg.kg_wgrad_nt(At, sa, Bt, sb, C, D, ks, case.gran_k, dtype, workspace=ws)
+    else:
+        def step():
+            kg.kg_wgrad(A, sa, B, sb, C, D, ks, case.gran_k, dtype, K_total=case.K_total,
+                        workspace=ws)
 
     args.warmup = warm_up(step, args.warmup)
     assert kg.kg_status() == kg.KG_OK
@@ -518,7 +527,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = (counters_for(args.workload, bool(flags), args.bf16_out)
+    roof["traffic"] = (counters_for(args.workload, bool(flags), args.bf16_out, nt=args.nt)
                        if args.gran_k is None else None)
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
@@ -544,6 +553,7 @@ def main():
                    "G": case.G, "M": case.M, "N": case.N,
                    "tokens": case.K_total, "gran_k": case.gran_k if not is_bf16 else None,
                    "fp8_mfma": bool(flags), "workspace": ws is not None,
+                   "layout": "K-major (NT)" if args.nt else "token-major (TN)",
                    "d_dtype": "bf16" if args.bf16_out else "fp32"},
         "roofline": roof,
         "pct_fp8_peak": round(100.0 * value / PEAK["fp8"], 2),
