@@ -61,48 +61,35 @@ struct DCfg {
   static constexpr int STAGE = SA_OFF + BM * 4;
   static constexpr int LOADS_A = BM * CHA / 64, LOADS_B = TK * CHB / 64;
   static constexpr int LOADS = LOADS_A + LOADS_B + 1;  // + the token scales
-  static constexpr int SLOTS = (LOADS + WAVES - 1) / WAVES;
+  // the two 4-wave halves take turns issuing a whole stage (as the K-grouped fp8 kernels)
+  static constexpr int SLOTS4 = (LOADS + 3) / 4;
   using Epi = CfgF8h;
   static_assert(BM * CHA % 64 == 0 && TK * CHB % 64 == 0, "stage must be whole wave loads");
   static_assert(Epi::BM == BM && Epi::BN == BN && Epi::WAVES_M == WAVES_M &&
                     Epi::THREADS == THREADS && Epi::NI == NI && Epi::NJ == NJ,
                 "epilogue geometry");
   static_assert(Epi::EPI_BYTES <= NS * STAGE, "epilogue fits the stages");
-  static_assert(LOADS <= WAVES * SLOTS && SLOTS <= 31, "loads per wave");
+  static_assert(SLOTS4 <= 31, "loads per wave");
 };
 
-// This lane's byte offsets for its loads of a stage (slot s: load k = w + WAVES * s),
-// relative to the stage's first token row / channel row / scale; pad chunks load
-// zeros from an offset past any range.
-struct DLoad {
-  uint32_t off[DCfg::SLOTS];
-};
-
-__device__ inline DLoad dgrad_offsets(const DParams& p) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  DLoad o;
-#pragma unroll
-  for (int s = 0; s < DCfg::SLOTS; ++s) {
-    const int k = w + DCfg::WAVES * s;
-    o.off[s] = kOobOffset;
-    if (k < DCfg::LOADS_A) {
-      const int idx = 64 * k + lane, row = idx / DCfg::CHA, ch = idx - row * DCfg::CHA;
-      if (ch < 8) o.off[s] = (uint32_t)(row * p.K + 16 * ch);
-    } else if (k < DCfg::LOADS_A + DCfg::LOADS_B) {
-      const int idx = 64 * (k - DCfg::LOADS_A) + lane, row = idx / DCfg::CHB,
-                ch = idx - row * DCfg::CHB;
-      if (ch < 8) o.off[s] = (uint32_t)(row * p.N + 16 * ch);
-    } else if (k == DCfg::LOADS_A + DCfg::LOADS_B) {
-      o.off[s] = 16 * lane;  // 256 token scales
-    }
+// This lane's byte offset for load k of a stage, relative to the stage's first token
+// row / weight row / scale; pad chunks load zeros from an offset past any range.
+__device__ inline uint32_t dgrad_off(const DParams& p, int k, int lane) {
+  if (k < DCfg::LOADS_A) {
+    const int idx = 64 * k + lane, row = idx / DCfg::CHA, ch = idx - row * DCfg::CHA;
+    return ch < 8 ? (uint32_t)(row * p.K + 16 * ch) : kOobOffset;
+  } else if (k < DCfg::LOADS_A + DCfg::LOADS_B) {
+    const int idx = 64 * (k - DCfg::LOADS_A) + lane, row = idx / DCfg::CHB,
+              ch = idx - row * DCfg::CHB;
+    return ch < 8 ? (uint32_t)(row * p.N + 16 * ch) : kOobOffset;
   }
-  return o;
+  return 16 * lane;  // 256 token scales
 }
 
 // Stage kb of a tile: token rows [row0, row0 + rows) of dy, channels [128 kb, 128 kb +
 // 128); weight rows 128 kb .. 128 kb + 127 of expert g, columns [n0, n0 + 128); the
 // tokens' scales of block kb. Rows past `rows` read as zero.
-__device__ inline void dgrad_load_stage(const DParams& p, const DLoad& lo, unsigned char* st,
+__device__ inline void dgrad_load_stage(const DParams& p, unsigned char* st,
                                         int64_t row0, int rows, int g, int kb, int n0) {
   const int w = uniform(threadIdx.x >> 6);
   const v4i ra = make_rsrc(p.A + row0 * p.K + (int64_t)kb * DCfg::TK,
@@ -111,15 +98,18 @@ __device__ inline void dgrad_load_stage(const DParams& p, const DLoad& lo, unsig
                            (uint32_t)((DCfg::TK - 1) * p.N + DCfg::BN));
   const v4i rs = make_rsrc(p.sa + (int64_t)kb * p.M_total + row0, (uint32_t)(rows * 4));
   const uint32_t sA = lds_addr(st), sB = sA + DCfg::OPA, sS = sA + DCfg::SA_OFF;
+  // the waves of half kb & 1 (one wave per SIMD) issue the whole stage
+  if ((w >> 2) != (kb & 1)) return;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int s = 0; s < DCfg::SLOTS; ++s) {
-    const int k = w + DCfg::WAVES * s;
+  for (int s = 0; s < DCfg::SLOTS4; ++s) {
+    const int k = (w & 3) + 4 * s;
     if (k < DCfg::LOADS_A + DCfg::LOADS_B) {
       const bool is_a = k < DCfg::LOADS_A;
       load16_lds(is_a ? ra : rb, is_a ? sA + 1024 * k : sB + 1024 * (k - DCfg::LOADS_A),
-                 lo.off[s]);
+                 dgrad_off(p, k, lane));
     } else if (k == DCfg::LOADS_A + DCfg::LOADS_B) {
-      load16_lds(rs, sS, lo.off[s]);
+      load16_lds(rs, sS, dgrad_off(p, k, lane));
     }
   }
 }
@@ -234,7 +224,6 @@ __global__ __launch_bounds__(DCfg::THREADS, 1) void kg_dgrad_kernel(DParams p) {
   const int grid = gridDim.x, b = blockIdx.x;
   // as in the K-grouped kernel: XCD-contiguous runs when the items take several rounds
   const int slot = (grid % 8 == 0 && total > grid) ? (b % 8) * (grid / 8) + b / 8 : b;
-  const DLoad lo = dgrad_offsets(p);
   const int nk = p.K / DCfg::TK, nbn = p.N / DCfg::BN;
   for (int base = 0; base < total; base += grid) {
     const int idx = base + slot;
@@ -258,14 +247,14 @@ __global__ __launch_bounds__(DCfg::THREADS, 1) void kg_dgrad_kernel(DParams p) {
 #pragma unroll
       for (int jn = 0; jn < DCfg::NJ; ++jn) acc[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the previous item's stores
-    if (nk > 0) dgrad_load_stage(p, lo, smem, row0, rows, g, 0, n0);
+    if (nk > 0) dgrad_load_stage(p, smem, row0, rows, g, 0, n0);
     for (int kb = 0; kb < nk; ++kb) {
       // stage kb is in buffer kb % 2; stage kb + 1 loads into the other one while
       // stage kb computes
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
       if (kb + 1 < nk)
-        dgrad_load_stage(p, lo, smem + ((kb + 1) & 1) * DCfg::STAGE, row0, rows, g, kb + 1, n0);
+        dgrad_load_stage(p, smem + ((kb + 1) & 1) * DCfg::STAGE, row0, rows, g, kb + 1, n0);
       const float swv = swg[(int64_t)kb * nbn];
       dgrad_compute<FAST>(smem + (kb & 1) * DCfg::STAGE, swv, acc);
     }
