@@ -63,8 +63,9 @@ __device__ inline T wave_incl_scan(T v) {
 
 // Block-wide: load ks, check counts, scan offsets, order experts. Returns KG_OK
 // or KG_ERR_KSUM; every thread returns the same value. THREADS is the block size
-// (256 or 512); each thread owns kMaxGroups / THREADS consecutive experts.
-template <int THREADS>
+// (256 or 512); each thread owns kMaxGroups / THREADS consecutive experts. SPREAD:
+// place the empty experts between the others (else last).
+template <int THREADS, bool SPREAD = true>
 __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, Sched s,
                            int64_t* wsum_k, int32_t* wsum_b) {
   constexpr int E = kMaxGroups / THREADS, W = THREADS / 64;
@@ -116,16 +117,38 @@ __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, 
   for (int i = 0; i < W; ++i) total += wsum_k[i];
   __syncthreads();
   if (any_neg || total != K_total) return KG_ERR_KSUM;
-  // Longest-first order of experts (ties by index) when G is small; identity otherwise.
+  // When G is small: experts with tokens longest first (ties by index), and the empty
+  // ones (fill items: stores only) after them or, with SPREAD, spread evenly between
+  // them, so that their stores run beside other workgroups' GEMM tiles rather than
+  // all at the end (measured 3% on 256 experts with 51 empty, precise mode). Live
+  // expert of rank r sits at (r + 1/2) / L of the way, empty expert e (by index) at
+  // (e + 1/2) / E, live first on ties. Identity order otherwise.
   if (G <= 256) {
+    int L = 0;
+    for (int h = 0; h < G; ++h) L += s.ks[h] > 0;
+    const int Ez = G - L;
+    // without SPREAD every empty expert goes after every live one
+    const int Ls = SPREAD ? L : 0;
     for (int g = t; g < G; g += THREADS) {
       const int kt = s.ks[g];
-      int rank = 0;
-      for (int h = 0; h < G; ++h) {
-        const int kh = s.ks[h];
-        rank += (kh > kt) | ((kh == kt) & (h < g));
+      int pos = 0;
+      if (kt > 0) {
+        int r = 0;
+        for (int h = 0; h < G; ++h) {
+          const int kh = s.ks[h];
+          r += (kh > kt) | ((kh == kt) & (h < g));
+        }
+        int before = 0;  // empty experts placed before live rank r
+        for (int e = 0; e < Ez && SPREAD; ++e) before += (2 * e + 1) * L < (2 * r + 1) * Ez;
+        pos = r + before;
+      } else {
+        int e = 0;
+        for (int h = 0; h < g; ++h) e += s.ks[h] == 0;
+        int before = SPREAD ? 0 : L;  // live experts placed before empty rank e
+        for (int r = 0; r < Ls; ++r) before += (2 * r + 1) * Ez <= (2 * e + 1) * L;
+        pos = e + before;
       }
-      s.order[rank] = (uint16_t)g;
+      s.order[pos] = (uint16_t)g;
     }
   } else {
     for (int g = t; g < G; g += THREADS) s.order[g] = (uint16_t)g;

@@ -1265,7 +1265,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   __shared__ int32_t wsum_b[kMaxWaves];
   Sched s = sched_carve(smem + CF::NS * CF::STAGE, p.G);
   const int gran = KIND == BF16 ? CF::TK : p.gran;
-  if (sched_build<CF::THREADS>(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
+  // stream-K walks the live experts' stages first and the fill tiles last
+  if (sched_build<CF::THREADS, !SPLIT>(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
     if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
     return;
   }
