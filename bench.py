@@ -153,6 +153,46 @@ def copy_calibration(args, dev):
     del src, dst
 
 
+# Every LAUNCH_SAMPLE-th timed step is bracketed by its own pair of events (the
+# roofline's per-launch duration); the others run back to back. An event record
+# between two launches costs the GPU several microseconds (measured ~7 us per step
+# on the default problem), so only a sample of the launches carries them.
+LAUNCH_SAMPLE = 8
+
+
+def timed_steps(step, steps, stream):
+    """Time exactly `steps` calls of `step` on `stream`, synchronised before and after.
+    Returns (ms_per_step, avg_launch_ms, wall_s, sampled): ms_per_step from events at
+    the region's two ends, avg_launch_ms the mean of the sampled launches' own events."""
+    import torch
+    def sampled(k):
+        return k % LAUNCH_SAMPLE == LAUNCH_SAMPLE // 2 or (steps <= LAUNCH_SAMPLE // 2 and
+                                                          k == steps - 1)
+    n = sum(sampled(k) for k in range(steps))
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    i = 0
+    for k in range(steps):
+        if sampled(k):
+            pairs[i][0].record(stream)
+            step()
+            pairs[i][1].record(stream)
+            i += 1
+        else:
+            step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    avg_launch_ms = sum(a.elapsed_time(b) for a, b in pairs) / n
+    return ms_per_step, avg_launch_ms, wall, n
+
+
 def warm_up(step, warmup, seconds=1.0):
     """Run `warmup` untimed steps; with None, as many as fit in `seconds` (at least
     10). Returns the number run."""
@@ -187,11 +227,13 @@ def cpu_baseline(case, budget_s=12.0):
         assert rc == kgref.OK
         return time.perf_counter() - t0
 
+    # grow the sample towards budget_s of oracle time (the whole workload when that
+    # takes less)
     rows = 8
     t = run(rows)
     if t < budget_s / 4:
-        rows = int(min(M, max(rows, rows * budget_s / max(t, 1e-3) / 2)))
-        rows = max(8, rows - rows % 8)
+        rows = int(min(M, max(rows, rows * budget_s / max(t, 1e-3))))
+        rows = M if rows >= M else max(8, rows - rows % 8)
         t = run(rows)
     flops = 2.0 * tokens * rows * N
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": kgref.last_threads(),
@@ -251,17 +293,8 @@ def requant_main(args):
     args.warmup = warm_up(step, args.warmup)
     assert kg.kg_status() == kg.KG_OK
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s_, e_ in ev:
-        s_.record(stream)
-        step()
-        e_.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step, avg_ms, _, nsampled = timed_steps(step, args.steps, stream)
     assert kg.kg_status() == kg.KG_OK
-    avg_ms = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev)
-    ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
     nbytes = (K * H * (2 if src == kg.KG_SRC_BF16 else 1) + (0 if xs is None else xs.numel() * 4)
               + K * H + nblk * H * (4 if kind == kg.KG_E4M3_F32SCALE else 1))
     achieved = nbytes / (avg_ms / 1e3) / 1e9
@@ -283,7 +316,8 @@ def requant_main(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
                      "traffic": counters_for(args.requant, False, False, "kg_requant"),
-                     "algorithmic_bytes": nbytes},
+                     "algorithmic_bytes": nbytes, "launch_ms": round(avg_ms, 5),
+                     "launches_timed": nsampled},
     }
     if not args.no_cpu:
         from oracle import kgref
@@ -332,19 +366,8 @@ def dgrad_main(args):
     args.warmup = warm_up(step, args.warmup)
     assert kg.kg_status() == kg.KG_OK
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s_, e_ in ev:
-        s_.record(stream)
-        step()
-        e_.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_per_step, avg_ms, wall, nsampled = timed_steps(step, args.steps, stream)
     assert kg.kg_status() == kg.KG_OK
-    avg_ms = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev)
-    ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
     flops = c.flops
     nbytes = c.algorithmic_bytes(4 if args.fp32_out else 2)
     mfma_peak = PEAK["fp8"]
@@ -361,6 +384,8 @@ def dgrad_main(args):
                                    "kg_dgrad")
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
+    roof["launch_ms"] = round(avg_ms, 5)
+    roof["launches_timed"] = nsampled
     line = {
         "metric": "M-grouped dgrad TFLOP/s (2*M_total*N*K) + % of FP8 MFMA / HBM roofline, 1 GPU",
         "value": round(flops / (ms_per_step / 1e3) / 1e12, 3),
@@ -497,21 +522,8 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
-        step()
-        e.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_per_step, avg_launch_ms, wall, nsampled = timed_steps(step, args.steps, stream)
     assert kg.kg_status() == kg.KG_OK
-    launch_ms = [s.elapsed_time(e) for s, e in ev]
-    total_ms = ev[0][0].elapsed_time(ev[-1][1])
-    ms_per_step = total_ms / args.steps
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
 
     flops = case.flops
     nbytes = case.algorithmic_bytes(2 if args.bf16_out else 4)
@@ -532,6 +544,8 @@ def main():
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     roof["roofline_ms"] = round(max(t_mfma, t_hbm) * 1e3, 4)
+    roof["launch_ms"] = round(avg_launch_ms, 5)
+    roof["launches_timed"] = nsampled
 
     value = flops / (ms_per_step / 1e3) / 1e12
     dname = "bf16" if is_bf16 else ("fp8 e4m3 (fp8 MFMA)" if flags else "fp8 e4m3 (bf16 MFMA)")
