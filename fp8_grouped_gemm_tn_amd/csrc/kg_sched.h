@@ -63,11 +63,11 @@ __device__ inline T wave_incl_scan(T v) {
 
 // Block-wide: load ks, check counts, scan offsets, order experts. Returns KG_OK
 // or KG_ERR_KSUM; every thread returns the same value. THREADS is the block size
-// (256 or 512); each thread owns kMaxGroups / THREADS consecutive experts. SPREAD:
+// (256 or 512); each thread owns kMaxGroups / THREADS consecutive experts. spread:
 // place the empty experts between the others (else last).
-template <int THREADS, bool SPREAD = true>
+template <int THREADS>
 __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, Sched s,
-                           int64_t* wsum_k, int32_t* wsum_b) {
+                           int64_t* wsum_k, int32_t* wsum_b, bool spread = false) {
   constexpr int E = kMaxGroups / THREADS, W = THREADS / 64;
   static_assert(E * THREADS == kMaxGroups && W <= kMaxWaves, "block size");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -118,7 +118,7 @@ __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, 
   __syncthreads();
   if (any_neg || total != K_total) return KG_ERR_KSUM;
   // When G is small: experts with tokens longest first (ties by index), and the empty
-  // ones (fill items: stores only) after them or, with SPREAD, spread evenly between
+  // ones (fill items: stores only) after them or, with spread, spread evenly between
   // them, so that their stores run beside other workgroups' GEMM tiles rather than
   // all at the end (measured 3% on 256 experts with 51 empty, precise mode). Live
   // expert of rank r sits at (r + 1/2) / L of the way, empty expert e (by index) at
@@ -127,8 +127,8 @@ __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, 
     int L = 0;
     for (int h = 0; h < G; ++h) L += s.ks[h] > 0;
     const int Ez = G - L;
-    // without SPREAD every empty expert goes after every live one
-    const int Ls = SPREAD ? L : 0;
+    // without spread every empty expert goes after every live one
+    const int Ls = spread ? L : 0;
     for (int g = t; g < G; g += THREADS) {
       const int kt = s.ks[g];
       int pos = 0;
@@ -139,12 +139,12 @@ __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, 
           r += (kh > kt) | ((kh == kt) & (h < g));
         }
         int before = 0;  // empty experts placed before live rank r
-        for (int e = 0; e < Ez && SPREAD; ++e) before += (2 * e + 1) * L < (2 * r + 1) * Ez;
+        for (int e = 0; e < Ez && spread; ++e) before += (2 * e + 1) * L < (2 * r + 1) * Ez;
         pos = r + before;
       } else {
         int e = 0;
         for (int h = 0; h < g; ++h) e += s.ks[h] == 0;
-        int before = SPREAD ? 0 : L;  // live experts placed before empty rank e
+        int before = spread ? 0 : L;  // live experts placed before empty rank e
         for (int r = 0; r < Ls; ++r) before += (2 * r + 1) * Ez <= (2 * e + 1) * L;
         pos = e + before;
       }

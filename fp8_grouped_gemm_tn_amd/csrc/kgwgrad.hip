@@ -1265,20 +1265,38 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   __shared__ int32_t wsum_b[kMaxWaves];
   Sched s = sched_carve(smem + CF::NS * CF::STAGE, p.G);
   const int gran = KIND == BF16 ? CF::TK : p.gran;
-  // stream-K walks the live experts' stages first and the fill tiles last
-  if (sched_build<CF::THREADS, !SPLIT>(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
+  const int T = p.tiles_m * p.tiles_n;
+  const int grid = gridDim.x;
+  const bool one_round = (int64_t)p.G * T <= grid;
+  // Multi-round whole-tile launches spread the empty experts' fill tiles between the
+  // GEMM tiles; stream-K, and a launch whose items all run at once, take the live
+  // experts first and the fill tiles last.
+  if (sched_build<CF::THREADS>(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b,
+                               !SPLIT && !one_round) != KG_OK) {
     if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
     return;
   }
-  const int T = p.tiles_m * p.tiles_n;
-  const int grid = gridDim.x;
   // Workgroup b runs on XCD b % 8. With several rounds of items, each XCD takes a
   // contiguous run of every round (neighbouring tiles that share operand rows in
-  // its L2). A single round is dealt round-robin instead: all eight L2s then serve
-  // GEMM tiles (measured faster on MI355X when the round also holds fill items).
+  // its L2). When all items fit in one round, XCD x takes the x-th eighth of the GEMM
+  // tiles (a contiguous run: mostly one expert, sharing operand rows in its L2) and
+  // the x-th eighth of the fill tiles, so that every L2 serves GEMM tiles; if an XCD's
+  // share would not fit its workgroups, items are dealt round-robin.
   const int b = blockIdx.x;
-  const bool one_round = (int64_t)p.G * p.tiles_m * p.tiles_n <= grid;
-  const int slot = (grid % 8 == 0 && !one_round) ? (b % 8) * (grid / 8) + b / 8 : b;
+  int slot = b;
+  if (grid % 8 == 0 && !one_round) {
+    slot = (b % 8) * (grid / 8) + b / 8;
+  } else if (grid % 8 == 0 && !SPLIT && p.G <= 256) {  // live experts first (see above)
+    int live = 0;
+    for (int g = 0; g < p.G; ++g) live += s.ks[g] > 0;
+    const int gm = live * T, nf = p.G * T - gm, per = grid / 8;
+    if ((gm + 7) / 8 + (nf + 7) / 8 <= per) {
+      const int x = b % 8, r = b / 8;
+      const int g_lo = x * gm / 8, g_n = (x + 1) * gm / 8 - g_lo;
+      const int f_lo = x * nf / 8, f_n = (x + 1) * nf / 8 - f_lo;
+      slot = r < g_n ? g_lo + r : r - g_n < f_n ? gm + f_lo + (r - g_n) : p.G * T;
+    }
+  }
   const LoadOffsets<CF> lo = load_offsets<CF>(p);
 
   if constexpr (SPLIT) {
