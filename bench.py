@@ -68,11 +68,17 @@ for _m, _n, _k in ((4096, 2112, 7168), (4096, 24576, 1536), (4096, 32768, 512),
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and whitespace removed (a comment
+    edit does not change the kernels, so it does not invalidate stored counters)."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_grouped_gemm_tn_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,9 +15,10 @@
 //    first. The hardware places workgroup b on XCD b % 8. When the items take
 //    several rounds of the grid, each XCD's workgroups take a contiguous run of
 //    neighbouring tiles of one expert and share their operand rows in that XCD's
-//    L2; a single round is dealt round-robin, so that GEMM and fill items spread
-//    over all eight L2s.
-//  * Empty experts become copy/fill items (D = C, or 0).
+//    L2; in a single round each XCD takes an eighth of the GEMM items and an eighth
+//    of the fill items, so that every L2 serves GEMM tiles.
+//  * Empty experts become copy/fill items (D = C, or 0), placed between the live
+//    experts' items in multi-round launches so their stores overlap GEMM tiles.
 //  * Operands move global -> LDS with buffer loads that write LDS directly; token
 //    rows past the expert's end are outside the buffer's range and read as zero,
 //    which masks ragged tails in both operands.
