@@ -192,3 +192,36 @@ def test_nt_full_size_sampled(name):
         del D
     del At, Bt, t, case, ws
     torch.cuda.empty_cache()
+
+
+def test_nt_edge_cases():
+    # every expert empty (K_total = 0, rows of length 0): D = C bit for bit
+    say("nt all empty")
+    case = small_case(F32, 128, [0, 0, 0], 64, 64, seed=31)
+    t = to_dev(case)
+    At = torch.zeros((64, 16), dtype=torch.uint8, device=dev())[:, :0]  # row stride 16
+    Bt = torch.zeros((64, 16), dtype=torch.uint8, device=dev())[:, :0]
+    D = torch.full((3, 64, 64), float("nan"), device=dev())
+    kg.kg_wgrad_nt(At, t["sa"], Bt, t["sb"], t["C"], D, t["ks"], 128, F32)
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    assert torch.equal(D.cpu().view(torch.int32), case.C.view(torch.int32))
+    # one expert of one token, the smallest tile (bf16: the 8-element row unit)
+    say("nt single token 16x16")
+    case = small_case(BF, 128, [1], 16, 16, seed=32)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t, extra=0)
+    D = run_nt(case, t, At, Bt)
+    D_ref, bound = nt_oracle(case, At, Bt)
+    check_close(D, D_ref, bound, "nt 16x16")
+    # 1024 experts, UE8M0 per 32 tokens, many tiny and empty experts
+    say("nt G = 1024")
+    rng = np.random.default_rng(33)
+    ks = rng.integers(0, 40, 1024).astype(np.int32)
+    ks[rng.choice(1024, 100, replace=False)] = 0
+    case = small_case(UE8, 32, ks, 16, 32, seed=33)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    D = run_nt(case, t, At, Bt, FAST)
+    D_ref, bound = nt_oracle(case, At, Bt)
+    check_close(D, D_ref, bound, "nt G=1024", fast=True)
