@@ -70,6 +70,7 @@ def check(D, ref, bound, fast=False, what=""):
     ([300, 0, 1, 517, 256], 384, 512),   # ragged experts, an empty one, several m-tiles
     ([40], 128, 128),                    # one partial tile, one stage
     ([0, 257, 0], 256, 1024),            # 257 rows: a full tile and a one-row tile
+    ([300, 0, 1, 517, 256], 768, 384),   # N a multiple of 256: the wide tile (fp8 MFMA)
 ])
 @pytest.mark.parametrize("flags", [0, FAST])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
