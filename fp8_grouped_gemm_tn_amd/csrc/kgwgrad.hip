@@ -600,9 +600,9 @@ __device__ inline void load_stage(const Params& p, const LoadOffsets<CF>& lo, un
   } else {
     // the resource starts at (row 0, column m0) and ends with the expert's last row
     // of this stage: rows past it, and columns past the row end of the last row,
-    // read as zero
-    ra = make_rsrc(p.A + t0 * eM + m0 * CF::ELT, (uint32_t)(rows * eM - m0 * CF::ELT));
-    rb = make_rsrc(p.B + t0 * eN + n0 * CF::ELT, (uint32_t)(rows * eN - n0 * CF::ELT));
+    // read as zero (rows * eM reaches 2^31 for M = 2^24: unsigned arithmetic)
+    ra = make_rsrc(p.A + t0 * eM + m0 * CF::ELT, (uint32_t)rows * (uint32_t)eM - (uint32_t)(m0 * CF::ELT));
+    rb = make_rsrc(p.B + t0 * eN + n0 * CF::ELT, (uint32_t)rows * (uint32_t)eN - (uint32_t)(n0 * CF::ELT));
   }
   const uint32_t sA = lds_addr(st), sB = sA + CF::OPA;
   auto issue = [&](int k, uint32_t off0) {

@@ -381,6 +381,31 @@ def sampled_check(case, t, D, n=1500, seed=0, fast=False):
             assert (D[g].view(torch.int32) == 0).all()
 
 
+# M or N at 2^24 (the largest accepted) and M x N at 2^29 (the largest expert output
+# whose byte offsets fit 32 bits): one stage's rows of a 2^24-wide operand span 2^31
+# bytes, and the epilogue's offsets in one expert's C reach 2^31.
+LIMIT_CASES = [(F32, 128, 1 << 24, 16), (UE8, 32, 1 << 24, 16), (BF, 128, 1 << 24, 16),
+               (F32, 128, 16, 1 << 24), (BF, 128, 16, 1 << 24),
+               (F32, 128, 1 << 14, 1 << 15), (BF, 128, 1 << 15, 1 << 14)]
+
+
+@pytest.mark.parametrize("dtype,gran,M,N", LIMIT_CASES)
+def test_size_limits_sampled(dtype, gran, M, N):
+    """Largest accepted shapes, ragged experts (37 and 91 tokens) around an empty one,
+    with C; sampled outputs (tile corners included) in both modes, empty expert bit-exact."""
+    say("size limit", dtype, gran, M, N)
+    case = inputs.make_case("limit", [37, 0, 91], M, N, dtype, gran, with_c=True, seed=21,
+                            device="cuda")
+    t = to_dev(case)
+    D = torch.empty((case.G, M, N), dtype=torch.float32, device=dev())
+    for flags in ((0, FAST) if dtype != BF else (0,)):
+        say("size limit run", dtype, gran, M, N, flags)
+        run_gpu(case, t, D=D, flags=flags)
+        sampled_check(case, t, D, n=600, seed=M ^ N, fast=bool(flags))
+    del D, t, case
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["bf16", "zipf_fp8", "ue8m0_many", "local_share"])
 def test_full_size_workloads_sampled(name):
     say("full size", name)
