@@ -234,6 +234,25 @@ def make_case(name, ks, M, N, dtype, gran_k=128, with_c=True, seed=0, device="cp
                 meta=dict(seed=seed, device=str(dev)))
 
 
+def make_ternary_bf16_case(name, ks, M, N, seed=0, device="cpu"):
+    """bf16 operands with values in {-1, 0, +1} and integer C in [-64, 64]: every
+    partial sum of up to 2^24 tokens is an integer that fp32 holds exactly, so a
+    result must equal the exact one bit for bit, however long the experts. Draw
+    order: A, B, C."""
+    ks = np.asarray(ks, dtype=np.int32)
+    G = ks.size
+    K_total = int(ks.astype(np.int64).sum())
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    A = torch.randint(-1, 2, (K_total, M), generator=gen, device=dev, dtype=torch.int8)
+    B = torch.randint(-1, 2, (K_total, N), generator=gen, device=dev, dtype=torch.int8)
+    C = torch.randint(-64, 65, (G, M, N), generator=gen, device=dev, dtype=torch.int32)
+    return Case(name=name, G=G, M=M, N=N, ks=ks, dtype=BF16, gran_k=128,
+                A=A.to(torch.bfloat16), B=B.to(torch.bfloat16), sa=None, sb=None,
+                C=C.to(torch.float32), meta=dict(seed=seed, device=str(dev), ternary=True))
+
+
 # (m, n, k) of the issue page's non-grouped 1D1D fp8 GEMM table
 SINGLE_SHAPES = ((4096, 2112, 7168), (4096, 24576, 1536), (4096, 32768, 512),
                  (4096, 7168, 16384), (4096, 4096, 7168), (4096, 7168, 2048))

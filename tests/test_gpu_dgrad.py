@@ -146,3 +146,42 @@ def test_dgrad_full_size_sampled(name):
         check(got, ref, bound, fast=bool(flags), what=name)
         del D
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- size limits
+
+def sampled(c, t, flags, out, n, seed):
+    h = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in
+         dict(A=c.A, sa=c.sa, W=c.W, sw=c.sw, ms=c.ms).items()}
+    rng = np.random.default_rng(seed)
+    st = rng.integers(0, c.M_total, n)
+    sn = rng.integers(0, c.N, n)
+    off = np.concatenate([[0], np.cumsum(c.ms)])
+    edges = [r for g in range(c.G) if c.ms[g] > 0 for r in (off[g], off[g + 1] - 1)]
+    st = np.concatenate([st, edges, edges])
+    sn = np.concatenate([sn, np.zeros(len(edges), np.int64), np.full(len(edges), c.N - 1)])
+    rc, ref, bound = kgref.dgrad_sampled(h["A"], h["sa"], h["W"], h["sw"], h["ms"], c.N, c.K,
+                                         st, sn)
+    assert rc == kgref.OK
+    D = run(c, t, flags, out=out)
+    got = D[torch.from_numpy(st).to(D.device), torch.from_numpy(sn).to(D.device)]
+    check(got, ref, bound, fast=bool(flags), what=f"limit N={c.N} K={c.K}")
+
+
+# N = 2097024 is the largest multiple of 128 whose 256-row output tile has byte
+# offsets below 2^31 (2096896, a multiple of 256, takes the fp8-MFMA mode's wide
+# tile); K = 8388480 the largest whose 256-row activation tile does.
+@pytest.mark.parametrize("ms,N,K,flags,out", [
+    ([37, 0, 91, 1], 2097024, 128, 0, torch.float32),
+    ([37, 0, 91, 1], 2097024, 128, FAST, torch.bfloat16),
+    ([37, 0, 91, 1], 2096896, 128, FAST, torch.float32),
+    ([37, 0, 91], 128, 8388480, 0, torch.bfloat16),
+    ([37, 0, 91], 256, 8388480, FAST, torch.float32),
+])
+def test_dgrad_size_limits_sampled(ms, N, K, flags, out):
+    say("dgrad limit", ms, N, K, flags, out)
+    c = inputs.make_dgrad_case("limit", ms, N, K, seed=25, device="cuda")
+    t = to_dev(c)
+    sampled(c, t, flags, out, n=60, seed=N ^ K)
+    del t, c
+    torch.cuda.empty_cache()

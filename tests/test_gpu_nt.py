@@ -225,3 +225,82 @@ def test_nt_edge_cases():
     D = run_nt(case, t, At, Bt, FAST)
     D_ref, bound = nt_oracle(case, At, Bt)
     check_close(D, D_ref, bound, "nt G=1024", fast=True)
+
+
+# ---------------------------------------------------------------- size limits
+
+@pytest.mark.parametrize("dtype,gran,flags", [(F32, 128, 0), (F32, 128, FAST), (BF, 128, 0)])
+def test_nt_limit_m_2p24_bit_identical(dtype, gran, flags):
+    """M = 2^24 (the largest accepted), ragged experts around an empty one, with C:
+    the K-major kernel equals the token-major one bit for bit (whole tiles), and
+    sampled outputs match the oracle."""
+    from tests.test_gpu_parity import sampled_check
+    M, N = 1 << 24, 16
+    say("nt limit M", dtype, gran, flags)
+    case = inputs.make_case("limit", [37, 0, 91], M, N, dtype, gran, with_c=True, seed=23,
+                            device="cuda")
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    D = run_nt(case, t, At, Bt, flags)
+    D_tn = torch.full_like(D, float("nan"))
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], gran, dtype | flags)
+    torch.cuda.synchronize()
+    assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
+    del D_tn, At, Bt
+    sampled_check(case, t, D, n=300, seed=1, fast=bool(flags))
+    del D, t, case
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,K", [(F32, 16_000_000), (BF, 8_000_000)])
+def test_nt_limit_row_length(dtype, K):
+    """K-major rows near the longest accepted (256 rows of one load span just under
+    2^32 bytes), three experts (one empty) over K tokens, M and N below one tile:
+    whole tiles equal the token-major kernel bit for bit; whole tiles and stream-K
+    (with the workspace) match the oracle on sampled outputs. The bf16 operands are
+    ternary with integer C, so that its experts of 2.7M and 5.3M tokens have exact
+    fp32 sums and the outputs must equal the oracle's exactly (with N(0, 1) data,
+    fp32 accumulation over 5.3M tokens is ~2e-5 off in relative Frobenius norm)."""
+    from tests.test_gpu_parity import sampled_check
+    ks = [K // 3 + 1, 0, K - K // 3 - 1]
+    say("nt limit rows", dtype, K)
+    if dtype == BF:
+        case = inputs.make_ternary_bf16_case("long", ks, 32, 48, seed=24, device="cuda")
+    else:
+        case = inputs.make_case("long", ks, 32, 48, dtype, 128, with_c=True, seed=24,
+                                device="cuda")
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    elt = 2 if dtype == BF else 1
+    assert 256 * At.stride(0) * elt <= 0xFFFFFF00 and 256 * Bt.stride(0) * elt <= 0xFFFFFF00
+    h = case.host()
+    rng = np.random.default_rng(4)
+    sg = np.array([0, 2] * 20, np.int64)
+    sm = np.concatenate([rng.integers(0, 32, 36), [0, 31, 0, 31]]).astype(np.int64)
+    sn = np.concatenate([rng.integers(0, 48, 36), [0, 47, 47, 0]]).astype(np.int64)
+    rc, ref, bound = kgref.wgrad_sampled(h["A"], h["sa"], h["B"], h["sb"], h["C"], h["ks"], 32,
+                                         48, 128, dtype, sg, sm, sn)
+    assert rc == kgref.OK
+
+    def check(D):
+        got = D[torch.from_numpy(sg).to(D.device), torch.from_numpy(sm).to(D.device),
+                torch.from_numpy(sn).to(D.device)].double().cpu().numpy()
+        if dtype == BF:
+            assert np.array_equal(got, ref), f"{(got != ref).sum()} sampled outputs not exact"
+        else:
+            assert (np.abs(got - ref) <= RTOL * bound + ATOL).all()
+            assert np.linalg.norm(got - ref) <= FROB * np.linalg.norm(ref)
+        assert torch.equal(D[1].view(torch.int32), t["C"][1].view(torch.int32))
+
+    D = run_nt(case, t, At, Bt)
+    D_tn = torch.full_like(D, float("nan"))
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], 128, dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
+    check(D)
+    ws = kg.new_workspace(dev())
+    say("nt limit rows stream-K", dtype, K)
+    D = run_nt(case, t, At, Bt, workspace=ws)
+    check(D)
+    del D, D_tn, At, Bt, ws, t, case
+    torch.cuda.empty_cache()
