@@ -79,6 +79,75 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _tensors_on_gpu(ref, **named):
+    """Every given tensor contiguous (or, for the names in `strided`, checked by the
+    caller) and on `ref`'s GPU. Checked after the shapes, so that shape errors
+    show on any device."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        _need(t.is_cuda, f"{name} must be a GPU tensor")
+        _need(t.device == ref.device, f"{name} is on {t.device}, D on {ref.device}")
+
+
+def _operand_dtype_ok(t, dtype):
+    import torch
+    if dtype == KG_BF16:
+        return t.dtype == torch.bfloat16
+    return t.element_size() == 1 and t.dtype != torch.bool
+
+
+def _scale_dtype_ok(t, dtype):
+    import torch
+    return t.dtype == (torch.float32 if dtype == KG_E4M3_F32SCALE else torch.uint8)
+
+
+def _check_wgrad(A_cols, B_cols, sa, sb, C, D, ks, K_total, gran_k, dtype, A, B, kmajor):
+    """Shapes and dtypes of a kg_wgrad / kg_wgrad_nt call (the C ABI takes plain
+    pointers and cannot see extents). The scale tensors need at least
+    ceil(K_total / gran_k) rows (their exact count, sum ceil(ks / gran_k), would
+    take ks off the GPU)."""
+    import torch
+    base = dtype & 0xFF
+    _need(base in (KG_E4M3_F32SCALE, KG_E4M3_UE8M0, KG_BF16), f"unknown dtype {base}")
+    _need(D.dim() == 3, "D must be [G, M, N]")
+    _need(D.dtype in (torch.float32, torch.bfloat16), "D must be float32 or bfloat16")
+    _need(D.is_contiguous(), "D must be contiguous")
+    G, M, N = D.shape
+    _need(ks.dim() == 1 and ks.numel() == G and ks.dtype == torch.int32 and ks.is_contiguous(),
+          "ks must be a contiguous int32 [G] tensor")
+    if C is not None:
+        _need(C.shape == D.shape and C.dtype == D.dtype and C.is_contiguous(),
+              "C must be a contiguous tensor of D's shape and dtype")
+    _need(A.dim() == 2 and B.dim() == 2, "A and B must be 2-D")
+    _need(A_cols == M and B_cols == N, "A and B must have M and N channels (D is [G, M, N])")
+    _need(_operand_dtype_ok(A, base) and _operand_dtype_ok(B, base),
+          "A and B must be bfloat16 for KG_BF16, 1-byte fp8 codes otherwise")
+    if kmajor:
+        _need(A.shape[1] >= K_total and B.shape[1] >= K_total, "At and Bt hold fewer tokens than K_total")
+    else:
+        _need(A.is_contiguous() and B.is_contiguous(), "A and B must be contiguous")
+        _need(A.shape[0] >= K_total and B.shape[0] >= K_total, "A and B hold fewer rows than K_total")
+    if base == KG_BF16:
+        _need(sa is None and sb is None, "bf16 operands take no scales")
+    elif K_total > 0:
+        _need(sa is not None and sb is not None, "fp8 operands need sa and sb")
+        nmin = -(-int(K_total) // int(gran_k)) if gran_k > 0 else 0
+        _need(sa.dim() == 2 and sa.shape[1] == M and sb.dim() == 2 and sb.shape[1] == N,
+              "sa must be [nblk, M] and sb [nblk, N]")
+        _need(sa.shape[0] >= nmin and sb.shape[0] >= nmin,
+              f"sa and sb need at least ceil(K_total / gran_k) = {nmin} rows")
+        _need(_scale_dtype_ok(sa, base) and _scale_dtype_ok(sb, base),
+              "scales must be float32 (fp32 scales) or uint8 (UE8M0)")
+        _need(sa.is_contiguous() and sb.is_contiguous(), "sa and sb must be contiguous")
+    _tensors_on_gpu(D, A=A, B=B, sa=sa, sb=sb, C=C, ks=ks)
+
+
 def kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream=None):
     """Call kg_wgrad with torch device tensors (or None); returns the status code."""
     return lib().kg_wgrad(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D), _ptr(ks),
@@ -120,13 +189,18 @@ def kg_wgrad(A, sa, B, sb, C, D, ks, gran_k, dtype, K_total=None, stream=None, w
     A bfloat16 D (and C) selects the bf16-output variant (KG_FLAG_D_BF16).
     `workspace` (from new_workspace) lets problems with few tiles use every CU."""
     import torch
+    if K_total is None:
+        K_total = A.shape[0]
+    if C is not None and C.dtype != D.dtype:
+        raise TypeError("C and D must have the same dtype")
+    _check_wgrad(A.shape[1] if A.dim() == 2 else -1, B.shape[1] if B.dim() == 2 else -1, sa, sb,
+                 C, D, ks, K_total, gran_k, dtype, A, B, kmajor=False)
+    if workspace is not None:
+        _need(workspace.is_contiguous(), "workspace must be contiguous")
+        _tensors_on_gpu(D, workspace=workspace)
     G, M, N = D.shape
     if D.dtype == torch.bfloat16:
         dtype |= KG_FLAG_D_BF16
-    if C is not None and C.dtype != D.dtype:
-        raise TypeError("C and D must have the same dtype")
-    if K_total is None:
-        K_total = A.shape[0]
     if workspace is None:
         rc = kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream)
     else:
@@ -154,15 +228,22 @@ def kg_wgrad_nt(At, sa, Bt, sb, C, D, ks, gran_k, dtype, stream=None, workspace=
     stride along tokens (row strides, e.g. of a padded buffer, are passed as lda and
     ldb). D [G, M, N]; a bfloat16 D selects the bf16-output variant."""
     import torch
-    G, M, N = D.shape
     if At.dim() != 2 or Bt.dim() != 2 or At.stride(1) != 1 or Bt.stride(1) != 1:
         raise ValueError("At and Bt must be 2-D with unit stride along tokens")
     if At.shape[1] != Bt.shape[1]:
         raise ValueError("At and Bt must have the same number of tokens")
-    if D.dtype == torch.bfloat16:
-        dtype |= KG_FLAG_D_BF16
+    _need(At.stride(0) >= At.shape[1] and Bt.stride(0) >= Bt.shape[1],
+          "At and Bt rows must not overlap (row stride >= tokens)")
     if C is not None and C.dtype != D.dtype:
         raise TypeError("C and D must have the same dtype")
+    _check_wgrad(At.shape[0], Bt.shape[0], sa, sb, C, D, ks, At.shape[1], gran_k, dtype, At, Bt,
+                 kmajor=True)
+    if workspace is not None:
+        _need(workspace.is_contiguous(), "workspace must be contiguous")
+        _tensors_on_gpu(D, workspace=workspace)
+    G, M, N = D.shape
+    if D.dtype == torch.bfloat16:
+        dtype |= KG_FLAG_D_BF16
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = kg_wgrad_nt_raw(At, At.stride(0), sa, Bt, Bt.stride(0), sb, C, D, ks, G, M, N,
                          At.shape[1], gran_k, dtype, workspace, ws_bytes, stream)
@@ -199,13 +280,29 @@ def kg_requant(X, xs, ks, gran_k, scale_kind, nblk, Q=None, S=None, stream=None)
     [K_total, H/128]; ks int32 [G] on the GPU; nblk = sum(ceil(ks / gran_k)) (the scale
     rows; the caller knows ks). Returns (Q uint8 [K_total, H], S [nblk, H])."""
     import torch
+    _need(X.dim() == 2 and X.is_contiguous(), "X must be a contiguous [K_total, H] tensor")
     K_total, H = X.shape
     src = KG_SRC_BF16 if X.dtype == torch.bfloat16 else KG_SRC_E4M3_1X128
+    _need(src == KG_SRC_BF16 or (X.element_size() == 1 and X.dtype != torch.bool),
+          "X must be bfloat16 or 1-byte e4m3 codes")
+    if src == KG_SRC_BF16:
+        _need(xs is None, "a bf16 source takes no xs")
+    else:
+        _need(xs is not None and xs.dtype == torch.float32 and xs.is_contiguous() and
+              tuple(xs.shape) == (K_total, -(-H // 128)),
+              "an fp8 source needs contiguous float32 xs [K_total, H / 128]")
+    _need(ks.dim() == 1 and ks.dtype == torch.int32 and ks.is_contiguous(),
+          "ks must be a contiguous int32 [G] tensor")
+    sdt = torch.float32 if scale_kind == KG_E4M3_F32SCALE else torch.uint8
     if Q is None:
         Q = torch.empty((K_total, H), dtype=torch.uint8, device=X.device)
     if S is None:
-        sdt = torch.float32 if scale_kind == KG_E4M3_F32SCALE else torch.uint8
         S = torch.empty((nblk, H), dtype=sdt, device=X.device)
+    _need(tuple(Q.shape) == (K_total, H) and Q.element_size() == 1 and Q.is_contiguous(),
+          "Q must be a contiguous 1-byte [K_total, H] tensor")
+    _need(tuple(S.shape) == (nblk, H) and S.dtype == sdt and S.is_contiguous(),
+          f"S must be a contiguous {sdt} [nblk, H] tensor")
+    _tensors_on_gpu(X, xs=xs, ks=ks, Q=Q, S=S)
     rc = kg_requant_raw(X, xs, ks, ks.numel(), H, K_total, gran_k, src, scale_kind, Q, S, stream)
     if rc != KG_OK:
         raise KgError(rc, "kg_requant")
@@ -223,7 +320,21 @@ def kg_dgrad(A, sa, W, sw, D, ms, flags=0, stream=None):
     W [G, K, N] fp8 bytes, sw [G, K/128, N/128] fp32, ms [G] int32, D [M_total, N]
     (float32, or bfloat16 for the bf16 output). All on the GPU."""
     import torch
+    _need(W.dim() == 3 and W.element_size() == 1 and W.is_contiguous(),
+          "W must be contiguous fp8 codes [G, K, N]")
     G, K, N = W.shape
+    _need(A.dim() == 2 and A.shape[1] == K and A.element_size() == 1 and A.is_contiguous(),
+          "A must be contiguous fp8 codes [M_total, K]")
+    M_total = A.shape[0]
+    _need(tuple(sa.shape) == (-(-K // 128), M_total) and sa.dtype == torch.float32 and
+          sa.is_contiguous(), "sa must be contiguous float32 [K / 128, M_total]")
+    _need(tuple(sw.shape) == (G, -(-K // 128), -(-N // 128)) and sw.dtype == torch.float32 and
+          sw.is_contiguous(), "sw must be contiguous float32 [G, K / 128, N / 128]")
+    _need(ms.dim() == 1 and ms.numel() == G and ms.dtype == torch.int32 and ms.is_contiguous(),
+          "ms must be a contiguous int32 [G] tensor")
+    _need(tuple(D.shape) == (M_total, N) and D.dtype in (torch.float32, torch.bfloat16) and
+          D.is_contiguous(), "D must be a contiguous float32 or bfloat16 [M_total, N] tensor")
+    _tensors_on_gpu(D, A=A, sa=sa, W=W, sw=sw, ms=ms)
     if D.dtype == torch.bfloat16:
         flags |= KG_FLAG_D_BF16
     rc = kg_dgrad_raw(A, sa, W, sw, D, ms, G, N, K, A.shape[0], flags, stream)

@@ -245,3 +245,99 @@ def test_dgrad_empty_problems_launch_nothing():
     assert dcall(G=0) == B.KG_OK
     assert dcall(N=0) == B.KG_OK
     assert dcall(M=0) == B.KG_OK
+
+
+# ---------------------------------------------------------------- binding checks
+# The C ABI takes plain pointers; the Python wrappers check tensor shapes, dtypes,
+# layout and device before calling it. CPU tensors: a well-formed call ends at the
+# device check.
+
+def _wgrad_args(**over):
+    import torch
+    M, N, K = 32, 48, 100
+    a = dict(A=torch.zeros((K, M), dtype=torch.uint8), sa=torch.zeros((2, M)),
+             B=torch.zeros((K, N), dtype=torch.uint8), sb=torch.zeros((2, N)), C=None,
+             D=torch.zeros((2, M, N)), ks=torch.tensor([60, 40], dtype=torch.int32),
+             gran_k=128, dtype=kg.KG_E4M3_F32SCALE)
+    a.update(over)
+    return a
+
+
+def _bad_wgrad_cases():
+    import torch
+    return [
+        (dict(A=torch.zeros((100, 16), dtype=torch.uint8)), "channels"),
+        (dict(ks=torch.tensor([100], dtype=torch.int32)), "ks must"),
+        (dict(ks=torch.tensor([60, 40], dtype=torch.int64)), "ks must"),
+        (dict(sa=torch.zeros((2, 16))), "sa must be"),
+        (dict(sa=torch.zeros((0, 32)), sb=torch.zeros((0, 48))), "rows"),
+        (dict(sa=torch.zeros((2, 32), dtype=torch.uint8)), "scales must"),
+        (dict(A=torch.zeros((100, 32), dtype=torch.bfloat16)), "1-byte"),
+        (dict(A=torch.zeros((50, 32), dtype=torch.uint8), K_total=100), "fewer rows"),
+        (dict(C=torch.zeros((2, 32, 16))), "C must"),
+        (dict(D=torch.zeros((2, 48, 32)).transpose(1, 2)), "contiguous"),
+        (dict(D=torch.zeros((2, 32, 48), dtype=torch.float64)), "float32 or bfloat16"),
+        (dict(dtype=kg.KG_BF16, A=torch.zeros((100, 32), dtype=torch.bfloat16),
+              B=torch.zeros((100, 48), dtype=torch.bfloat16)), "no scales"),
+        (dict(), "GPU tensor"),
+    ]
+
+
+def test_wgrad_binding_rejects_bad_tensors():
+    for over, msg in _bad_wgrad_cases():
+        with pytest.raises(ValueError, match=msg):
+            kg.kg_wgrad(**_wgrad_args(**over))
+
+
+def test_wgrad_nt_binding_rejects_bad_tensors():
+    import torch
+    a = _wgrad_args()
+    At = torch.zeros((32, 112), dtype=torch.uint8)[:, :100]
+    Bt = torch.zeros((48, 112), dtype=torch.uint8)[:, :100]
+    call = lambda **o: kg.kg_wgrad_nt(o.get("At", At), a["sa"], o.get("Bt", Bt), a["sb"], None,
+                                      o.get("D", a["D"]), a["ks"], 128, a["dtype"])
+    with pytest.raises(ValueError, match="unit stride"):
+        call(At=torch.zeros((100, 32), dtype=torch.uint8).t())
+    with pytest.raises(ValueError, match="same number of tokens"):
+        call(Bt=torch.zeros((48, 112), dtype=torch.uint8)[:, :90])
+    with pytest.raises(ValueError, match="channels"):
+        call(At=torch.zeros((16, 112), dtype=torch.uint8)[:, :100])
+    with pytest.raises(ValueError, match="must not overlap"):
+        call(At=torch.zeros((32 * 50 + 50,), dtype=torch.uint8).as_strided((32, 100), (50, 1)))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        call()
+
+
+def test_dgrad_binding_rejects_bad_tensors():
+    import torch
+    G, K, N, Mt = 2, 256, 128, 40
+    ok = dict(A=torch.zeros((Mt, K), dtype=torch.uint8), sa=torch.zeros((2, Mt)),
+              W=torch.zeros((G, K, N), dtype=torch.uint8), sw=torch.zeros((G, 2, 1)),
+              D=torch.zeros((Mt, N)), ms=torch.tensor([30, 10], dtype=torch.int32))
+    for over, msg in [(dict(A=torch.zeros((Mt, 128), dtype=torch.uint8)), "A must"),
+                      (dict(sa=torch.zeros((Mt, 2))), "sa must"),
+                      (dict(sw=torch.zeros((G, 2, 2))), "sw must"),
+                      (dict(ms=torch.tensor([40], dtype=torch.int32)), "ms must"),
+                      (dict(D=torch.zeros((Mt, 256))), "D must"),
+                      (dict(W=torch.zeros((G, K, N))), "W must"),
+                      (dict(), "GPU tensor")]:
+        a = dict(ok, **over)
+        with pytest.raises(ValueError, match=msg):
+            kg.kg_dgrad(a["A"], a["sa"], a["W"], a["sw"], a["D"], a["ms"])
+
+
+def test_requant_binding_rejects_bad_tensors():
+    import torch
+    ks = torch.tensor([60, 40], dtype=torch.int32)
+    X = torch.zeros((100, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="no xs"):
+        kg.kg_requant(X, torch.zeros((100, 2)), ks, 128, kg.KG_E4M3_F32SCALE, 2)
+    with pytest.raises(ValueError, match="xs"):
+        kg.kg_requant(torch.zeros((100, 256), dtype=torch.uint8), None, ks, 128,
+                      kg.KG_E4M3_F32SCALE, 2)
+    with pytest.raises(ValueError, match="S must"):
+        kg.kg_requant(X, None, ks, 128, kg.KG_E4M3_F32SCALE, 2, S=torch.zeros((2, 256), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="X must"):
+        kg.kg_requant(X.t(), None, ks, 128, kg.KG_E4M3_F32SCALE, 2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kg.kg_requant(X, None, ks, 128, kg.KG_E4M3_F32SCALE, 2)
