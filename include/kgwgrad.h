@@ -268,7 +268,8 @@ int kg_requant(const void* X, const float* xs, const int32_t* ks, int G, int H, 
  * pointer 16-byte aligned except sw and ms (4 bytes) (KG_ERR_ALIGN). Errors before
  * any launch: KG_ERR_DTYPE (unknown flag), KG_ERR_SHAPE (negative sizes), KG_ERR_NULL,
  * KG_ERR_ALIGN, KG_ERR_ALIAS (D overlapping an input), KG_ERR_UNSUPPORTED (G > 1024,
- * N or K > 2^24, M_total > 2^31 - 1, or a tile's offsets past 32 bits), KG_ERR_HIP.
+ * M_total > 2^31 - 1, or byte offsets within a 256-row tile past 2^31: N > 2097024
+ * or K > 8388480), KG_ERR_HIP.
  * A ms that holds a negative count or does not add up to M_total is reported by
  * kg_status (KG_ERR_KSUM) and nothing is written. G, N or M_total == 0: KG_OK, no
  * launch. Rows of D are written exactly once (by the tile that owns them).

@@ -236,6 +236,9 @@ def dcall(A=FAKE, sa=FAKE, W=FAKE + (1 << 28), sw=FAKE, D=FAKE + (1 << 30), ms=F
     (dict(D=FAKE + (1 << 30) + 4), B.KG_ERR_ALIGN),
     (dict(D=FAKE + 4096), B.KG_ERR_ALIAS),                 # D overlaps A
     (dict(D=FAKE + (1 << 28), flags=kg.KG_FLAG_D_BF16), B.KG_ERR_ALIAS),  # D on W
+    (dict(N=2097152, M=1, D=FAKE + (1 << 40)), B.KG_ERR_UNSUPPORTED),    # 256 x N x 4 >= 2^31
+    (dict(K=8388608, M=1, W=FAKE + (1 << 40), D=FAKE + (1 << 44)),
+     B.KG_ERR_UNSUPPORTED),                                              # 256 x K >= 2^31
 ])
 def test_dgrad_synchronous_errors(kw, code):
     assert dcall(**kw) == code
