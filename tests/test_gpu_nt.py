@@ -304,3 +304,40 @@ def test_nt_limit_row_length(dtype, K):
     check(D)
     del D, D_tn, At, Bt, ws, t, case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,gran,flags", PATHS)
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("split", [False, True])
+def test_nt_canaries_every_path(dtype, gran, flags, out, split):
+    """K-major: nothing written outside D (guard regions), two runs give the same
+    bits; whole tiles equal the token-major kernel's bits in the same mode, stream-K
+    matches the oracle."""
+    from tests.test_gpu_parity import guarded
+    say("nt canaries", dtype, gran, flags, out, split)
+    case = small_case(dtype, gran, [129, 0, 400, 1], 272, 144, seed=17)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    C = t["C"] if out == torch.float32 else t["C"].to(torch.bfloat16)
+    ws = kg.new_workspace(dev()) if split else None
+    D, intact = guarded((case.G, case.M, case.N), out)
+    runs = []
+    for _ in range(2):
+        kg.kg_wgrad_nt(At, t["sa"], Bt, t["sb"], C, D, t["ks"], gran, dtype | flags, workspace=ws)
+        assert kg.kg_status() == kg.KG_OK
+        torch.cuda.synchronize()
+        assert intact(), "a write landed outside D"
+        runs.append(D.clone())
+    assert torch.equal(runs[0].view(torch.int16), runs[1].view(torch.int16))
+    if split:
+        # stream-K cuts ranges in stages, whose length may differ between the layouts
+        D_ref, bound = nt_oracle(case, At, Bt, C=C.float().cpu().numpy())
+        if out == torch.float32:
+            check_close(D, D_ref, bound, "nt canaries", fast=bool(flags))
+        else:
+            check_bf16_out(D, D_ref, bound, "nt canaries", fast=bool(flags))
+        return
+    D_tn = torch.empty_like(D)
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], C, D_tn, t["ks"], gran, dtype | flags)
+    torch.cuda.synchronize()
+    assert torch.equal(D.view(torch.int16), D_tn.view(torch.int16))

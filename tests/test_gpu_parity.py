@@ -44,7 +44,7 @@ def to_dev(case):
 def run_gpu(case, t, D=None, C="default", check_status=True, flags=0):
     if D is None:
         D = torch.full((case.G, case.M, case.N), float("nan"), dtype=torch.float32, device=dev())
-    Cp = t["C"] if C == "default" else C
+    Cp = t["C"] if isinstance(C, str) else C
     kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], Cp, D, t["ks"], case.gran_k,
                 case.dtype | flags, K_total=case.K_total)
     if check_status:
@@ -55,7 +55,7 @@ def run_gpu(case, t, D=None, C="default", check_status=True, flags=0):
 
 def oracle_full(case, C="default"):
     h = case.host()
-    Ch = h["C"] if C == "default" else C
+    Ch = h["C"] if isinstance(C, str) else C
     rc, D, bound = kgref.wgrad(h["A"], h["sa"], h["B"], h["sb"], Ch, h["ks"], case.M, case.N,
                                case.gran_k, case.dtype)
     assert rc == kgref.OK
@@ -261,6 +261,55 @@ def test_guard_canaries_and_determinism():
     assert (buf[:pad] == 12345.0).all() and (buf[pad + n:] == 12345.0).all()
     D2 = run_gpu(case, t)
     assert torch.equal(D.view(torch.int32), D2.view(torch.int32)), "run-to-run bits differ"
+
+
+CANARY_PATHS = [(F32, 128, 0), (F32, 128, FAST), (F32, 32, 0), (F32, 32, FAST), (UE8, 32, 0),
+                (UE8, 32, FAST), (UE8, 128, 0), (UE8, 128, FAST), (BF, 128, 0)]
+
+
+def guarded(shape, dtype, pad=4096):
+    """A tensor of `shape` inside a buffer whose `pad` elements before and after hold a
+    canary pattern; returns (tensor, check) where check() asserts the canaries."""
+    n = int(np.prod(shape))
+    if dtype == torch.float32:
+        buf = torch.full((n + 2 * pad,), 12345.0, dtype=torch.float32, device=dev())
+        pat = torch.tensor(12345.0).view(torch.int32).item()
+        raw = buf.view(torch.int32)
+    else:
+        raw = torch.full((n + 2 * pad,), 0x3F8F, dtype=torch.int16, device=dev())
+        buf, pat = raw.view(torch.bfloat16), 0x3F8F
+    check = lambda: (raw[:pad] == pat).all().item() and (raw[pad + n:] == pat).all().item()
+    return buf[pad:pad + n].view(*shape), check
+
+
+@pytest.mark.parametrize("dtype,gran,flags", CANARY_PATHS)
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("split", [False, True])
+def test_canaries_every_path(dtype, gran, flags, out, split):
+    """Every kind and mode, fp32 and bf16 output, whole tiles and (with the workspace,
+    fp32 output) stream-K: ragged tiles in both dimensions, an empty and a one-token
+    expert, with C. Nothing is written outside D, two runs give the same bits, and the
+    result matches the oracle."""
+    say("canaries", dtype, gran, flags, out, split)
+    case = small_case(dtype, gran, [129, 0, 400, 1], 272, 144, seed=17)
+    t = to_dev(case)
+    C = t["C"] if out == torch.float32 else t["C"].to(torch.bfloat16)
+    ws = kg.new_workspace(dev()) if split else None
+    D, intact = guarded((case.G, case.M, case.N), out)
+    runs = []
+    for _ in range(2):
+        kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], C, D, t["ks"], gran, dtype | flags,
+                    workspace=ws)
+        assert kg.kg_status() == kg.KG_OK
+        torch.cuda.synchronize()
+        assert intact(), "a write landed outside D"
+        runs.append(D.clone())
+    assert torch.equal(runs[0].view(torch.int16), runs[1].view(torch.int16)), "run-to-run bits differ"
+    D_ref, bound = oracle_full(case, C=C.float().cpu().numpy())
+    if out == torch.float32:
+        check_close(D, D_ref, bound, "canaries", fast=bool(flags))
+    else:
+        check_bf16_out(D, D_ref, bound, "canaries", fast=bool(flags))
 
 
 def test_power_of_two_scales_bit_exact_on_gpu():

@@ -43,12 +43,20 @@ def run_case(src, kind, gran, ks, H, seed):
     xsd = None if xs is None else xs.to(d)
     ksd = torch.from_numpy(ks).to(d)
     sdt = torch.float32 if kind == kg.KG_E4M3_F32SCALE else torch.uint8
-    Q = torch.full((K, H), 0x5A, dtype=torch.uint8, device=d)
-    S = torch.full((nblk, H), 0x5A, dtype=torch.uint8, device=d).view(sdt) if sdt == torch.uint8 \
-        else torch.full((nblk, H), float("nan"), device=d)
+    # Q and S inside guarded buffers (4 KB of 0x5A bytes before and after each)
+    pad = 4096
+    qbuf = torch.full((K * H + 2 * pad,), 0x5A, dtype=torch.uint8, device=d)
+    Q = qbuf[pad:pad + K * H].view(K, H)
+    ssz = nblk * H * (4 if sdt == torch.float32 else 1)
+    sbuf = torch.full((ssz + 2 * pad,), 0x5A, dtype=torch.uint8, device=d)
+    S = sbuf[pad:pad + ssz].view(sdt).view(nblk, H)
+    if sdt == torch.float32:
+        S.fill_(float("nan"))
     rc = kg.kg_requant_raw(Xd, xsd, ksd, ks.size, H, K, gran, src, kind, Q, S)
     assert rc == kg.KG_OK
     assert kg.kg_status() == kg.KG_OK
+    for buf, n in ((qbuf, K * H), (sbuf, ssz)):
+        assert (buf[:pad] == 0x5A).all() and (buf[pad + n:] == 0x5A).all(), "write outside Q or S"
     rc, Qr, Sr = kgref.requant(Xh, xsh, ks, H, gran, SRC[src], KIND[kind])
     assert rc == kgref.OK
     Qg = Q.cpu().numpy()
