@@ -21,12 +21,15 @@ _lib = None
 
 
 def lib():
-    """Load the oracle library, compiling it first only if it is not built."""
+    """Load the oracle library, compiling it first only if it is not built.
+    KGREF_LIB names another build of kgref.c (the test suite's planted-mistake
+    check loads deliberately broken copies that way)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("KGREF_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.kgref_e4m3.restype = ctypes.c_double
         L.kgref_e4m3.argtypes = [ctypes.c_uint8]
