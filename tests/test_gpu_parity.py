@@ -191,6 +191,10 @@ SPLIT_SHAPES = [
     ([300, 0, 517], 256, 256, True),      # few stages over every CU: tiles cut into 1-stage units
     ([4000, 1234], 512, 1024, False),     # several tiles per expert, cuts inside tiles
     ([0, 1, 33, 0], 256, 512, True),      # tiny and empty experts
+    # the largest group count stream-K takes (64), and one more (whole tiles although
+    # a workspace is given); ragged experts, every ninth one empty
+    ([0 if i % 9 == 0 else (37 * i) % 301 + 1 for i in range(64)], 128, 256, True),
+    ([0 if i % 9 == 0 else (37 * i) % 301 + 1 for i in range(65)], 128, 256, False),
 ]
 
 
