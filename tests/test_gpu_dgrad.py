@@ -71,6 +71,11 @@ def check(D, ref, bound, fast=False, what=""):
     ([40], 128, 128),                    # one partial tile, one stage
     ([0, 257, 0], 256, 1024),            # 257 rows: a full tile and a one-row tile
     ([300, 0, 1, 517, 256], 768, 384),   # N a multiple of 256: the wide tile (fp8 MFMA)
+    # the largest group count of the wide tile (512), one more, and the most groups
+    # (1024): 0-5 rows per expert, every seventh one empty
+    ([0 if i % 7 == 0 else i % 5 + 1 for i in range(512)], 256, 128),
+    ([0 if i % 7 == 0 else i % 5 + 1 for i in range(513)], 256, 128),
+    ([0 if i % 7 == 0 else i % 5 + 1 for i in range(1024)], 128, 256),
 ])
 @pytest.mark.parametrize("flags", [0, FAST])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])

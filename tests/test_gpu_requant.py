@@ -84,6 +84,14 @@ def test_requant_bit_exact_routed_shape(kind):
     run_case(kg.KG_SRC_BF16, kind, 128 if kind == kg.KG_E4M3_F32SCALE else 32, ks, 1024, seed=9)
 
 
+@pytest.mark.parametrize("kind,gran", [(kg.KG_E4M3_F32SCALE, 128), (kg.KG_E4M3_UE8M0, 32)])
+def test_requant_bit_exact_most_groups(kind, gran):
+    # G = 1024 (the most accepted): 0-40 tokens per expert, every seventh one empty
+    say("requant 1024 groups", kind, gran)
+    ks = [0 if i % 7 == 0 else (13 * i) % 41 for i in range(1024)]
+    run_case(kg.KG_SRC_BF16, kind, gran, ks, 256, seed=12)
+
+
 def test_requant_ksum_mismatch_writes_nothing():
     say("requant ksum")
     d = torch.device("cuda:0")
