@@ -1068,14 +1068,21 @@ __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][
       const v4bf x1 = rd16<CF, CF::ROWA>(aBase, i, kk, 1);
       af[i] = v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
+    v8bf bf[CF::NJ];
 #pragma unroll
     for (int jn = 0; jn < CF::NJ; ++jn) {
       const v4bf y0 = rd16<CF, CF::ROWB>(bBase, jn, kk, 0);
       const v4bf y1 = rd16<CF, CF::ROWB>(bBase, jn, kk, 1);
-      const v8bf b = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-#pragma unroll
-      for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i], b, acc[i][jn]);
+      bf[jn] = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
     }
+    // K-major: keep the step's B reads together (left alone, the scheduler reads one
+    // fragment, waits for it and runs its four MFMAs, fragment after fragment: 3%
+    // slower on the default bf16 problem)
+    if constexpr (CF::NT) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jn = 0; jn < CF::NJ; ++jn)
+#pragma unroll
+      for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i], bf[jn], acc[i][jn]);
   }
 }
 
