@@ -735,8 +735,11 @@ __device__ inline float e8m0_scale(int e) {
 
 // Fragment readers. `base` is this lane's base in the operand: token-major, its row
 // of the transposing read; K-major, its channel row of the wave's first sub-tile
-// plus its first token byte (the K-major offsets below are then immediates). Both
-// layouts give a lane the same tokens, so the MFMAs see the same operands.
+// plus its first token byte (the K-major offsets below are then immediates). For the
+// fp8 kinds both layouts give a lane the same tokens, so the MFMAs see the same
+// operands; K-major bf16 gives lane group q tokens 8q..8q+7 of each 32-token step
+// (one 16-byte read; the paired 8-byte reads of the token-major order conflicted in
+// the LDS banks), an order the MFMA sums with different roundings.
 // fp8, tokens 32kk + 8q .. +7 of sub-tile row (column) i (K-major base: + 8q):
 template <class CF, int ROW>
 __device__ inline v2i rd8(const unsigned char* base, int i, int kk) {
@@ -762,13 +765,11 @@ __device__ inline v8i rdf8(const unsigned char* base, int i) {
   }
 }
 
-// bf16, tokens 32kk + 16h + 4q .. +3 of sub-tile row (column) i (K-major base: + 8q)
+// bf16 token-major, tokens 32kk + 16h + 4q .. +3 of sub-tile row (column) i (the
+// K-major bf16 path reads 8 consecutive tokens per lane instead, see compute_bf16)
 template <class CF, int ROW>
 __device__ inline v4bf rd16(const unsigned char* base, int i, int kk, int h) {
-  if constexpr (CF::NT)
-    return *(const v4bf*)(base + i * CF::NT_SUB + 64 * kk + 32 * h);
-  else
-    return tr16(base + (32 * kk + 16 * h) * ROW + 32 * i);
+  return tr16(base + (32 * kk + 16 * h) * ROW + 32 * i);
 }
 
 // ---------------------------------------------------------------- compute policies
@@ -1048,15 +1049,17 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
 // bf16: lane 4r+c of a 16-lane group names token row r, halfwords 4c..4c+3; lane
 // base row 4q + j/4. For MFMA kk lane group q takes tokens 32kk + 4q + 0..3 and
 // 32kk + 16 + 4q + 0..3 (a half-wave reads 8 consecutive rows per transposing read).
+// K-major: lane (q, j) reads tokens 32kk + 8q .. +7 of channel row j in one 16-byte
+// read (A and B alike, so the MFMA pairs the same tokens).
 template <class CF>
 __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = 4 * q + (j >> 2);
-  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + 8 * q
+  const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + 16 * q
                                       : st + lrow * CF::ROWA + 8 * (j & 3) + 2 * (wm * CF::WM);
-  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + 8 * q
+  const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + 16 * q
                                       : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 3) +
                                             2 * (wn * CF::WN);
 #pragma unroll
@@ -1064,20 +1067,27 @@ __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][
     v8bf af[CF::NI];
 #pragma unroll
     for (int i = 0; i < CF::NI; ++i) {
-      const v4bf x0 = rd16<CF, CF::ROWA>(aBase, i, kk, 0);
-      const v4bf x1 = rd16<CF, CF::ROWA>(aBase, i, kk, 1);
-      af[i] = v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      if constexpr (CF::NT) {
+        af[i] = *(const v8bf*)(aBase + i * CF::NT_SUB + 64 * kk);
+      } else {
+        const v4bf x0 = rd16<CF, CF::ROWA>(aBase, i, kk, 0);
+        const v4bf x1 = rd16<CF, CF::ROWA>(aBase, i, kk, 1);
+        af[i] = v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
     }
     v8bf bf[CF::NJ];
 #pragma unroll
     for (int jn = 0; jn < CF::NJ; ++jn) {
-      const v4bf y0 = rd16<CF, CF::ROWB>(bBase, jn, kk, 0);
-      const v4bf y1 = rd16<CF, CF::ROWB>(bBase, jn, kk, 1);
-      bf[jn] = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+      if constexpr (CF::NT) {
+        bf[jn] = *(const v8bf*)(bBase + jn * CF::NT_SUB + 64 * kk);
+      } else {
+        const v4bf y0 = rd16<CF, CF::ROWB>(bBase, jn, kk, 0);
+        const v4bf y1 = rd16<CF, CF::ROWB>(bBase, jn, kk, 1);
+        bf[jn] = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+      }
     }
-    // K-major: keep the step's B reads together (left alone, the scheduler reads one
-    // fragment, waits for it and runs its four MFMAs, fragment after fragment: 3%
-    // slower on the default bf16 problem)
+    // K-major: keep the step's B reads together (left alone, the scheduler read one
+    // fragment, waited for it and ran its four MFMAs, fragment after fragment)
     if constexpr (CF::NT) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int jn = 0; jn < CF::NJ; ++jn)

@@ -3,8 +3,11 @@ the CPU oracle (kgref.wgrad_nt), with the tolerances of the token-major path
 (precise: 1e-5 * sum|ab| + 1e-6 per element, Frobenius 1e-5; fp8-MFMA mode:
 2^-10 * sum|ab| + 1e-6, Frobenius 1e-4). The K-major operands sit in row buffers
 padded with NaN codes, so a read past an expert's tokens or into the padding shows.
-Both layouts hand every MFMA the same operands, so in whole-tile mode the K-major
-result also equals the token-major kernel's bit for bit.
+For the fp8 kinds both layouts hand every MFMA the same operands, so in whole-tile
+mode the K-major result also equals the token-major kernel's bit for bit. The bf16
+K-major kernel gives the MFMA a step's tokens in another order (one 16-byte LDS read
+per lane), whose sums round differently: it is held to the oracle's tolerance (and
+is exact wherever the sums are, see test_nt_limit_row_length).
 """
 import numpy as np
 import pytest
@@ -66,11 +69,12 @@ def test_nt_ragged_matches_oracle_and_token_major(dtype, gran, flags):
     check_close(D, D_ref, bound, f"nt {dtype} {gran} {flags}", fast=bool(flags))
     g = NT_KS.index(0)
     assert torch.equal(D[g].cpu().view(torch.int32), case.C[g].view(torch.int32))
-    # the token-major kernel on the same matrices: the same bits
-    D_tn = torch.full_like(D, float("nan"))
-    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], gran, dtype | flags)
-    torch.cuda.synchronize()
-    assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
+    # the token-major kernel on the same matrices: the same bits (fp8 kinds)
+    if dtype != BF:
+        D_tn = torch.full_like(D, float("nan"))
+        kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], gran, dtype | flags)
+        torch.cuda.synchronize()
+        assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
 
 
 @pytest.mark.parametrize("dtype,gran,flags", [(F32, 128, 0), (UE8, 32, FAST), (BF, 128, 0)])
@@ -232,8 +236,8 @@ def test_nt_edge_cases():
 @pytest.mark.parametrize("dtype,gran,flags", [(F32, 128, 0), (F32, 128, FAST), (BF, 128, 0)])
 def test_nt_limit_m_2p24_bit_identical(dtype, gran, flags):
     """M = 2^24 (the largest accepted), ragged experts around an empty one, with C:
-    the K-major kernel equals the token-major one bit for bit (whole tiles), and
-    sampled outputs match the oracle."""
+    sampled outputs match the oracle, and the fp8 kinds equal the token-major kernel
+    bit for bit (whole tiles)."""
     from tests.test_gpu_parity import sampled_check
     M, N = 1 << 24, 16
     say("nt limit M", dtype, gran, flags)
@@ -242,11 +246,13 @@ def test_nt_limit_m_2p24_bit_identical(dtype, gran, flags):
     t = to_dev(case)
     At, Bt = nt_dev(case, t)
     D = run_nt(case, t, At, Bt, flags)
-    D_tn = torch.full_like(D, float("nan"))
-    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], gran, dtype | flags)
-    torch.cuda.synchronize()
-    assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
-    del D_tn, At, Bt
+    if dtype != BF:
+        D_tn = torch.full_like(D, float("nan"))
+        kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], gran, dtype | flags)
+        torch.cuda.synchronize()
+        assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
+        del D_tn
+    del At, Bt
     sampled_check(case, t, D, n=300, seed=1, fast=bool(flags))
     del D, t, case
     torch.cuda.empty_cache()
@@ -311,8 +317,8 @@ def test_nt_limit_row_length(dtype, K):
 @pytest.mark.parametrize("split", [False, True])
 def test_nt_canaries_every_path(dtype, gran, flags, out, split):
     """K-major: nothing written outside D (guard regions), two runs give the same
-    bits; whole tiles equal the token-major kernel's bits in the same mode, stream-K
-    matches the oracle."""
+    bits; whole tiles of the fp8 kinds equal the token-major kernel's bits in the same
+    mode; bf16 and stream-K match the oracle."""
     from tests.test_gpu_parity import guarded
     say("nt canaries", dtype, gran, flags, out, split)
     case = small_case(dtype, gran, [129, 0, 400, 1], 272, 144, seed=17)
@@ -336,6 +342,13 @@ def test_nt_canaries_every_path(dtype, gran, flags, out, split):
             check_close(D, D_ref, bound, "nt canaries", fast=bool(flags))
         else:
             check_bf16_out(D, D_ref, bound, "nt canaries", fast=bool(flags))
+        return
+    if dtype == BF:
+        D_ref, bound = nt_oracle(case, At, Bt, C=C.float().cpu().numpy())
+        if out == torch.float32:
+            check_close(D, D_ref, bound, "nt canaries")
+        else:
+            check_bf16_out(D, D_ref, bound, "nt canaries")
         return
     D_tn = torch.empty_like(D)
     kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], C, D_tn, t["ks"], gran, dtype | flags)
