@@ -735,11 +735,12 @@ __device__ inline float e8m0_scale(int e) {
 
 // Fragment readers. `base` is this lane's base in the operand: token-major, its row
 // of the transposing read; K-major, its channel row of the wave's first sub-tile
-// plus its first token byte (the K-major offsets below are then immediates). For the
-// fp8 kinds both layouts give a lane the same tokens, so the MFMAs see the same
-// operands; K-major bf16 gives lane group q tokens 8q..8q+7 of each 32-token step
-// (one 16-byte read; the paired 8-byte reads of the token-major order conflicted in
-// the LDS banks), an order the MFMA sums with different roundings.
+// plus its first token byte (the K-major offsets below are then immediates). Both
+// layouts give a lane the same tokens, so the MFMAs see the same operands, except in
+// two K-major paths that read whole 16-byte runs instead (the split runs of the
+// token-major order conflicted in the LDS banks): bf16 (compute_bf16) and fp32
+// scales in the fp8-MFMA mode (rdf8n); the MFMA sums those orders with different
+// roundings.
 // fp8, tokens 32kk + 8q .. +7 of sub-tile row (column) i (K-major base: + 8q):
 template <class CF, int ROW>
 __device__ inline v2i rd8(const unsigned char* base, int i, int kk) {
@@ -780,13 +781,29 @@ __device__ inline v4bf rd16(const unsigned char* base, int i, int kk, int h) {
 
 // fast fp8 + fp32 scales: one fp8 MFMA per sub-tile gives the block partial; the
 // rescale of sub-tile s-1 is issued after the MFMA of sub-tile s so they overlap.
+// K-major fp8-MFMA mode with fp32 scales: lane group q takes tokens 32q .. 32q+31 of
+// the 128-token step, two aligned 16-byte reads (the split runs of the token-major
+// order conflict in the LDS banks; the block partial is rescaled after the MFMA, so
+// any order shared by A and B gives it, with its own roundings)
+template <class CF>
+__device__ inline v8i rdf8n(const unsigned char* base, int i) {
+  if constexpr (CF::NT) {
+    const unsigned char* r = base + i * CF::NT_SUB;
+    const v4i x0 = *(const v4i*)(r);
+    const v4i x1 = *(const v4i*)(r + 16);
+    return v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  } else {
+    return rdf8<CF, CF::ROWA>(base, i);
+  }
+}
+
 template <class CF>
 __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = fast_row(q, j);
-  const int lbyte = 32 * (q >> 1) + 8 * (q & 1);  // K-major: first token byte
+  const int lbyte = CF::NT ? 32 * q : 32 * (q >> 1) + 8 * (q & 1);  // K-major: first token byte
   const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + lbyte
                                       : st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
   const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + lbyte
@@ -795,9 +812,9 @@ __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF:
   const float* sSb = (const float*)(st + CF::SB_OFF);
   v8i af[CF::NI];
 #pragma unroll
-  for (int i = 0; i < CF::NI; ++i) af[i] = rdf8<CF, CF::ROWA>(aBase, i);
+  for (int i = 0; i < CF::NI; ++i) af[i] = CF::NT ? rdf8n<CF>(aBase, i) : rdf8<CF, CF::ROWA>(aBase, i);
   constexpr int S = CF::NI * CF::NJ;
-  v8i bcur = rdf8<CF, CF::ROWB>(bBase, 0), bnext = bcur;
+  v8i bcur = CF::NT ? rdf8n<CF>(bBase, 0) : rdf8<CF, CF::ROWB>(bBase, 0), bnext = bcur;
   v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
   // rescale of sub-tile (pi, pj): acc += (sa[rows] * sb[col]) * partial
   auto rescale = [&](int pi, int pj, const v4f& part) {
@@ -809,7 +826,7 @@ __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF:
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int jn = s / CF::NI, i = s % CF::NI;
-    if (i == 0 && jn + 1 < CF::NJ) bnext = rdf8<CF, CF::ROWB>(bBase, jn + 1);
+    if (i == 0 && jn + 1 < CF::NJ) bnext = CF::NT ? rdf8n<CF>(bBase, jn + 1) : rdf8<CF, CF::ROWB>(bBase, jn + 1);
     const v4f part = mfma_fp8(af[i], bcur, v4f{0.f, 0.f, 0.f, 0.f});
     if (s > 0) rescale((s - 1) % CF::NI, (s - 1) / CF::NI, prev);
     prev = part;
