@@ -1103,8 +1103,10 @@ __device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][
         bf[jn] = v8bf{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
       }
     }
-    // K-major: keep the step's B reads together (left alone, the scheduler read one
-    // fragment, waited for it and ran its four MFMAs, fragment after fragment)
+    // K-major: keep the step's B reads ahead of its MFMAs (with the earlier 8-byte
+    // runs the scheduler read one fragment, waited and ran its four MFMAs, fragment
+    // after fragment; with the 16-byte reads it keeps them together by itself and
+    // this barrier changes nothing measurable)
     if constexpr (CF::NT) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int jn = 0; jn < CF::NJ; ++jn)
