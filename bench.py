@@ -7,11 +7,18 @@ path: device scan of the expert sizes, schedule, grouped contraction with the
 block rescale, epilogue with C, empty-expert fill). Inputs are resident in HBM
 before the timed region. Prints one JSON line.
 
-Default workload: bf16, G = 4 experts, M = 1024, N = 2048, 16384 tokens routed
-uniformly over three experts (the second expert gets none), D accumulated onto
-C. The other workloads (worked, zipf_fp8, ue8m0_many, local_share, and the six
-non-grouped shapes single_m{m}_n{n}_k{k} of the issue page's 1D1D table) are
-selectable with --workload.
+Default workload: one GPU's local expert share, G = 8 experts, M = 7168, N = 4096,
+262144 tokens with per-expert counts ~N(32768, 8192), fp8 e4m3 with fp32 scales per
+128 tokens, D accumulated onto C; the default (precise) mode, which meets the
+1e-5 tolerance. The other workloads (worked, bf16, zipf_fp8, ue8m0_many, and the
+six non-grouped shapes single_m{m}_n{n}_k{k} of the issue page's 1D1D table) are
+selectable with --workload; --fast selects the fp8-MFMA mode.
+
+Untimed steps run before the timed ones: the --warmup steps asked for, then more
+until about one second has passed (--settle-s), so that the clocks have settled.
+After the timed region, `cold` times launches that each follow a 1 GiB write (L2
+and the 256 MB MALL hold none of the inputs), and `worked_shape` gives the worked
+shape's microseconds per call (launch-latency bound).
 
     python bench.py --dgrad NAME [--fast] [--fp32-out]
 
@@ -31,8 +38,12 @@ reports GB/s of algorithmic traffic (source read, codes and scales written) agai
 The JSON line carries:
   value / ms_per_step     TFLOP/s of useful work 2*sum(K_g)*M*N over the timed steps
   roofline                the kernel's average launch time (HIP events on its
-                          stream) against its bound: MFMA peak for its dtype or
-                          8 TB/s of HBM, whichever the algorithmic work hits first;
+                          stream at the two ends of the back-to-back timed steps)
+                          against its bound: MFMA peak for its dtype or 8 TB/s of
+                          HBM, whichever the algorithmic work hits first; the
+                          precise fp8 mode also reports its fraction of the bf16
+                          MFMA peak it contracts at (bf16_mfma_ceiling_frac), and
+                          mfma_counters the stored rocprofv3 MFMA-busy record;
                           `traffic` is the measured HBM bytes per launch from
                           rocprofv3 counters (profiles/*.json) if those were taken
                           for the current kernel source, else null
@@ -105,7 +116,10 @@ def _counter_rows(path):
     with open(path) as f:
         for row in csv.DictReader(f):
             key = (row.get("Dispatch_Id") or row.get("Correlation_Id"), row["Kernel_Name"])
-            out.setdefault(key, {})[row["Counter_Name"]] = float(row["Counter_Value"])
+            rec = out.setdefault(key, {})
+            rec[row["Counter_Name"]] = float(row["Counter_Value"])
+            if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+                rec["duration_ns"] = float(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
     return out
 
 
@@ -143,6 +157,70 @@ def ingest_counters(fetch_csv, write_csv, name):
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT",
+                 "SQ_LDS_IDX_ACTIVE", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE",
+                 "GRBM_COUNT")
+SIMDS = 4 * 256  # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8  # GRBM counters come summed over the 8 XCDs' GRBMs
+
+
+def ingest_mfma(csv_path, name, command):
+    """MFMA utilisation of a kernel from one rocprofv3 --pmc pass over MFMA_COUNTERS
+    (CSV): per dispatch (median over the kernel's dispatches) the MFMA-busy fraction
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDS x SIMDs) (rocprofv3's MfmaUtil,
+    which takes the largest of the XCDs' GUI-active counts; the CSV holds their sum);
+    the busy pipe runs at the bf16 rate for bf16 MFMAs and at the fp8 rate for fp8
+    ones. Also the MFMA work it counted (MOPS x 512 flops) and the rate that gives over
+    the dispatch's duration, the shader clock (GUI-active cycles per second), LDS
+    bank-conflict cycles per LDS-active cycle, and the raw counters. `name` as for
+    ingest_counters."""
+    kern = "kg_wgrad"
+    for prefix in ("dgrad", "requant"):
+        if name.startswith(prefix + ":"):
+            kern, name = "kg_" + prefix, name[len(prefix) + 1:]
+    rows = _counter_rows(csv_path)
+    mine = [v for (d, k), v in rows.items() if kern + "_kernel" in k]
+    assert mine, f"no {kern} dispatch in {csv_path}"
+    med = lambda c: sorted(v.get(c, float("nan")) for v in mine)[len(mine) // 2]
+    raw = {c: med(c) for c in MFMA_COUNTERS + ("duration_ns",)}
+    busy = raw["SQ_VALU_MFMA_BUSY_CYCLES"] / (raw["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+    flops = (raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + raw["SQ_INSTS_VALU_MFMA_MOPS_F8"]) * 512
+    rec = {"workload": name, "kernel_source": kernel_source_hash(), "command": command,
+           "dispatches": len(mine),
+           "mfma_busy_frac": round(busy, 4),
+           "duration_ms_median": round(raw["duration_ns"] / 1e6, 4),
+           "shader_clock_ghz": round(raw["GRBM_GUI_ACTIVE"] / XCDS / raw["duration_ns"], 3),
+           "mfma_tflops_counted": round(flops / raw["duration_ns"] / 1e3, 1),
+           "mfma_flops_counted": (raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] +
+                                  raw["SQ_INSTS_VALU_MFMA_MOPS_F8"]) * 512,
+           "mfma_flops_bf16": raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512,
+           "mfma_flops_f8": raw["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512,
+           "lds_bank_conflict_per_active": round(raw["SQ_LDS_BANK_CONFLICT"] /
+                                                 max(raw["SQ_LDS_IDX_ACTIVE"], 1.0), 4),
+           "counters_median": raw}
+    path = os.path.join(ROOT, "profiles", f"{kern}_{name}_mfma.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def mfma_counters_for(name, kernel="kg_wgrad"):
+    """Stored MFMA counters of this kernel source and workload, or None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{name}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source") != kernel_source_hash():
+        return None
+    return {"mfma_busy_frac": rec["mfma_busy_frac"],
+            "mfma_flops_counted": rec["mfma_flops_counted"],
+            "shader_clock_ghz": rec["shader_clock_ghz"],
+            "lds_bank_conflict_per_active": rec["lds_bank_conflict_per_active"],
+            "source": os.path.relpath(path, ROOT)}
 
 
 def copy_calibration(args, dev):
@@ -200,21 +278,47 @@ def timed_steps(step, steps, stream):
 
 
 def warm_up(step, warmup, seconds=1.0):
-    """Run `warmup` untimed steps; with None, as many as fit in `seconds` (at least
-    10). Returns the number run."""
+    """Run `warmup` untimed steps (10 if None), then more untimed steps until about
+    `seconds` have passed in all: with only a few warm-up calls the first timed calls
+    run at lower clocks (the default line read 8-10% low). Returns (steps asked for,
+    steps run in all, seconds)."""
     import torch
-    if warmup is not None:
-        for _ in range(warmup):
+    asked = 10 if warmup is None else warmup
+    t0 = time.perf_counter()
+    for _ in range(asked):
+        step()
+    torch.cuda.synchronize()
+    n = asked
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
             step()
+        n += 5
         torch.cuda.synchronize()
-        return warmup
-    n, t0 = 0, time.perf_counter()
-    while n < 10 or time.perf_counter() - t0 < seconds:
-        for _ in range(10):
-            step()
-        n += 10
-        torch.cuda.synchronize()
-    return n
+    return asked, n, time.perf_counter() - t0
+
+
+# Bytes written between cold-cache launches: four times the 256 MB Infinity Cache
+# (MALL) and far more than the L2s, so that a launch finds none of its inputs cached.
+FLUSH_BYTES = 1 << 30
+
+
+def cold_launches(step, n, stream):
+    """Median duration (ms) of `n` launches of `step`, each preceded by a write of
+    FLUSH_BYTES to a scratch buffer outside its events (cold L2 and MALL)."""
+    import torch
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(n):
+        scratch.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del scratch
+    times.sort()
+    return times[len(times) // 2]
 
 
 def cpu_baseline(case, budget_s=12.0):
@@ -296,14 +400,14 @@ def requant_main(args):
         rc = kg.kg_requant_raw(X, xs, ksd, ks.size, H, K, gran, src, kind, Q, S)
         assert rc == kg.KG_OK, rc
 
-    args.warmup = warm_up(step, args.warmup)
+    args.warmup, settle_steps, settle_s = warm_up(step, args.warmup, args.settle_s)
     assert kg.kg_status() == kg.KG_OK
     stream = torch.cuda.current_stream()
     ms_per_step, avg_ms, _, nsampled = timed_steps(step, args.steps, stream)
     assert kg.kg_status() == kg.KG_OK
     nbytes = (K * H * (2 if src == kg.KG_SRC_BF16 else 1) + (0 if xs is None else xs.numel() * 4)
               + K * H + nblk * H * (4 if kind == kg.KG_E4M3_F32SCALE else 1))
-    achieved = nbytes / (avg_ms / 1e3) / 1e9
+    achieved = nbytes / (ms_per_step / 1e3) / 1e9
     line = {
         "metric": "requantiser GB/s of algorithmic HBM traffic (source read + codes and scales "
                   "written) + % of HBM roofline, 1 GPU",
@@ -322,8 +426,9 @@ def requant_main(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
                      "traffic": counters_for(args.requant, False, False, "kg_requant"),
-                     "algorithmic_bytes": nbytes, "launch_ms": round(avg_ms, 5),
-                     "launches_timed": nsampled},
+                     "algorithmic_bytes": nbytes, "launch_ms": round(ms_per_step, 5),
+                     "launch_ms_sampled_events": round(avg_ms, 5),
+                     "launches_timed": args.steps},
     }
     if not args.no_cpu:
         from oracle import kgref
@@ -369,7 +474,7 @@ def dgrad_main(args):
     def step():
         kg.kg_dgrad(c.A, c.sa, c.W, c.sw, D, ms, flags)
 
-    args.warmup = warm_up(step, args.warmup)
+    args.warmup, settle_steps, settle_s = warm_up(step, args.warmup, args.settle_s)
     assert kg.kg_status() == kg.KG_OK
     stream = torch.cuda.current_stream()
     ms_per_step, avg_ms, wall, nsampled = timed_steps(step, args.steps, stream)
@@ -378,7 +483,7 @@ def dgrad_main(args):
     nbytes = c.algorithmic_bytes(4 if args.fp32_out else 2)
     mfma_peak = PEAK["fp8"]
     t_mfma, t_hbm = flops / (mfma_peak * 1e12), nbytes / (HBM_GBS * 1e9)
-    secs = avg_ms / 1e3
+    secs = ms_per_step / 1e3
     if t_mfma >= t_hbm:
         roof = {"bound": "mfma", "achieved": round(flops / secs / 1e12, 3), "peak": mfma_peak,
                 "unit": "TFLOP/s"}
@@ -390,8 +495,9 @@ def dgrad_main(args):
                                    "kg_dgrad")
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
-    roof["launch_ms"] = round(avg_ms, 5)
-    roof["launches_timed"] = nsampled
+    roof["launch_ms"] = round(ms_per_step, 5)
+    roof["launch_ms_sampled_events"] = round(avg_ms, 5)
+    roof["launches_timed"] = args.steps
     line = {
         "metric": "M-grouped dgrad TFLOP/s (2*M_total*N*K) + % of FP8 MFMA / HBM roofline, 1 GPU",
         "value": round(flops / (ms_per_step / 1e3) / 1e12, 3),
@@ -447,9 +553,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps before the timed ones (default: as many as fit in "
                          "about one second, so that the GPU clocks have settled)")
-    ap.add_argument("--workload", default="bf16", choices=list(DESCR))
+    ap.add_argument("--workload", default="local_share", choices=list(DESCR))
     ap.add_argument("--fast", action="store_true", help="fp8 kinds: contract with the fp8 MFMA")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache launches (each after a 1 GiB write)")
+    ap.add_argument("--no-worked", action="store_true",
+                    help="skip the worked-shape (launch-latency) timing")
     ap.add_argument("--gran-k", type=int, default=None, choices=[32, 128],
                     help="replace an fp8 workload's scale granularity (tokens per scale)")
     ap.add_argument("--bf16-out", action="store_true",
@@ -462,6 +572,11 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run one plain 1 GiB device copy (untimed), so that a counter "
                          "run sees it beside the kernel (HBM counter calibration)")
+    ap.add_argument("--ingest-mfma", nargs=3, metavar=("CSV", "NAME", "COMMAND"),
+                    help="turn one rocprofv3 --pmc CSV over the MFMA counters into "
+                         "profiles/kg_wgrad_NAME_mfma.json (COMMAND: the profiled command)")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the timed ones (clock settling)")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "NAME"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) into "
                          "profiles/kg_wgrad_NAME_traffic.json")
@@ -485,6 +600,9 @@ def main():
         return
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
+        return
+    if args.ingest_mfma:
+        ingest_mfma(*args.ingest_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
@@ -523,7 +641,7 @@ def main():
             kg.kg_wgrad(A, sa, B, sb, C, D, ks, case.gran_k, dtype, K_total=case.K_total,
                         workspace=ws)
 
-    args.warmup = warm_up(step, args.warmup)
+    args.warmup, settle_steps, settle_s = warm_up(step, args.warmup, args.settle_s)
     assert kg.kg_status() == kg.KG_OK
     torch.cuda.synchronize()
 
@@ -537,21 +655,38 @@ def main():
     mfma_peak = PEAK["bf16"] if is_bf16 else PEAK["fp8"]
     t_mfma = flops / (mfma_peak * 1e12)
     t_hbm = nbytes / (HBM_GBS * 1e9)
-    secs = avg_launch_ms / 1e3
-    if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": round(flops / secs / 1e12, 3), "peak": mfma_peak,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+
+    def roof_of(ms):
+        secs = ms / 1e3
+        if bound == "mfma":
+            r = {"bound": "mfma", "achieved": round(flops / secs / 1e12, 3), "peak": mfma_peak,
+                 "unit": "TFLOP/s"}
+        else:
+            r = {"bound": "hbm", "achieved": round(nbytes / secs / 1e9, 3), "peak": HBM_GBS,
+                 "unit": "GB/s"}
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+        return r
+
+    # the roofline's launch duration: every timed launch (events at the two ends of the
+    # back-to-back region on the launch stream); the sampled per-launch events are kept
+    # beside it (they carry a few microseconds of event overhead each)
+    roof = roof_of(ms_per_step)
+    name = args.workload + ("_nt" if args.nt else "") + ("_fast" if flags else "") + \
+        ("_bf16out" if args.bf16_out else "")
     roof["traffic"] = (counters_for(args.workload, bool(flags), args.bf16_out, nt=args.nt)
                        if args.gran_k is None else None)
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     roof["roofline_ms"] = round(max(t_mfma, t_hbm) * 1e3, 4)
-    roof["launch_ms"] = round(avg_launch_ms, 5)
-    roof["launches_timed"] = nsampled
+    roof["launch_ms"] = round(ms_per_step, 5)
+    roof["launch_ms_sampled_events"] = round(avg_launch_ms, 5)
+    roof["launches_timed"] = args.steps
+    if not is_bf16 and not flags:
+        # the precise fp8 path contracts exactly widened values with the bf16 MFMA
+        roof["bf16_mfma_ceiling_frac"] = round(flops / (ms_per_step / 1e3) / 1e12 / PEAK["bf16"], 4)
+    if args.gran_k is None:
+        roof["mfma_counters"] = mfma_counters_for(name)
 
     value = flops / (ms_per_step / 1e3) / 1e12
     dname = "bf16" if is_bf16 else ("fp8 e4m3 (fp8 MFMA)" if flags else "fp8 e4m3 (bf16 MFMA)")
@@ -578,11 +713,56 @@ def main():
         "roofline": roof,
         "pct_fp8_peak": round(100.0 * value / PEAK["fp8"], 2),
         "hbm_gbs": round(nbytes / (ms_per_step / 1e3) / 1e9, 1),
+        "settle": {"steps": settle_steps, "s": round(settle_s, 3),
+                   "note": "untimed steps run in all before the timed region (at least the "
+                           "warmup steps asked for, and about one second so the clocks settle)"},
         "wall_s": round(wall, 4),
     }
+    if not args.no_cold:
+        cold_ms = cold_launches(step, min(args.steps, 20), stream)
+        assert kg.kg_status() == kg.KG_OK
+        cold = roof_of(cold_ms)
+        line["cold"] = {"launch_ms": round(cold_ms, 5), "value": round(flops / cold_ms / 1e9, 3),
+                        "unit": "TFLOP/s", "frac": cold["frac"], "bound": bound,
+                        "note": f"median of {min(args.steps, 20)} launches, each after a "
+                                f"{FLUSH_BYTES >> 20} MiB write outside its events (L2 and MALL cold)"}
+    del A, B, sa, sb, C, D
+    if args.workload != "worked" and not args.no_worked:
+        line["worked_shape"] = worked_shape_timing(kg, inputs)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)
+
+
+def worked_shape_timing(kg, inputs, calls=400):
+    """The how-to page's worked shape (3 experts of 32, 45 and 27 tokens, 64 x 128, fp8
+    with fp32 scales per 128 tokens): microseconds per call, launch-latency bound."""
+    import torch
+    c = inputs.workload("worked", device="cuda")
+    ks = torch.from_numpy(c.ks).cuda()
+    D = torch.empty((c.G, c.M, c.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        kg.kg_wgrad(c.A, c.sa, c.B, c.sb, None, D, ks, c.gran_k, c.dtype, K_total=c.K_total)
+
+    warm_up(step, 50, seconds=0.2)
+    stream = torch.cuda.current_stream()
+    ms, _, _, _ = timed_steps(step, calls, stream)
+    # one call on its own, events around it
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    singles = []
+    for _ in range(20):
+        torch.cuda.synchronize()
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        singles.append(a.elapsed_time(b))
+    assert kg.kg_status() == kg.KG_OK
+    singles.sort()
+    return {"workload": DESCR["worked"], "us_per_call_back_to_back": round(ms * 1e3, 2),
+            "us_single_call_events": round(singles[len(singles) // 2] * 1e3, 2),
+            "flops": c.flops, "bound": "launch latency"}
 
 
 if __name__ == "__main__":

@@ -17,29 +17,33 @@ KG_OK = 0
 KG_ERR_NULL, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_DTYPE = -1, -2, -3, -4
 KG_ERR_ALIGN, KG_ERR_ALIAS, KG_ERR_UNSUPPORTED, KG_ERR_HIP, KG_ERR_KSUM = -5, -6, -7, -8, -9
 KG_ERR_SPLIT = -10
+KG_ERR_SCALE_ROWS = -11
+KG_ERR_SCALE_RANGE = -12
 KG_SRC_BF16, KG_SRC_E4M3_1X128 = 0, 1
 ERROR_NAMES = {0: "KG_OK", -1: "KG_ERR_NULL", -2: "KG_ERR_SHAPE", -3: "KG_ERR_GRAN",
                -4: "KG_ERR_DTYPE", -5: "KG_ERR_ALIGN", -6: "KG_ERR_ALIAS",
                -7: "KG_ERR_UNSUPPORTED", -8: "KG_ERR_HIP", -9: "KG_ERR_KSUM",
-               -10: "KG_ERR_SPLIT"}
+               -10: "KG_ERR_SPLIT", -11: "KG_ERR_SCALE_ROWS",
+               -12: "KG_ERR_SCALE_RANGE"}
 
 # name -> (restype, argtypes): the symbols include/kgwgrad.h declares
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
 SIGNATURES = {
-    "kg_wgrad": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32,
-                        _vp]),
-    "kg_wgrad_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32,
-                           _vp, _i64, _vp]),
+    "kg_wgrad": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32,
+                        _i32, _vp]),
+    "kg_wgrad_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32,
+                           _i32, _vp, _i64, _vp]),
     "kg_wgrad_nt": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64,
-                           _i32, _i32, _vp]),
+                           _i64, _i32, _i32, _vp]),
     "kg_wgrad_nt_ws": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
-                              _i64, _i32, _i32, _vp, _i64, _vp]),
+                              _i64, _i64, _i32, _i32, _vp, _i64, _vp]),
     "kg_wgrad_workspace_bytes": (_i64, []),
     "kg_wgrad_workspace_flag_bytes": (_i64, []),
     "kg_status": (_i32, [_vp]),
     "kg_debug_offsets": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "kg_max_groups": (_i32, []),
-    "kg_requant": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "kg_requant": (_i32, [_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _i64,
+                          _vp]),
     "kg_dgrad": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp]),
 }
 
@@ -107,11 +111,19 @@ def _scale_dtype_ok(t, dtype):
     return t.dtype == (torch.float32 if dtype == KG_E4M3_F32SCALE else torch.uint8)
 
 
+def scale_rows_of(sa, sb):
+    """The scale_rows argument: rows that both scale tensors hold (0 without scales).
+    The library checks it against the rows the experts' blocks need."""
+    if sa is None or sb is None:
+        return 0
+    return int(min(sa.shape[0], sb.shape[0]))
+
+
 def _check_wgrad(A_cols, B_cols, sa, sb, C, D, ks, K_total, gran_k, dtype, A, B, kmajor):
     """Shapes and dtypes of a kg_wgrad / kg_wgrad_nt call (the C ABI takes plain
     pointers and cannot see extents). The scale tensors need at least
-    ceil(K_total / gran_k) rows (their exact count, sum ceil(ks / gran_k), would
-    take ks off the GPU)."""
+    ceil(K_total / gran_k) rows here; their row count goes to the library, which
+    checks the exact need, sum ceil(ks / gran_k), on the device."""
     import torch
     base = dtype & 0xFF
     _need(base in (KG_E4M3_F32SCALE, KG_E4M3_UE8M0, KG_BF16), f"unknown dtype {base}")
@@ -148,19 +160,25 @@ def _check_wgrad(A_cols, B_cols, sa, sb, C, D, ks, K_total, gran_k, dtype, A, B,
     _tensors_on_gpu(D, A=A, B=B, sa=sa, sb=sb, C=C, ks=ks)
 
 
-def kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream=None):
-    """Call kg_wgrad with torch device tensors (or None); returns the status code."""
+def kg_wgrad_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream=None,
+                 scale_rows=None):
+    """Call kg_wgrad with torch device tensors (or None); returns the status code.
+    scale_rows defaults to the rows the scale tensors hold."""
+    if scale_rows is None:
+        scale_rows = scale_rows_of(sa, sb)
     return lib().kg_wgrad(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D), _ptr(ks),
-                          int(G), int(M), int(N), int(K_total), int(gran_k), int(dtype),
-                          _stream(stream))
+                          int(G), int(M), int(N), int(K_total), int(scale_rows), int(gran_k),
+                          int(dtype), _stream(stream))
 
 
 def kg_wgrad_ws_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, ws, ws_bytes,
-                    stream=None):
+                    stream=None, scale_rows=None):
     """Call kg_wgrad_ws with torch device tensors (or None); returns the status code."""
+    if scale_rows is None:
+        scale_rows = scale_rows_of(sa, sb)
     return lib().kg_wgrad_ws(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D), _ptr(ks),
-                             int(G), int(M), int(N), int(K_total), int(gran_k), int(dtype),
-                             _ptr(ws), int(ws_bytes), _stream(stream))
+                             int(G), int(M), int(N), int(K_total), int(scale_rows), int(gran_k),
+                             int(dtype), _ptr(ws), int(ws_bytes), _stream(stream))
 
 
 def kg_wgrad_workspace_bytes():
@@ -212,15 +230,18 @@ def kg_wgrad(A, sa, B, sb, C, D, ks, gran_k, dtype, K_total=None, stream=None, w
 
 
 def kg_wgrad_nt_raw(At, lda, sa, Bt, ldb, sb, C, D, ks, G, M, N, K_total, gran_k, dtype,
-                    ws=None, ws_bytes=0, stream=None):
+                    ws=None, ws_bytes=0, stream=None, scale_rows=None):
     """Call kg_wgrad_nt (or kg_wgrad_nt_ws when `ws` is given); returns the status."""
+    if scale_rows is None:
+        scale_rows = scale_rows_of(sa, sb)
     if ws is None:
         return lib().kg_wgrad_nt(_ptr(At), int(lda), _ptr(sa), _ptr(Bt), int(ldb), _ptr(sb),
                                  _ptr(C), _ptr(D), _ptr(ks), int(G), int(M), int(N), int(K_total),
-                                 int(gran_k), int(dtype), _stream(stream))
+                                 int(scale_rows), int(gran_k), int(dtype), _stream(stream))
     return lib().kg_wgrad_nt_ws(_ptr(At), int(lda), _ptr(sa), _ptr(Bt), int(ldb), _ptr(sb),
                                 _ptr(C), _ptr(D), _ptr(ks), int(G), int(M), int(N), int(K_total),
-                                int(gran_k), int(dtype), _ptr(ws), int(ws_bytes), _stream(stream))
+                                int(scale_rows), int(gran_k), int(dtype), _ptr(ws), int(ws_bytes),
+                                _stream(stream))
 
 
 def kg_wgrad_nt(At, sa, Bt, sb, C, D, ks, gran_k, dtype, stream=None, workspace=None):
@@ -267,10 +288,15 @@ def kg_max_groups():
     return lib().kg_max_groups()
 
 
-def kg_requant_raw(X, xs, ks, G, H, K_total, gran_k, src, scale_kind, Q, S, stream=None):
-    """Call kg_requant with torch device tensors (or None); returns the status code."""
+def kg_requant_raw(X, xs, ks, G, H, K_total, gran_k, src, scale_kind, Q, S, stream=None,
+                   s_rows=None):
+    """Call kg_requant with torch device tensors (or None); returns the status code.
+    s_rows defaults to the rows S holds."""
+    if s_rows is None:
+        s_rows = 0 if S is None else S.shape[0]
     return lib().kg_requant(_ptr(X), _ptr(xs), _ptr(ks), int(G), int(H), int(K_total), int(gran_k),
-                            int(src), int(scale_kind), _ptr(Q), _ptr(S), _stream(stream))
+                            int(src), int(scale_kind), _ptr(Q), _ptr(S), int(s_rows),
+                            _stream(stream))
 
 
 def kg_requant(X, xs, ks, gran_k, scale_kind, nblk, Q=None, S=None, stream=None):

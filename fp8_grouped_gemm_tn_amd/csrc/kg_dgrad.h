@@ -275,7 +275,8 @@ __global__ __launch_bounds__(DC::THREADS, 1) void kg_dgrad_kernel(DParams p) {
     store_tile_gen<typename DC::Epi, false, OUTB>(smem, acc,
                                            OUTB ? (float*)((unsigned short*)p.D + row0 * p.N + n0)
                                                 : p.D + row0 * p.N + n0,
-                                           p.N, rows, DC::BN, nullptr, 0, nullptr, 0);
+                                           p.N, rows, DC::BN, nullptr, 0, nullptr, nullptr, 0,
+                                           0);
   }
 }
 

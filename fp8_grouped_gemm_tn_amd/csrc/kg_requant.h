@@ -47,6 +47,7 @@ struct QParams {
   const int32_t* ks;
   int G, H;
   int64_t K_total;
+  int64_t s_rows;  // rows of S
   int gran;
 };
 
@@ -109,8 +110,10 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
   __shared__ int32_t wsum_b[kMaxWaves];
   __shared__ float red[kQThreads / 64][kQCols];
   Sched s = sched_carve(smem, p.G);
-  if (sched_build<kQThreads>(p.ks, p.G, p.gran, p.K_total, s, wsum_k, wsum_b) != KG_OK) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
+  const int sched_rc =
+      sched_build<kQThreads>(p.ks, p.G, p.gran, p.K_total, s, wsum_k, wsum_b, false, p.s_rows);
+  if (sched_rc != KG_OK) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = sched_rc;
     return;
   }
   constexpr int SLABS = GRAN == 32 ? 4 : 1;
@@ -279,7 +282,7 @@ using namespace kg;
 
 extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int G, int H,
                           int64_t K_total, int gran_k, int src, int scale_kind, void* Q, void* S,
-                          void* stream) {
+                          int64_t s_rows, void* stream) {
   if (src != KG_SRC_BF16 && src != KG_SRC_E4M3_1X128) return KG_ERR_DTYPE;
   if (scale_kind != KG_E4M3_F32SCALE && scale_kind != KG_E4M3_UE8M0) return KG_ERR_DTYPE;
   if (G < 0 || H < 0 || K_total < 0) return KG_ERR_SHAPE;
@@ -291,6 +294,10 @@ extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int
   if (K_total > 0 && (X == nullptr || Q == nullptr || S == nullptr)) return KG_ERR_NULL;
   if (src == KG_SRC_E4M3_1X128 && K_total > 0 && xs == nullptr) return KG_ERR_NULL;
   if (src == KG_SRC_BF16 && xs != nullptr) return KG_ERR_NULL;
+  // S needs a row per block: at least ceil(K_total / gran_k) (the exact count,
+  // sum ceil(ks[g] / gran_k), is checked on the device)
+  if (K_total > 0 && (s_rows < 0 || s_rows < K_total / gran_k + (K_total % gran_k != 0)))
+    return KG_ERR_SCALE_ROWS;
   if (H % 128 != 0) return KG_ERR_ALIGN;
   if (((uintptr_t)X & 15) || ((uintptr_t)Q & 15) || ((uintptr_t)S & 15) || ((uintptr_t)xs & 3) ||
       ((uintptr_t)ks & 3))
@@ -302,7 +309,11 @@ extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
   };
-  if (overlap(X, xbytes, Q, qbytes) || overlap(S, 1, Q, qbytes) || overlap(X, xbytes, S, 1))
+  const int64_t srows = s_rows < K_total ? s_rows : K_total;
+  const size_t sbytes = (size_t)srows * H * (scale_kind == KG_E4M3_F32SCALE ? 4 : 1);
+  if (overlap(X, xbytes, Q, qbytes) || overlap(S, sbytes, Q, qbytes) ||
+      overlap(X, xbytes, S, sbytes) || overlap(xs, (size_t)K_total * (H / 128) * 4, S, sbytes) ||
+      overlap(ks, (size_t)G * 4, S, sbytes) || overlap(ks, (size_t)G * 4, Q, qbytes))
     return KG_ERR_ALIAS;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -318,6 +329,7 @@ extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int
   p.G = G;
   p.H = H;
   p.K_total = K_total;
+  p.s_rows = s_rows;
   p.gran = gran_k;
   // items are not known on the host (they depend on ks): enough persistent
   // workgroups for the largest case, eight per CU

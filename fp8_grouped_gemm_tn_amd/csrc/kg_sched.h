@@ -61,13 +61,16 @@ __device__ inline T wave_incl_scan(T v) {
   return v;
 }
 
-// Block-wide: load ks, check counts, scan offsets, order experts. Returns KG_OK
-// or KG_ERR_KSUM; every thread returns the same value. THREADS is the block size
+// Block-wide: load ks, check counts, scan offsets, order experts. Returns KG_OK,
+// KG_ERR_KSUM (a negative count, or counts that do not add up to K_total) or
+// KG_ERR_SCALE_ROWS (more blocks than max_blocks, the rows the caller's scale
+// tensors hold); every thread returns the same value. THREADS is the block size
 // (256 or 512); each thread owns kMaxGroups / THREADS consecutive experts. spread:
 // place the empty experts between the others (else last).
 template <int THREADS>
 __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, Sched s,
-                           int64_t* wsum_k, int32_t* wsum_b, bool spread = false) {
+                           int64_t* wsum_k, int32_t* wsum_b, bool spread = false,
+                           int64_t max_blocks = INT64_MAX) {
   constexpr int E = kMaxGroups / THREADS, W = THREADS / 64;
   static_assert(E * THREADS == kMaxGroups && W <= kMaxWaves, "block size");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -80,7 +83,8 @@ __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, 
   for (int e = 0; e < E; ++e) {
     kv[e] = g0 + e < G ? ks[g0 + e] : 0;
     neg |= kv[e] < 0;
-    bv[e] = kv[e] > 0 ? (kv[e] + gran - 1) / gran : 0;
+    // ceil(kv / gran) without forming kv + gran - 1 (which overflows near 2^31)
+    bv[e] = kv[e] > 0 ? kv[e] / gran + (kv[e] % gran != 0) : 0;
     if (g0 + e < G) s.ks[g0 + e] = kv[e];
     own_k += kv[e];
     own_b += bv[e];
@@ -113,10 +117,15 @@ __device__ int sched_build(const int32_t* ks, int G, int gran, int64_t K_total, 
     s.off[0] = 0;
     s.boff[0] = 0;
   }
-  int64_t total = 0;
-  for (int i = 0; i < W; ++i) total += wsum_k[i];
+  int64_t total = 0, total_b = 0;
+  for (int i = 0; i < W; ++i) {
+    total += wsum_k[i];
+    total_b += wsum_b[i];
+  }
   __syncthreads();
   if (any_neg || total != K_total) return KG_ERR_KSUM;
+  // (with consistent counts, total_b <= K_total / gran + G fits the int32 scan)
+  if (total_b > max_blocks) return KG_ERR_SCALE_ROWS;
   // When G is small: experts with tokens longest first (ties by index), and the empty
   // ones (fill items: stores only) after them or, with spread, spread evenly between
   // them, so that their stores run beside other workgroups' GEMM tiles rather than

@@ -72,12 +72,14 @@ struct Params {
   int G, M, N;
 
   int64_t K_total;
+  int64_t scale_rows;     // rows of sa and sb (INT64_MAX for bf16: no scales)
   uint32_t lda_b, ldb_b;  // K-major kernels: row strides of A and B in bytes
   int gran;  // tokens per scale row
   int tiles_m, tiles_n;
-  // stream-K mode when ws != nullptr: per-workgroup partial tiles and ready flags
+  // stream-K mode when ws != nullptr: two partial-tile slots per workgroup and an
+  // arrival counter per workgroup (for the cut tile whose first stage it holds)
   float* ws;
-  int* wsflag;
+  int* wscnt;
 };
 
 // Tile configuration: BM x BN per workgroup, THREADS / 64 waves as WAVES_M x WAVES_N,
@@ -394,8 +396,8 @@ __device__ inline void epi_coords(int idx, int ph, int pc, int m0, int n0, int& 
 // plus an optional addend tile `add` (C), plus `nparts` partial tiles (stream-K),
 // added in that order, stored to `dst`. Tiles are row-major from the tile origin:
 // dst and add with row stride `ld` floats (rows and columns past rows x cols are
-// not stored; addend bytes past add_bytes read as zero), partial q at parts + q *
-// BM * BN with row stride BN. Per pass (EPI_ROWS rows x two 16-column sub-tiles of
+// not stored; addend bytes past add_bytes read as zero), partial 0 at parts0 and
+// partial q > 0 at parts + (q - 1) * part_stride floats, each with row stride BN. Per pass (EPI_ROWS rows x two 16-column sub-tiles of
 // every wave column): the waves owning the pass's rows write their accumulators to
 // LDS while the addend goes global -> LDS by buffer loads; every thread adds the
 // addend to its float4 runs, then each partial in turn through the same LDS
@@ -405,7 +407,8 @@ __device__ inline void epi_coords(int idx, int ph, int pc, int m0, int n0, int& 
 template <class CF, bool SYS_STORE = false, bool OUTB = false>
 __device__ inline void store_tile_gen(unsigned char* lds, const v4f (&acc)[CF::NI][CF::NJ],
                                       float* dst, int ld, int rows, int cols, const float* add,
-                                      uint32_t add_bytes, const float* parts, int nparts) {
+                                      uint32_t add_bytes, const float* parts0, const float* parts,
+                                      size_t part_stride, int nparts) {
   static_assert(!(OUTB && SYS_STORE), "bf16 output is stored with ordinary stores");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
@@ -452,7 +455,8 @@ __device__ inline void store_tile_gen(unsigned char* lds, const v4f (&acc)[CF::N
             *(v4f*)(e + row * CF::EPI_STRIDE + lcol) += *(const v4f*)(cl + row * CF::EPI_COLS + lcol);
           }
         }
-        const v4i rp = make_rsrc(parts + (size_t)pq * CF::BM * CF::BN, CF::BM * CF::BN * 4);
+        const v4i rp = make_rsrc(pq == 0 ? parts0 : parts + (size_t)(pq - 1) * part_stride,
+                                 CF::BM * CF::BN * 4);
         __syncthreads();  // the previous addend in LDS is no longer read
         for (int k = w; k < CF::EPI_LOADS; k += CF::WAVES) {
           int row, lcol, m, n;
@@ -483,16 +487,17 @@ __device__ inline void store_tile_gen(unsigned char* lds, const v4f (&acc)[CF::N
   }
 }
 
-// acc + C + partial tiles -> D for expert g's tile at (m0, n0) (stream-K mode).
+// acc + C + partial tiles -> D for expert g's tile at (m0, n0) (stream-K mode; the
+// partial tiles as for store_tile_gen).
 template <class CF>
 __device__ inline void store_tile_parts(const Params& p, unsigned char* lds, int g, int m0, int n0,
-                                        const v4f (&acc)[CF::NI][CF::NJ], const float* parts,
-                                        int nparts) {
+                                        const v4f (&acc)[CF::NI][CF::NJ], const float* parts0,
+                                        const float* parts, size_t part_stride, int nparts) {
   const size_t org = (size_t)g * p.M * p.N + (size_t)m0 * p.N + n0;
   // C from the tile origin to the end of the expert's matrix
   const uint32_t cbytes = (uint32_t)((((size_t)(p.M - m0) - 1) * p.N + (p.N - n0)) * 4);
   store_tile_gen<CF>(lds, acc, p.D + org, p.N, p.M - m0, p.N - n0, p.C ? p.C + org : nullptr,
-                     cbytes, parts, nparts);
+                     cbytes, parts0, parts, part_stride, nparts);
 }
 
 // acc (this lane's 4 rows x 1 column of each 16x16 sub-tile) + C -> D. Per pass:
@@ -728,11 +733,6 @@ __device__ inline v8bf widen8(v2i x, float scale) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// E8M0 byte -> fp32 scale 2^(e-127); 255 is NaN.
-__device__ inline float e8m0_scale(int e) {
-  return e == 255 ? __builtin_nanf("") : __builtin_ldexpf(1.0f, e - 127);
-}
-
 // Fragment readers. `base` is this lane's base in the operand: token-major, its row
 // of the transposing read; K-major, its channel row of the wave's first sub-tile
 // plus its first token byte (the K-major offsets below are then immediates). Both
@@ -798,7 +798,7 @@ __device__ inline v8i rdf8n(const unsigned char* base, int i) {
 }
 
 template <class CF>
-__device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
+__device__ __forceinline__ void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
@@ -838,7 +838,7 @@ __device__ inline void compute_fast_f32s(const unsigned char* st, v4f (&acc)[CF:
 // fast fp8 + E8M0: the scaled MFMA takes lane 16b+i's exponent for (row i, 32-token
 // block b) and accumulates directly.
 template <class CF>
-__device__ inline void compute_fast_e8m0(const unsigned char* st, int gran,
+__device__ __forceinline__ void compute_fast_e8m0(const unsigned char* st, int gran,
                                          v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
@@ -878,7 +878,7 @@ __device__ inline void compute_fast_e8m0(const unsigned char* st, int gran,
 // stage (PROMOTE) the finished partial sum of sub-tile (i, jn) is rescaled by
 // sa (x) sb on the VALU, one sub-tile behind the MFMAs, and part is cleared.
 template <class CF, bool PROMOTE>
-__device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ],
+__device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ],
                                             v4f (&part)[CF::NI][CF::NJ]) {
   constexpr int KK = CF::TK / 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -954,7 +954,7 @@ __device__ inline void compute_precise_f32s(const unsigned char* st, v4f (&acc)[
 // fp8; fast: the 16x16x32 fp8 MFMA, whose operand is this lane's 8 tokens as they
 // come from the transposing read.
 template <class CF, bool FAST>
-__device__ inline void compute_f32s32(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
+__device__ __forceinline__ void compute_f32s32(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
   constexpr int KK = CF::TK / 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
@@ -1014,11 +1014,92 @@ __device__ inline void compute_f32s32(const unsigned char* st, v4f (&acc)[CF::NI
   rescale(CF::NI - 1, CF::NJ - 1, KK - 1, prev);
 }
 
-// precise fp8 + E8M0: every fragment is widened with its power-of-two scale
-// (exact), then the bf16 MFMAs accumulate straight into acc.
+// UE8M0 exponents whose scale 2^(e-127) can be folded into the bf16 widening exactly:
+// every scaled e4m3 magnitude (2^-9 .. 448) then stays a normal bf16 (2^-126 .. 2^128).
+constexpr int kE8FoldLo = 10, kE8FoldHi = 246;
+
+// True if a byte of x lies outside [kE8FoldLo, kE8FoldHi]: a byte below 10, or one
+// whose complement is below 9. Each test is the per-byte borrow test "(x - n) & ~x"
+// on the bytes' top bits, exact as a whole-word answer for n <= 128.
+__device__ inline bool e8_outside_fold(uint32_t x) {
+  const uint32_t y = ~x;
+  return (((x - 0x0A0A0A0Au) & y) | ((y - 0x09090909u) & x)) & 0x80808080u;
+}
+
+// 2^(e-127-c) as fp32, for 1 <= e - c <= 254: the exponent field e - c. cb = -c << 23
+// (one shift-and-add).
+__device__ inline float e8_pow2(uint32_t e, uint32_t cb) { return __uint_as_float((e << 23) + cb); }
+
+// Lane-wise minimum / maximum over the wave.
+__device__ inline int wave_min(int v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v = min(v, __shfl_xor(v, d, 64));
+  return v;
+}
+__device__ inline int wave_max(int v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v = max(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+// The widening and bf16 MFMAs of one E8M0 stage with A's scales folded as
+// 2^(ea - c - 127) and B's as 2^(eb + c - 127), c the shift of the step's scale row
+// (ca[row] = -c << 23, cb[row] = c << 23).
 template <class CF>
-__device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
-                                            v4f (&acc)[CF::NI][CF::NJ]) {
+__device__ __forceinline__ void e8m0_fold_stage(const unsigned char* aBase, const unsigned char* bBase,
+                                                const unsigned char* sSa, const unsigned char* sSb,
+                                                int g32, const uint32_t (&ca)[CF::TK / 32],
+                                                const uint32_t (&cb)[CF::TK / 32],
+                                                v4f (&acc)[CF::NI][CF::NJ]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
+  constexpr int KK = CF::TK / 32;
+  v8bf af[CF::NI][KK];
+#pragma unroll
+  for (int i = 0; i < CF::NI; ++i)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const float sc = e8_pow2(sSa[g32 * kk * CF::BM + wm * CF::WM + 16 * i + j], ca[kk]);
+      af[i][kk] = widen8(rd8<CF, CF::ROWA>(aBase, i, kk), sc);
+    }
+  v2i rnext[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, 0, kk);
+#pragma unroll
+  for (int jn = 0; jn < CF::NJ; ++jn) {
+    v8bf bf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const float sc = e8_pow2(sSb[g32 * kk * CF::BN + wn * CF::WN + 16 * jn + j], cb[kk]);
+      bf[kk] = widen8(rnext[kk], sc);
+    }
+    if (jn + 1 < CF::NJ) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, jn + 1, kk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i][kk], bf[kk], acc[i][jn]);
+  }
+}
+
+// precise fp8 + E8M0: each fragment is widened with its power-of-two scale (exact) and
+// the bf16 MFMAs accumulate straight into acc. The scaled values must be normal bf16s:
+// the wave first checks the exponents it uses in the stage (4 per dword read; channels
+// past M or N, mlim / nlim from the tile origin, and scale rows past srows, which hold
+// no token of the expert, are not looked at). If some lie outside [kE8FoldLo,
+// kE8FoldHi], then for each scale row (block) A's scales are folded as 2^(ea-c-127) and
+// B's as 2^(eb+c-127) with one shift c that brings the row's exponents inside (the
+// products keep 2^(ea+eb-254)). No such c exists only when the wave's exponents of one
+// operand in one block span more than 236, or the block's scale products leave fp32's
+// range (2^(ea+eb-254) above 2^238 or below 2^-234), or a scale is NaN (255): that
+// block then takes the nearest shift and KG_ERR_SCALE_RANGE is reported.
+template <class CF>
+__device__ __forceinline__ void compute_precise_e8m0(const unsigned char* st, int gran, int srows,
+                                                     int mlim, int nlim,
+                                                     v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
@@ -1033,34 +1114,65 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
   // 32-token run kk of the stage uses scale row kk (gran 32) or row 0 (gran 128)
   const int g32 = gran == 32 ? 1 : 0;
   constexpr int KK = CF::TK / 32;
-  v8bf af[CF::NI][KK];
+  // the wave's WM exponents of A and WN of B in a scale row: a dword per lane (M and N
+  // are multiples of 16, so a dword never straddles the tile's edge)
+  constexpr int DA = CF::WM / 4, DB = CF::WN / 4;
+  static_assert(DA + DB <= 64, "one dword per lane covers a scale row");
+  const int nrow = g32 ? srows : 1;
+  auto row_dword = [&](int row, uint32_t& x) __attribute__((always_inline)) {
+    const bool is_a = lane < DA;
+    const int ch = is_a ? wm * CF::WM + 4 * lane : wn * CF::WN + 4 * (lane - DA);
+    x = is_a ? *(const uint32_t*)(sSa + row * CF::BM + ch) : *(const uint32_t*)(sSb + row * CF::BN + ch);
+    return lane < DA + DB && ch < (is_a ? mlim : nlim);
+  };
+  bool outside = false;
 #pragma unroll
-  for (int i = 0; i < CF::NI; ++i)
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const float s = e8m0_scale(sSa[g32 * kk * CF::BM + wm * CF::WM + 16 * i + j]);
-      af[i][kk] = widen8(rd8<CF, CF::ROWA>(aBase, i, kk), s);
-    }
-  v2i rnext[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, 0, kk);
-#pragma unroll
-  for (int jn = 0; jn < CF::NJ; ++jn) {
-    v8bf bf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const float s = e8m0_scale(sSb[g32 * kk * CF::BN + wn * CF::WN + 16 * jn + j]);
-      bf[kk] = widen8(rnext[kk], s);
-    }
-    if (jn + 1 < CF::NJ) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, jn + 1, kk);
-    }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int i = 0; i < CF::NI; ++i) acc[i][jn] = mfma_bf16(af[i][kk], bf[kk], acc[i][jn]);
+  for (int row = 0; row < KK; ++row) {
+    uint32_t x;
+    if (row < nrow && row_dword(row, x)) outside |= e8_outside_fold(x);
   }
+  uint32_t ca[KK], cb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) ca[kk] = cb[kk] = 0;
+  if (__builtin_amdgcn_ballot_w64(outside) != 0) {
+#pragma unroll
+    for (int row = 0; row < KK; ++row) {
+      if (row >= nrow) break;
+      // the row's exponent ranges and shift
+      int amin = 255, amax = 0, bmin = 255, bmax = 0;
+      uint32_t x;
+      if (row_dword(row, x)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = (x >> (8 * r)) & 0xFF;
+          if (lane < DA) {
+            amin = min(amin, e);
+            amax = max(amax, e);
+          } else {
+            bmin = min(bmin, e);
+            bmax = max(bmax, e);
+          }
+        }
+      }
+      amin = wave_min(amin), amax = wave_max(amax), bmin = wave_min(bmin), bmax = wave_max(bmax);
+      const int c_lo = max(amax - kE8FoldHi, kE8FoldLo - bmin);
+      const int c_hi = min(amin - kE8FoldLo, kE8FoldHi - bmax);
+      int c = c_lo;
+      if (c_lo > c_hi || amax == 255 || bmax == 255) {
+        // no exact shift (or a NaN scale): avoid overflow first
+        c = max(min(c_lo, kE8FoldHi - bmax), amax - kE8FoldHi);
+        if (lane == 0) kgwgrad_status_word = KG_ERR_SCALE_RANGE;
+      }
+      c = uniform(c);
+      ca[row] = (uint32_t)(-c) << 23;
+      cb[row] = (uint32_t)c << 23;
+    }
+    if (!g32) {
+#pragma unroll
+      for (int kk = 1; kk < KK; ++kk) ca[kk] = ca[0], cb[kk] = cb[0];
+    }
+  }
+  e8m0_fold_stage<CF>(aBase, bBase, sSa, sSb, g32, ca, cb, acc);
 }
 
 // bf16: lane 4r+c of a 16-lane group names token row r, halfwords 4c..4c+3; lane
@@ -1069,7 +1181,7 @@ __device__ inline void compute_precise_e8m0(const unsigned char* st, int gran,
 // K-major: lane (q, j) reads tokens 32kk + 8q .. +7 of channel row j in one 16-byte
 // read (A and B alike, so the MFMA pairs the same tokens).
 template <class CF>
-__device__ inline void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
+__device__ __forceinline__ void compute_bf16(const unsigned char* st, v4f (&acc)[CF::NI][CF::NJ]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
@@ -1142,9 +1254,13 @@ __device__ inline v8bf frag_b16(const unsigned char* p) {
   return v8bf{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 }
 
+// E8M0: srows, the scale rows of the stage that belong to the expert's tokens; mlim and
+// nlim, the tile's channels inside M and N
 template <int KIND, bool FAST, class CF>
-__device__ inline void compute_stage(const unsigned char* st, int gran, bool promote,
-                                     v4f (&acc)[CF::NI][CF::NJ], v4f (&part)[CF::NI][CF::NJ]) {
+__device__ __forceinline__ void compute_stage(const unsigned char* st, int gran, bool promote,
+                                              int srows, int mlim, int nlim,
+                                              v4f (&acc)[CF::NI][CF::NJ],
+                                              v4f (&part)[CF::NI][CF::NJ]) {
   if constexpr (KIND == BF16) {
     compute_bf16<CF>(st, acc);
   } else if constexpr (KIND == F32S32) {
@@ -1159,7 +1275,7 @@ __device__ inline void compute_stage(const unsigned char* st, int gran, bool pro
   } else if constexpr (FAST) {
     compute_fast_e8m0<CF>(st, gran, acc);
   } else {
-    compute_precise_e8m0<CF>(st, gran, acc);
+    compute_precise_e8m0<CF>(st, gran, srows, mlim, nlim, acc);
   }
 }
 
@@ -1170,7 +1286,7 @@ __device__ inline void compute_stage(const unsigned char* st, int gran, bool pro
 // expert. The stage buffers must be free on entry (callers barrier first); on
 // return every load of the unit has completed (LDS may still be read by other waves).
 template <int KIND, bool FAST, class CF>
-__device__ inline void item_gemm(const Params& p, const LoadOffsets<CF>& lo, unsigned char* smem,
+__device__ __forceinline__ void item_gemm(const Params& p, const LoadOffsets<CF>& lo, unsigned char* smem,
                                  int64_t t_begin, int Kg, int boff_g, int m0, int n0, int nk,
                                  int kb0, int kb1, v4f (&acc)[CF::NI][CF::NJ]) {
   const int n = kb1 - kb0;  // stages of this unit
@@ -1269,7 +1385,10 @@ __device__ inline void item_gemm(const Params& p, const LoadOffsets<CF>& lo, uns
     }
     const int kb = kb0 + j;
     const bool promote = ((kb + 1) % (128 / CF::TK) == 0) || kb + 1 == nk;
-    compute_stage<KIND, FAST, CF>(smem + buf * CF::STAGE, p.gran, promote, acc, part);
+    // E8M0, gran 32: scale rows of the stage's tokens (the last stage may hold fewer)
+    const int srows = KIND == E8M0 ? (min(CF::TK, Kg - CF::TK * kb) + 31) / 32 : 0;
+    compute_stage<KIND, FAST, CF>(smem + buf * CF::STAGE, p.gran, promote, srows, p.M - m0,
+                                  p.N - n0, acc, part);
     buf = buf + 1 == CF::NS ? 0 : buf + 1;
   }
 }
@@ -1282,16 +1401,13 @@ __device__ inline void zero_acc(v4f (&acc)[CF::NI][CF::NJ]) {
     for (int jn = 0; jn < CF::NJ; ++jn) acc[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
-// Split-tile partial sums (stream-K mode): slot c holds workgroup c's partial of the
-// tile it starts inside, a row-major BM x BN tile.
+// Split-tile partial sums (stream-K mode): workgroup c owns slots 2c (the cut tile its
+// range starts with) and 2c + 1 (the cut tile its range ends with, when that is
+// another one), row-major BM x BN tiles.
 template <class CF>
-__device__ inline float* partial_slot(const Params& p, int c) {
-  return p.ws + (size_t)c * CF::BM * CF::BN;
+__device__ inline float* partial_slot(const Params& p, int s) {
+  return p.ws + (size_t)s * CF::BM * CF::BN;
 }
-
-// Longest wait for a partial (s_sleep 2 units each): a missing partial ends the wait
-// with KG_ERR_SPLIT in the status word instead of a hang.
-constexpr int kSpinLimit = 1 << 22;
 
 template <int KIND, bool FAST, class CF>
 __device__ void split_tiles(const Params& p, const Sched& s, unsigned char* smem,
@@ -1310,9 +1426,10 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   // Multi-round whole-tile launches spread the empty experts' fill tiles between the
   // GEMM tiles; stream-K, and a launch whose items all run at once, take the live
   // experts first and the fill tiles last.
-  if (sched_build<CF::THREADS>(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b,
-                               !SPLIT && !one_round) != KG_OK) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = KG_ERR_KSUM;
+  const int sched_rc = sched_build<CF::THREADS>(p.ks, p.G, gran, p.K_total, s, wsum_k, wsum_b,
+                                                !SPLIT && !one_round, p.scale_rows);
+  if (sched_rc != KG_OK) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = sched_rc;
     return;
   }
   // Workgroup b runs on XCD b % 8. With several rounds of items, each XCD takes a
@@ -1368,16 +1485,26 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
 }
 
 // Stream-K mode (few tiles): the stages of all non-empty tiles, in item order, form
-// one line of length W; workgroup `slot` takes [W*slot/grid, W*(slot+1)/grid). A
-// tile cut by range ends is summed by the workgroup that holds its first stage: it
-// finishes that unit last in its range, and adds, in workgroup order, the partials
-// that the following workgroups wrote from the first unit of their ranges (so the
-// result does not depend on timing). Empty experts' fill tiles follow.
+// one line of length W; workgroup `slot` takes [W*slot/grid, W*(slot+1)/grid). A tile
+// that lies inside one range is finished by that workgroup. A tile cut by range ends
+// has parts in workgroups c0 .. c1: every part writes its partial to its own slot
+// (write-through stores), waits for them, and adds one to the tile's arrival counter
+// (counter c0). The part that arrives last (the counter reached c1 - c0 + 1) resets the
+// counter and adds C and all the partials in workgroup order, so the result does not
+// depend on timing, and no workgroup ever waits for another: the mode needs neither
+// co-resident workgroups nor an idle GPU. Empty experts' fill tiles follow.
+//
+// Visibility of the partials: a part's stores bypass the caches (sc0 sc1) and the wave
+// waits for their completion (vmcnt) before the workgroup barrier that precedes its
+// counter increment; the last part reads the partials with loads that bypass the
+// caches too, after its own increment has returned. Every increment thus follows the
+// completion of its part's stores, and the reads follow every increment, without a
+// cache-wide write-back or invalidation.
 template <int KIND, bool FAST, class CF>
 __device__ void split_tiles(const Params& p, const Sched& s, unsigned char* smem,
                             const LoadOffsets<CF>& lo, int slot) {
   __shared__ int64_t sk_cum[kMaxSplitGroups + 1];
-  __shared__ int sk_flag;
+  __shared__ int sk_last;
   const int T = p.tiles_m * p.tiles_n;
   const int grid = gridDim.x;
   if (threadIdx.x == 0) {
@@ -1390,11 +1517,10 @@ __device__ void split_tiles(const Params& p, const Sched& s, unsigned char* smem
   }
   __syncthreads();
   const int64_t W = sk_cum[p.G];
-  // no range is empty: with fewer stages than workgroups, workgroup c < W takes
-  // stage c and the rest take none (they come last, so never sit between a tile's
-  // first workgroup and its later ones)
+  // with fewer stages than workgroups, workgroup c < W takes stage c and the rest none
   auto range_lo = [&](int c) { return W >= grid ? W * c / grid : (int64_t)min(c, (int)W); };
   const int64_t lo_pos = range_lo(slot), hi_pos = range_lo(slot + 1);
+  constexpr size_t kTile = (size_t)CF::BM * CF::BN;
   for (int64_t pos = lo_pos; pos < hi_pos;) {
     int r = 0;
     while (sk_cum[r + 1] <= pos) ++r;
@@ -1414,42 +1540,34 @@ __device__ void split_tiles(const Params& p, const Sched& s, unsigned char* smem
     zero_acc<CF>(acc);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the previous unit's stores
     item_gemm<KIND, FAST, CF>(p, lo, smem, t_begin, Kg, boff_g, m0, n0, nk, kb0, kb1, acc);
-    if (kb0 > 0) {
-      // a later part of a cut tile: publish it for the tile's first workgroup
-      // written through to memory, so no cache-wide write-back is needed
-      store_tile_gen<CF, true>(smem, acc, partial_slot<CF>(p, slot), CF::BN, CF::BM, CF::BN,
-                               nullptr, 0, nullptr, 0);
+    const int64_t tile_lo = sk_cum[r] + (int64_t)t * nk, tile_hi = tile_lo + nk;
+    if (tile_lo >= lo_pos && tile_hi <= hi_pos) {
+      store_tile_parts<CF>(p, smem, g, m0, n0, acc, nullptr, nullptr, 0, 0);
+    } else {
+      // the workgroups holding the tile: c0 (its first stage) .. c1 (its last)
+      int c0 = slot, c1 = slot;
+      while (c0 > 0 && range_lo(c0) > tile_lo) --c0;
+      while (c1 + 1 < grid && range_lo(c1 + 1) < tile_hi) ++c1;
+      const int nparts = c1 - c0 + 1;
+      // publish this part: slot 2c for the unit a range starts with, else 2c + 1
+      store_tile_gen<CF, true>(smem, acc, partial_slot<CF>(p, 2 * slot + (pos == lo_pos ? 0 : 1)),
+                               CF::BN, CF::BM, CF::BN, nullptr, 0, nullptr, nullptr, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's partial stores are done
       __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_store(p.wsflag + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      int nparts = 0;
-      if (kb1 < nk) {
-        // the first part: wait for the following workgroups' partials, which the
-        // epilogue adds in workgroup order
-        const int64_t tile_end = sk_cum[r] + (int64_t)(t + 1) * nk;
-        while (slot + 1 + nparts < grid && range_lo(slot + 1 + nparts) < tile_end) ++nparts;
-        if (threadIdx.x == 0) {
-          int ok = 1;
-          for (int c = slot + 1; c <= slot + nparts && ok; ++c) {
-            ok = 0;
-            for (int spin = 0; spin < kSpinLimit; ++spin) {
-              if (__hip_atomic_load(p.wsflag + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1) {
-                ok = 1;
-                break;
-              }
-              __builtin_amdgcn_s_sleep(2);
-            }
-            if (ok) __hip_atomic_store(p.wsflag + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          if (!ok) kgwgrad_status_word = KG_ERR_SPLIT;
-          sk_flag = ok;
-        }
-        __syncthreads();  // the partials are read around the caches (sc0 sc1)
-        if (!sk_flag) nparts = 0;
+      if (threadIdx.x == 0) {
+        const int before =
+            __hip_atomic_fetch_add(p.wscnt + c0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sk_last = before == nparts - 1;
+        if (sk_last) __hip_atomic_store(p.wscnt + c0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      store_tile_parts<CF>(p, smem, g, m0, n0, acc, partial_slot<CF>(p, slot + 1), nparts);
+      __syncthreads();
+      if (sk_last) {
+        // C + the partials of c0 .. c1 in that order (read around the caches)
+        zero_acc<CF>(acc);
+        const int s0 = 2 * c0 + (range_lo(c0) == tile_lo ? 0 : 1);
+        store_tile_parts<CF>(p, smem, g, m0, n0, acc, partial_slot<CF>(p, s0),
+                             partial_slot<CF>(p, 2 * (c0 + 1)), 2 * kTile, nparts);
+      }
     }
     pos += kb1 - kb0;
   }
@@ -1494,12 +1612,13 @@ struct Launch {
   const void* fn;
   int stage_bytes;  // all stages
   int bm, bn, threads;
+  int tk, ns;       // tokens per stage, stages in the ring
 };
 
 template <int KIND, bool FAST, class CF, bool SPLIT = false, bool OUTB = false>
 static Launch launch_of() {
   return Launch{(const void*)kg_wgrad_kernel<KIND, FAST, CF, SPLIT, OUTB>, CF::NS * CF::STAGE,
-                CF::BM, CF::BN, CF::THREADS};
+                CF::BM, CF::BN, CF::THREADS, CF::TK, CF::NS};
 }
 
 // bf16 output (whole tiles only: stream-K is not taken with a bf16 D)
@@ -1552,6 +1671,17 @@ static Launch pick(int kind, bool fast, bool small = false, bool split = false,
             : pick_t<false>(kind, fast, small, split, outb);
 }
 
+// Stream-K workspace: one int arrival counter per workgroup (the counter area is padded
+// to a multiple of 256 bytes), then two partial tiles per workgroup of the largest
+// (256 x 256) tile configuration.
+static constexpr size_t split_flag_bytes(int cus) {
+  return ((size_t)cus * sizeof(int) + 255) & ~(size_t)255;
+}
+
+static constexpr size_t split_ws_bytes(int cus) {
+  return split_flag_bytes(cus) + 2 * (size_t)cus * CfgB16::BM * CfgB16::BN * sizeof(float);
+}
+
 struct DeviceInfo {
   int cus = 0;
   bool ready = false;
@@ -1599,15 +1729,6 @@ using namespace kg;
 
 extern "C" int kg_max_groups(void) { return kMaxGroups; }
 
-// Stream-K workspace: one int ready flag per workgroup (the flag area is padded to a
-// multiple of 256 bytes), then one partial tile per workgroup of the bf16 full-tile
-// configuration.
-static size_t split_flag_bytes(int cus) { return ((size_t)cus * sizeof(int) + 255) & ~(size_t)255; }
-
-static size_t split_ws_bytes(int cus) {
-  return split_flag_bytes(cus) + (size_t)cus * CfgB16::BM * CfgB16::BN * sizeof(float);
-}
-
 static int current_cus(int* cus) {
   int dev = 0;
   const hipError_t eg = hipGetDevice(&dev);
@@ -1634,8 +1755,8 @@ extern "C" int64_t kg_wgrad_workspace_flag_bytes(void) {
 // A [K_total, M] and B [K_total, N]
 static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const void* B,
                      int64_t ldb, const void* sb, const void* C, void* D, const int32_t* ks, int G,
-                     int M, int N, int64_t K_total, int gran_k, int dtype_flags, void* workspace,
-                     int64_t workspace_bytes, void* stream) {
+                     int M, int N, int64_t K_total, int64_t scale_rows, int gran_k,
+                     int dtype_flags, void* workspace, int64_t workspace_bytes, void* stream) {
   const int dtype = dtype_flags & 0xFF;
   const int flags = dtype_flags & ~0xFF;
   if (dtype != KG_E4M3_F32SCALE && dtype != KG_E4M3_UE8M0 && dtype != KG_BF16)
@@ -1658,6 +1779,11 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
   } else if (K_total > 0 && (sa == nullptr || sb == nullptr)) {
     return KG_ERR_NULL;
   }
+  // every expert's blocks need their scale rows: at least ceil(K_total / gran_k) in
+  // all (the exact count, sum ceil(ks[g] / gran_k), is checked on the device)
+  if (dtype != KG_BF16 && K_total > 0 &&
+      (scale_rows < 0 || scale_rows < K_total / gran_k + (K_total % gran_k != 0)))
+    return KG_ERR_SCALE_ROWS;
   if (M % 16 != 0 || N % 16 != 0) return KG_ERR_ALIGN;
   if (misaligned(A) || misaligned(B) || misaligned(sa) || misaligned(sb) || misaligned(C) ||
       misaligned(D) || ((uintptr_t)ks & 3) != 0 || ((uintptr_t)workspace & 255) != 0)
@@ -1674,7 +1800,13 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
   const size_t bbytes = nt ? (size_t)N * ldb * elt : (size_t)K_total * N * elt;
   const size_t dbytes = (size_t)G * M * N * (out_bf16 ? 2 : 4);
   if (C != nullptr && C != D && overlap(C, dbytes, D, dbytes)) return KG_ERR_ALIAS;
-  if (overlap(A, abytes, D, dbytes) ||
+  const size_t sesz = dtype == KG_E4M3_F32SCALE ? 4 : 1;
+  // (the kernel reads at most K_total + G rows: sum ceil(ks[g] / gran_k) <= K_total)
+  const int64_t srows = scale_rows < K_total ? scale_rows : K_total;
+  const size_t sabytes = dtype == KG_BF16 ? 0 : (size_t)srows * M * sesz;
+  const size_t sbbytes = dtype == KG_BF16 ? 0 : (size_t)srows * N * sesz;
+  if (overlap(A, abytes, D, dbytes) || overlap(sa, sabytes, D, dbytes) ||
+      overlap(sb, sbbytes, D, dbytes) ||
       overlap(B, bbytes, D, dbytes) || overlap(ks, (size_t)G * 4, D, dbytes) ||
       overlap(workspace, (size_t)workspace_bytes, D, dbytes) ||
       (C != nullptr && overlap(workspace, (size_t)workspace_bytes, C, dbytes)))
@@ -1720,14 +1852,28 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
   p.M = M;
   p.N = N;
   p.K_total = K_total;
+  p.scale_rows = dtype == KG_BF16 ? INT64_MAX : scale_rows;
   p.lda_b = nt ? (uint32_t)(lda * elt) : 0;
   p.ldb_b = nt ? (uint32_t)(ldb * elt) : 0;
   p.gran = dtype == KG_BF16 ? 0 : gran_k;
   p.tiles_m = tiles_m;
   p.tiles_n = tiles_n;
   p.ws = split ? (float*)((unsigned char*)workspace + split_flag_bytes(cus)) : nullptr;
-  p.wsflag = split ? (int*)workspace : nullptr;
+  p.wscnt = split ? (int*)workspace : nullptr;
   const int grid = split ? cus : (int)(total < cus ? total : cus);
+  // KG_PRINT_CONFIG=1 in the environment: the configuration of every launch on stderr
+  static const bool print_config = getenv("KG_PRINT_CONFIG") != nullptr;
+  if (print_config) {
+    static const char* kind_names[4] = {"e4m3+f32", "e4m3+ue8m0", "bf16", "e4m3+f32"};
+    fprintf(stderr,
+            "kgwgrad: %s %s gran %d%s%s G %d M %d N %d K_total %lld | tile %dx%d, %d-token "
+            "stages x %d, %d threads, %s, grid %d, %lld tiles (%d x %d per expert), LDS %d B\n",
+            nt ? "K-major" : "token-major", kind_names[kind], dtype == KG_BF16 ? 0 : gran_k,
+            fast ? " fp8-MFMA" : dtype == KG_BF16 ? "" : " precise", out_bf16 ? " bf16-out" : "",
+            G, M, N, (long long)K_total, L.bm, L.bn, L.tk, L.ns, L.threads,
+            split ? "stream-K" : "whole tiles", grid, (long long)total, tiles_m, tiles_n,
+            L.stage_bytes + sched_bytes(G));
+  }
   void* args[] = {&p};
   const hipError_t e = hipLaunchKernel(L.fn, dim3(grid), dim3(L.threads), args,
                                        L.stage_bytes + sched_bytes(G), (hipStream_t)stream);
@@ -1737,33 +1883,35 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
 
 extern "C" int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb,
                            const void* C, void* D, const int32_t* ks, int G, int M, int N,
-                           int64_t K_total, int gran_k, int dtype_flags, void* workspace,
-                           int64_t workspace_bytes, void* stream) {
-  return wgrad_run(false, A, 0, sa, B, 0, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags,
-                   workspace, workspace_bytes, stream);
+                           int64_t K_total, int64_t scale_rows, int gran_k, int dtype_flags,
+                           void* workspace, int64_t workspace_bytes, void* stream) {
+  return wgrad_run(false, A, 0, sa, B, 0, sb, C, D, ks, G, M, N, K_total, scale_rows, gran_k,
+                   dtype_flags, workspace, workspace_bytes, stream);
 }
 
 extern "C" int kg_wgrad_nt_ws(const void* A, int64_t lda, const void* sa, const void* B,
                               int64_t ldb, const void* sb, const void* C, void* D,
-                              const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
-                              int dtype_flags, void* workspace, int64_t workspace_bytes,
-                              void* stream) {
-  return wgrad_run(true, A, lda, sa, B, ldb, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags,
-                   workspace, workspace_bytes, stream);
+                              const int32_t* ks, int G, int M, int N, int64_t K_total,
+                              int64_t scale_rows, int gran_k, int dtype_flags, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+  return wgrad_run(true, A, lda, sa, B, ldb, sb, C, D, ks, G, M, N, K_total, scale_rows, gran_k,
+                   dtype_flags, workspace, workspace_bytes, stream);
 }
 
 extern "C" int kg_wgrad_nt(const void* A, int64_t lda, const void* sa, const void* B, int64_t ldb,
                            const void* sb, const void* C, void* D, const int32_t* ks, int G, int M,
-                           int N, int64_t K_total, int gran_k, int dtype_flags, void* stream) {
-  return wgrad_run(true, A, lda, sa, B, ldb, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags,
-                   nullptr, 0, stream);
+                           int N, int64_t K_total, int64_t scale_rows, int gran_k, int dtype_flags,
+                           void* stream) {
+  return wgrad_run(true, A, lda, sa, B, ldb, sb, C, D, ks, G, M, N, K_total, scale_rows, gran_k,
+                   dtype_flags, nullptr, 0, stream);
 }
 
 extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb,
                         const void* C, void* D, const int32_t* ks, int G, int M, int N,
-                        int64_t K_total, int gran_k, int dtype_flags, void* stream) {
-  return kg_wgrad_ws(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype_flags, nullptr, 0,
-                     stream);
+                        int64_t K_total, int64_t scale_rows, int gran_k, int dtype_flags,
+                        void* stream) {
+  return kg_wgrad_ws(A, sa, B, sb, C, D, ks, G, M, N, K_total, scale_rows, gran_k, dtype_flags,
+                     nullptr, 0, stream);
 }
 
 extern "C" int kg_status(void* stream) {

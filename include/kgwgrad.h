@@ -27,6 +27,12 @@
  *
  * Thread safety: calls on different streams may run concurrently; they share
  * one per-device status word (see kg_status).
+ *
+ * Environment: with KG_VERBOSE set (to any value) the HIP runtime's errors go to
+ * stderr; with KG_PRINT_CONFIG set, every kg_wgrad* launch's configuration (layout, kind,
+ * tile and stage shape, whole tiles or stream-K, grid, tiles, LDS bytes) does, as the
+ * knowledge-base index page's debugging article describes for the pages' own
+ * kernel-configuration switch.
  */
 #ifndef KGWGRAD_H
 #define KGWGRAD_H
@@ -73,9 +79,15 @@ typedef enum {
   KG_ERR_UNSUPPORTED = -7, /* a combination this build does not implement (see kg_wgrad)   */
   KG_ERR_HIP = -8,         /* the HIP runtime reported an error                            */
   KG_ERR_KSUM = -9,        /* some ks[g] < 0, or sum(ks) != K_total (reported by kg_status) */
-  KG_ERR_SPLIT = -10       /* stream-K mode: a partial tile never became ready (reported by
-                              kg_status; D is incomplete and the workspace must be zeroed
-                              again before its next use)                                    */
+  KG_ERR_SPLIT = -10,      /* reserved: the stream-K mode no longer waits for partial tiles,
+                              so nothing reports this code any more                         */
+  KG_ERR_SCALE_ROWS = -11, /* the scale tensors hold fewer rows than the experts' blocks need,
+                              sum_g ceil(ks[g] / gran_k): returned when scale_rows <
+                              ceil(K_total / gran_k), else found on the device (reported by
+                              kg_status; nothing is written)                                */
+  KG_ERR_SCALE_RANGE = -12 /* KG_E4M3_UE8M0 in the default mode: a block's scales lie outside
+                              the accuracy envelope (see kg_wgrad); D is written, but the
+                              block's terms may be inexact (reported by kg_status)          */
 } kg_status_code;
 
 /*
@@ -89,7 +101,10 @@ typedef enum {
  *          equal to D (in-place accumulate)
  *   D      [G, M, N] fp32 (bf16 with KG_FLAG_D_BF16), output
  *   ks     [G] int32, device memory: tokens per expert, in expert order
- *   nblk   = sum_g ceil(ks[g] / gran_k)
+ *   nblk   = sum_g ceil(ks[g] / gran_k), the scale rows the experts' blocks use
+ *   K_total  rows of A and B; sum_g ks[g] must equal it
+ *   scale_rows  rows that sa and sb each hold (>= nblk); ignored for bf16. The kernel
+ *          never reads past row nblk - 1; scale_rows bounds that on the device.
  *   gran_k tokens per scale block: 128 or 32 (fp8); ignored for bf16
  *   stream a hipStream_t (NULL: the default stream)
  *
@@ -98,14 +113,31 @@ typedef enum {
  * (kg_max_groups), M and N to 2^24, M * N to 2^29 and K_total to 2^31 - 1
  * (KG_ERR_UNSUPPORTED beyond).
  *
+ * Accuracy (default mode): every product of two fp8 (or bf16) values is exact, sums
+ * are fp32, and each block's partial sum is scaled once, so |D - D_exact| stays near
+ * 2^-24 sum_t |a b| per term added; the tests hold it to 1e-5 sum_t |a b| + 1e-6 per
+ * element and 1e-5 in Frobenius norm. That envelope assumes:
+ *  - fp32 scales whose products sa * sb stay in fp32's normal range, and results
+ *    (and single products) that fit fp32;
+ *  - UE8M0 scales any exponent byte 0 .. 254 (2^-127 .. 2^127) such that, in every
+ *    block and for every 64 channels of A and 128 of B that one wave handles, A's
+ *    exponents span at most 236 and B's at most 236, and the block's products
+ *    2^(ea + eb - 254) lie within 2^-234 .. 2^238. Outside that (or with a NaN scale,
+ *    255) the block's terms may be inexact and kg_status reports KG_ERR_SCALE_RANGE.
+ *    The fp8-MFMA mode's scaled MFMA takes every exponent 0 .. 254 directly;
+ *  - experts of up to about 10^6 tokens: fp32 sums of K random-sign terms drift by
+ *    about sqrt(K / 64) * 2^-24 of their norm (the Frobenius bound then nears 1e-5;
+ *    sums of few-bit values, e.g. integers, stay exact to 2^24).
+ *
  * Returns KG_OK after enqueueing, or an error code before enqueueing anything (D
  * untouched). G == 0, M == 0 or N == 0 return KG_OK without a launch. A ks that
  * does not add up to K_total or holds a negative count is detected on the device:
- * the kernel then writes nothing and records KG_ERR_KSUM for kg_status.
+ * the kernel then writes nothing and records KG_ERR_KSUM for kg_status; so does an
+ * nblk above scale_rows (KG_ERR_SCALE_ROWS).
  */
 int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb, const void* C,
-             void* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
-             int dtype, void* stream);
+             void* D, const int32_t* ks, int G, int M, int N, int64_t K_total,
+             int64_t scale_rows, int gran_k, int dtype, void* stream);
 
 /*
  * kg_wgrad_ws -- kg_wgrad with a caller-owned workspace that lets small bf16
@@ -114,28 +146,28 @@ int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb, const
  * When G <= 64, D is fp32, and the problem's output tiles would occupy at most
  * half of the compute units, or whole rounds of tiles would leave more than 30%
  * of them idle, the token range of every tile is cut across all compute units
- * (stream-K): the workgroup that holds a tile's first tokens adds the partial
- * tiles of the workgroups that hold its later tokens, in a fixed order, so results
- * do not depend on timing. Other problems, or a NULL / too small workspace, run
- * exactly as kg_wgrad.
+ * (stream-K): every workgroup that holds part of a cut tile writes its partial sum
+ * to the workspace and counts its arrival; the one that arrives last adds C and the
+ * partials in a fixed order, so results do not depend on timing, and no workgroup
+ * waits for another (other kernels may run beside it). Other problems, or a NULL /
+ * too small workspace, run exactly as kg_wgrad.
  *
  *   workspace        device memory, 256-byte aligned, at least
  *                    kg_wgrad_workspace_bytes() bytes. Its first
- *                    kg_wgrad_workspace_flag_bytes() bytes are ready flags: they must
- *                    be zero before the first use, and every call that completes
- *                    with KG_OK leaves them zero again; the rest is scratch for
- *                    partial tiles and needs no initialisation. It must not overlap
- *                    C or D. Calls that share a workspace must not run concurrently.
+ *                    kg_wgrad_workspace_flag_bytes() bytes are arrival counters: they
+ *                    must be zero before the first use, and every call that completes
+ *                    leaves them zero again; the rest is scratch for partial tiles and
+ *                    needs no initialisation. It must not overlap C or D. Calls that
+ *                    share a workspace must not run concurrently.
  *   workspace_bytes  its size in bytes
  *
  * Returns and errors as kg_wgrad; KG_ERR_ALIGN for a workspace that is not 256-byte
- * aligned, KG_ERR_ALIAS for one that overlaps C or D. kg_status reports
- * KG_ERR_SPLIT if a partial tile was never published (the kernel then gives up
- * after about 0.2 s instead of waiting forever).
+ * aligned, KG_ERR_ALIAS for one that overlaps C or D.
  */
 int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, const void* C,
-                void* D, const int32_t* ks, int G, int M, int N, int64_t K_total, int gran_k,
-                int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+                void* D, const int32_t* ks, int G, int M, int N, int64_t K_total,
+                int64_t scale_rows, int gran_k, int dtype, void* workspace,
+                int64_t workspace_bytes, void* stream);
 
 /*
  * kg_wgrad_nt, kg_wgrad_nt_ws -- kg_wgrad and kg_wgrad_ws with K-major (NT)
@@ -152,8 +184,8 @@ int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, co
  *   B    [N, ldb]  the same for B
  *   ldb  row stride of B in elements, as lda
  *
- * Everything else (scales sa [nblk, M] and sb [nblk, N], C, D, ks, gran_k, dtype and
- * flags, workspace) is as for kg_wgrad / kg_wgrad_ws, and so is the result: with
+ * Everything else (scales sa [nblk, M] and sb [nblk, N] with scale_rows, C, D, ks,
+ * gran_k, dtype and flags, workspace) is as for kg_wgrad / kg_wgrad_ws, and so is the result: with
  * whole tiles (no stream-K), bit for bit what kg_wgrad returns on the token-major
  * operands.
  * Expert starts need no alignment. Extra errors, returned before anything is
@@ -162,39 +194,45 @@ int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, co
  */
 int kg_wgrad_nt(const void* A, int64_t lda, const void* sa, const void* B, int64_t ldb,
                 const void* sb, const void* C, void* D, const int32_t* ks, int G, int M, int N,
-                int64_t K_total, int gran_k, int dtype, void* stream);
+                int64_t K_total, int64_t scale_rows, int gran_k, int dtype, void* stream);
 int kg_wgrad_nt_ws(const void* A, int64_t lda, const void* sa, const void* B, int64_t ldb,
                    const void* sb, const void* C, void* D, const int32_t* ks, int G, int M,
-                   int N, int64_t K_total, int gran_k, int dtype, void* workspace,
-                   int64_t workspace_bytes, void* stream);
+                   int N, int64_t K_total, int64_t scale_rows, int gran_k, int dtype,
+                   void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * kg_wgrad_workspace_bytes -- workspace size that kg_wgrad_ws needs on the current
- * device (one 256 KB partial tile per compute unit plus flags), or -1 if the HIP
+ * device (two 256 KB partial tiles per compute unit plus counters), or -1 if the HIP
  * runtime reports an error.
  */
 int64_t kg_wgrad_workspace_bytes(void);
 
 /*
- * kg_wgrad_workspace_flag_bytes -- size of the flag area at the start of the
- * workspace (zero before first use, kept zero by successful calls), or -1 if the
- * HIP runtime reports an error.
+ * kg_wgrad_workspace_flag_bytes -- size of the arrival-counter area at the start of
+ * the workspace (zero before first use, kept zero by every call), or -1 if the HIP
+ * runtime reports an error.
  */
 int64_t kg_wgrad_workspace_flag_bytes(void);
 
 /*
- * kg_status -- synchronise `stream`, then return and clear the device status
- * word of the current device (KG_OK, KG_ERR_KSUM if a kg_wgrad call since the
- * last kg_status found an inconsistent ks, or KG_ERR_SPLIT). Returns KG_ERR_HIP if the stream
- * reports an error.
+ * kg_status -- synchronise `stream`, then return and clear the device status word of
+ * the current device: KG_OK, or the last asynchronous error a call since the previous
+ * kg_status recorded (KG_ERR_KSUM, KG_ERR_SCALE_ROWS, KG_ERR_SCALE_RANGE). The how-to
+ * page ("Dispatch and Tensor-Map Handling") has the host check the per-expert counts
+ * against the operands before any work; with the counts in device memory that check
+ * runs in the kernel, which writes nothing on a mismatch and leaves the verdict here.
+ * Returns KG_ERR_HIP if the stream reports an error.
  */
 int kg_status(void* stream);
 
 /*
  * kg_debug_offsets -- run the device prefix scan that kg_wgrad's kernels use and
  * write off[G+1] (int64 token offsets) and boff[G+1] (int32 scale-row offsets)
- * to device memory. Test hook. Errors: KG_ERR_NULL, KG_ERR_SHAPE (G < 0 or
- * G > 1024), KG_ERR_GRAN (gran_k <= 0), KG_ERR_HIP.
+ * to device memory: the expert boundaries that the how-to page's "FP8 Implementation
+ * Example" builds from its per-expert counts (its counts 32, 45 and 27 start the
+ * experts at tokens 0, 32 and 77 of 104), and the first scale row of each expert.
+ * Test hook. Errors: KG_ERR_NULL, KG_ERR_SHAPE (G < 0 or G > 1024), KG_ERR_GRAN
+ * (gran_k <= 0), KG_ERR_HIP.
  */
 int kg_debug_offsets(const int32_t* ks, int G, int gran_k, int64_t* off, int32_t* boff,
                      void* stream);
@@ -231,14 +269,18 @@ int kg_max_groups(void);
  *
  *   scale_kind  KG_E4M3_F32SCALE or KG_E4M3_UE8M0; gran_k 32 or 128
  *   H           a multiple of 128; X, Q, S 16-byte aligned
+ *   s_rows      rows that S holds (>= nblk); no row past nblk - 1 is written
  *
  * Errors (before any launch): KG_ERR_DTYPE, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_NULL,
- * KG_ERR_ALIGN, KG_ERR_ALIAS (X or S overlapping Q), KG_ERR_UNSUPPORTED (G > 1024),
- * KG_ERR_HIP. A ks that does not add up to K_total is reported by kg_status
- * (KG_ERR_KSUM) and nothing is written. G == 0 or H == 0: KG_OK, no launch.
+ * KG_ERR_ALIGN, KG_ERR_ALIAS (outputs overlapping each other or an input),
+ * KG_ERR_UNSUPPORTED (G > 1024), KG_ERR_SCALE_ROWS (s_rows < ceil(K_total / gran_k)),
+ * KG_ERR_HIP. A ks that does not add up to K_total (KG_ERR_KSUM), or whose nblk
+ * exceeds s_rows (KG_ERR_SCALE_ROWS), is reported by kg_status and nothing is
+ * written. G == 0 or H == 0: KG_OK, no launch.
  */
 int kg_requant(const void* X, const float* xs, const int32_t* ks, int G, int H, int64_t K_total,
-               int gran_k, int src, int scale_kind, void* Q, void* S, void* stream);
+               int gran_k, int src, int scale_kind, void* Q, void* S, int64_t s_rows,
+               void* stream);
 
 /*
  * kg_dgrad -- enqueue the M-grouped GEMM of the data gradient, dx = dy . w per expert

@@ -46,9 +46,9 @@ FAKE = 0x100000  # an aligned, never dereferenced address
 
 
 def call(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE + (1 << 31),
-         G=3, M=64, N=128, K=104, gran=128, dtype=kg.KG_E4M3_F32SCALE):
+         G=3, M=64, N=128, K=104, gran=128, dtype=kg.KG_E4M3_F32SCALE, rows=3):
     v = lambda x: None if x is None else ctypes.c_void_p(x)
-    return B.lib().kg_wgrad(v(A), v(sa), v(Bp), v(sb), v(C), v(D), v(ks), G, M, N, K, gran,
+    return B.lib().kg_wgrad(v(A), v(sa), v(Bp), v(sb), v(C), v(D), v(ks), G, M, N, K, rows, gran,
                             dtype, None)
 
 
@@ -79,6 +79,14 @@ def call(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE 
     (dict(D=FAKE + (1 << 30) + 8), B.KG_ERR_ALIGN),
     (dict(C=FAKE + (1 << 30) + 64), B.KG_ERR_ALIAS),  # partial overlap of C and D
     (dict(D=FAKE + 4096), B.KG_ERR_ALIAS),  # D overlaps A
+    # scale rows: fewer than ceil(K_total / gran_k) (1 here, 4 at gran 32)
+    (dict(rows=0), B.KG_ERR_SCALE_ROWS),
+    (dict(rows=-5), B.KG_ERR_SCALE_ROWS),
+    (dict(rows=3, gran=32), B.KG_ERR_SCALE_ROWS),
+    (dict(rows=0, dtype=kg.KG_E4M3_UE8M0, gran=32), B.KG_ERR_SCALE_ROWS),
+    # ... and scale tensors of that many rows overlapping D
+    (dict(sb=FAKE + (1 << 30) - 1024, rows=3), B.KG_ERR_ALIAS),
+    (dict(sa=FAKE + (1 << 30) + 1024, rows=3), B.KG_ERR_ALIAS),
 ])
 def test_synchronous_errors(kw, code):
     assert call(**kw) == code
@@ -87,11 +95,11 @@ def test_synchronous_errors(kw, code):
 def call_ws(ws=FAKE + (1 << 32), ws_bytes=1 << 26, **kw):
     v = lambda x: None if x is None else ctypes.c_void_p(x)
     a = dict(A=FAKE, sa=FAKE, Bp=FAKE, sb=FAKE, C=None, D=FAKE + (1 << 30), ks=FAKE + (1 << 31),
-             G=3, M=64, N=128, K=104, gran=128, dtype=kg.KG_E4M3_F32SCALE)
+             G=3, M=64, N=128, K=104, rows=3, gran=128, dtype=kg.KG_E4M3_F32SCALE)
     a.update(kw)
     return B.lib().kg_wgrad_ws(v(a["A"]), v(a["sa"]), v(a["Bp"]), v(a["sb"]), v(a["C"]), v(a["D"]),
-                               v(a["ks"]), a["G"], a["M"], a["N"], a["K"], a["gran"], a["dtype"],
-                               v(ws), ws_bytes, None)
+                               v(a["ks"]), a["G"], a["M"], a["N"], a["K"], a["rows"], a["gran"],
+                               a["dtype"], v(ws), ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -100,6 +108,7 @@ def call_ws(ws=FAKE + (1 << 32), ws_bytes=1 << 26, **kw):
     (dict(ws_bytes=-1), B.KG_ERR_SHAPE),
     (dict(M=1 << 15, N=1 << 15), B.KG_ERR_UNSUPPORTED),      # M * N above 2^29
     (dict(gran=64), B.KG_ERR_GRAN),
+    (dict(rows=0), B.KG_ERR_SCALE_ROWS),
 ])
 def test_workspace_entry_point_errors(kw, code):
     assert call_ws(**kw) == code
@@ -108,10 +117,12 @@ def test_workspace_entry_point_errors(kw, code):
 def call_nt(ws=None, ws_bytes=0, **kw):
     v = lambda x: None if x is None else ctypes.c_void_p(x)
     a = dict(A=FAKE, lda=112, sa=FAKE, Bp=FAKE, ldb=112, sb=FAKE, C=None, D=FAKE + (1 << 30),
-             ks=FAKE + (1 << 31), G=3, M=64, N=128, K=104, gran=128, dtype=kg.KG_E4M3_F32SCALE)
+             ks=FAKE + (1 << 31), G=3, M=64, N=128, K=104, rows=3, gran=128,
+             dtype=kg.KG_E4M3_F32SCALE)
     a.update(kw)
     args = (v(a["A"]), a["lda"], v(a["sa"]), v(a["Bp"]), a["ldb"], v(a["sb"]), v(a["C"]),
-            v(a["D"]), v(a["ks"]), a["G"], a["M"], a["N"], a["K"], a["gran"], a["dtype"])
+            v(a["D"]), v(a["ks"]), a["G"], a["M"], a["N"], a["K"], a["rows"], a["gran"],
+            a["dtype"])
     if ws is None:
         return B.lib().kg_wgrad_nt(*args, None)
     return B.lib().kg_wgrad_nt_ws(*args, v(ws), ws_bytes, None)
@@ -129,15 +140,18 @@ def call_nt(ws=None, ws_bytes=0, **kw):
     (dict(A=FAKE + 8), B.KG_ERR_ALIGN),
     (dict(dtype=kg.KG_BF16, sa=None, sb=None, lda=108), B.KG_ERR_ALIGN),  # 216 bytes
     (dict(ws=FAKE + (1 << 32) + 16, ws_bytes=1 << 26), B.KG_ERR_ALIGN),
+    (dict(rows=0), B.KG_ERR_SCALE_ROWS),
 ])
 def test_nt_synchronous_errors(kw, code):
     assert call_nt(**kw) == code
 
 
 def call_rq(X=FAKE, xs=None, ks=FAKE + (1 << 31), G=2, H=256, K=300, gran=128,
-            src=B.KG_SRC_BF16, kind=kg.KG_E4M3_F32SCALE, Q=FAKE + (1 << 32), S=FAKE + (1 << 33)):
+            src=B.KG_SRC_BF16, kind=kg.KG_E4M3_F32SCALE, Q=FAKE + (1 << 32), S=FAKE + (1 << 33),
+            rows=4):
     v = lambda x: None if x is None else ctypes.c_void_p(x)
-    return B.lib().kg_requant(v(X), v(xs), v(ks), G, H, K, gran, src, kind, v(Q), v(S), None)
+    return B.lib().kg_requant(v(X), v(xs), v(ks), G, H, K, gran, src, kind, v(Q), v(S), rows,
+                              None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -154,6 +168,9 @@ def call_rq(X=FAKE, xs=None, ks=FAKE + (1 << 31), G=2, H=256, K=300, gran=128,
     (dict(H=192), B.KG_ERR_ALIGN),
     (dict(Q=FAKE + (1 << 32) + 8), B.KG_ERR_ALIGN),
     (dict(Q=FAKE + 4096), B.KG_ERR_ALIAS),                 # Q overlaps X
+    (dict(rows=2), B.KG_ERR_SCALE_ROWS),                   # S: fewer rows than ceil(300 / 128)
+    (dict(rows=-1), B.KG_ERR_SCALE_ROWS),
+    (dict(S=FAKE + (1 << 32) + 300 * 256 - 512), B.KG_ERR_ALIAS),  # S overlaps Q's end
 ])
 def test_requant_synchronous_errors(kw, code):
     assert call_rq(**kw) == code

@@ -105,6 +105,30 @@ def test_requant_ksum_mismatch_writes_nothing():
     assert (Q == 7).all() and (S == 3.0).all()
 
 
+def test_requant_too_few_scale_rows_writes_nothing():
+    """ks [60, 30, 10] at gran 128 needs 3 scale rows, while the host can only require
+    ceil(100 / 128) = 1: S with 1 or 2 rows passes the host check and the kernel reports
+    KG_ERR_SCALE_ROWS without writing. At gran 32 the host bound, ceil(100 / 32) = 4,
+    already rejects 3 rows."""
+    say("requant scale rows")
+    d = torch.device("cuda:0")
+    X = torch.randn(100, 128, device=d).to(torch.bfloat16)
+    ks = torch.tensor([60, 30, 10], dtype=torch.int32, device=d)
+    Q = torch.full((100, 128), 7, dtype=torch.uint8, device=d)
+    S = torch.full((3, 128), 3.0, device=d)
+    for rows in (1, 2):
+        assert kg.kg_requant_raw(X, None, ks, 3, 128, 100, 128, kg.KG_SRC_BF16,
+                                 kg.KG_E4M3_F32SCALE, Q, S[:rows], s_rows=rows) == kg.KG_OK
+        assert kg.kg_status() == kg.KG_ERR_SCALE_ROWS
+        assert (Q == 7).all() and (S == 3.0).all()
+    assert kg.kg_requant_raw(X, None, ks, 3, 128, 100, 32, kg.KG_SRC_BF16,
+                             kg.KG_E4M3_F32SCALE, Q, S, s_rows=3) == kg.KG_ERR_SCALE_ROWS
+    assert kg.kg_requant_raw(X, None, ks, 3, 128, 100, 128, kg.KG_SRC_BF16,
+                             kg.KG_E4M3_F32SCALE, Q, S) == kg.KG_OK
+    assert kg.kg_status() == kg.KG_OK
+    assert not (S == 3.0).any()
+
+
 def test_requant_feeds_wgrad():
     # the requantised operands run through kg_wgrad and match the oracle GEMM on them
     say("requant -> wgrad")
