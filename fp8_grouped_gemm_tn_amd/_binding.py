@@ -33,6 +33,8 @@ SIGNATURES = {
                         _i32, _vp]),
     "kg_wgrad_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32,
                            _i32, _vp, _i64, _vp]),
+    "kg_wgrad_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64,
+                                _i32, _i32, _vp]),
     "kg_wgrad_nt": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64,
                            _i64, _i32, _i32, _vp]),
     "kg_wgrad_nt_ws": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
@@ -179,6 +181,17 @@ def kg_wgrad_ws_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, ws,
     return lib().kg_wgrad_ws(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D), _ptr(ks),
                              int(G), int(M), int(N), int(K_total), int(scale_rows), int(gran_k),
                              int(dtype), _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def kg_wgrad_noalloc_raw(A, sa, B, sb, C, D, ks, G, M, N, K_total, gran_k, dtype, stream=None,
+                         scale_rows=None):
+    """Call kg_wgrad_noalloc (the library's static scratch instead of a workspace) with
+    torch device tensors (or None); returns the status code."""
+    if scale_rows is None:
+        scale_rows = scale_rows_of(sa, sb)
+    return lib().kg_wgrad_noalloc(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D),
+                                  _ptr(ks), int(G), int(M), int(N), int(K_total),
+                                  int(scale_rows), int(gran_k), int(dtype), _stream(stream))
 
 
 def kg_wgrad_workspace_bytes():

@@ -1682,8 +1682,16 @@ static constexpr size_t split_ws_bytes(int cus) {
   return split_flag_bytes(cus) + 2 * (size_t)cus * CfgB16::BM * CfgB16::BN * sizeof(float);
 }
 
+// The scratch of kg_wgrad_noalloc: the stream-K workspace for up to kScratchCUs compute
+// units (128 MiB + 1 KiB), one copy per device, held until the process ends. In host
+// code `scratch` names a host-side stand-in: its device address is taken once per
+// device with hipGetSymbolAddress (DeviceInfo::scratch) and only that is used.
+constexpr int kScratchCUs = 256;
+static __device__ __align__(256) unsigned char scratch[split_ws_bytes(kScratchCUs)];
+
 struct DeviceInfo {
   int cus = 0;
+  void* scratch = nullptr;  // device address of this device's `scratch`
   bool ready = false;
 };
 static std::mutex g_mu;
@@ -1709,10 +1717,20 @@ static int device_setup(int dev) {
                               l.stage_bytes + sched_bytes(kMaxGroups));
       if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
     }
+    void* sp = nullptr;
+    e = hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || sp == nullptr) return hip_fail(e, "hipGetSymbolAddress");
     d.cus = cus;
+    d.scratch = sp;
     d.ready = true;
   }
   return KG_OK;
+}
+
+// Zeroes n ints (the stream-K arrival counters of kg_wgrad_noalloc's scratch) with
+// ordinary stores, so that a call captured in a HIP graph holds no memset node.
+__global__ void kg_clear_kernel(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
 static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -1753,10 +1771,13 @@ extern "C" int64_t kg_wgrad_workspace_flag_bytes(void) {
 
 // nt: K-major operands A [M, lda] and B [N, ldb] (elements), else token-major
 // A [K_total, M] and B [K_total, N]
+// clear_counters: zero the workspace's arrival counters before a stream-K launch (the
+// library's own scratch, whose last user may have been any earlier call)
 static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const void* B,
                      int64_t ldb, const void* sb, const void* C, void* D, const int32_t* ks, int G,
                      int M, int N, int64_t K_total, int64_t scale_rows, int gran_k,
-                     int dtype_flags, void* workspace, int64_t workspace_bytes, void* stream) {
+                     int dtype_flags, void* workspace, int64_t workspace_bytes, void* stream,
+                     bool clear_counters = false) {
   const int dtype = dtype_flags & 0xFF;
   const int flags = dtype_flags & ~0xFF;
   if (dtype != KG_E4M3_F32SCALE && dtype != KG_E4M3_UE8M0 && dtype != KG_BF16)
@@ -1861,6 +1882,12 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
   p.ws = split ? (float*)((unsigned char*)workspace + split_flag_bytes(cus)) : nullptr;
   p.wscnt = split ? (int*)workspace : nullptr;
   const int grid = split ? cus : (int)(total < cus ? total : cus);
+  if (split && clear_counters) {
+    hipLaunchKernelGGL(kg_clear_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, p.wscnt,
+                       (int)(split_flag_bytes(cus) / sizeof(int)));
+    const hipError_t ec = hipGetLastError();
+    if (ec != hipSuccess) return hip_fail(ec, "kernel launch");
+  }
   // KG_PRINT_CONFIG=1 in the environment: the configuration of every launch on stderr
   static const bool print_config = getenv("KG_PRINT_CONFIG") != nullptr;
   if (print_config) {
@@ -1904,6 +1931,21 @@ extern "C" int kg_wgrad_nt(const void* A, int64_t lda, const void* sa, const voi
                            void* stream) {
   return wgrad_run(true, A, lda, sa, B, ldb, sb, C, D, ks, G, M, N, K_total, scale_rows, gran_k,
                    dtype_flags, nullptr, 0, stream);
+}
+
+extern "C" int kg_wgrad_noalloc(const void* A, const void* sa, const void* B, const void* sb,
+                                const void* C, void* D, const int32_t* ks, int G, int M, int N,
+                                int64_t K_total, int64_t scale_rows, int gran_k, int dtype_flags,
+                                void* stream) {
+  int dev = 0;
+  const hipError_t eg = hipGetDevice(&dev);
+  if (eg != hipSuccess) return hip_fail(eg, "hipGetDevice");
+  const int rc = device_setup(dev);
+  if (rc != KG_OK) return rc;
+  // the scratch covers the stream-K workspace of kScratchCUs compute units
+  if (split_ws_bytes(g_dev[dev].cus) > sizeof(scratch)) return KG_ERR_UNSUPPORTED;
+  return wgrad_run(false, A, 0, sa, B, 0, sb, C, D, ks, G, M, N, K_total, scale_rows, gran_k,
+                   dtype_flags, g_dev[dev].scratch, (int64_t)sizeof(scratch), stream, true);
 }
 
 extern "C" int kg_wgrad(const void* A, const void* sa, const void* B, const void* sb,

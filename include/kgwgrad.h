@@ -170,6 +170,22 @@ int kg_wgrad_ws(const void* A, const void* sa, const void* B, const void* sb, co
                 int64_t workspace_bytes, void* stream);
 
 /*
+ * kg_wgrad_noalloc -- kg_wgrad_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid it): the
+ * workspace is the library's own static device array (128 MiB + 1 KiB per device,
+ * held from the library's first use on a device until the process ends), so the call
+ * allocates and frees nothing. Arguments, results and errors as kg_wgrad_ws without
+ * the workspace arguments; KG_ERR_UNSUPPORTED on a device with more than 256 compute
+ * units (whose stream-K workspace would exceed the array). Before a stream-K launch a
+ * small kernel zeroes the array's counters (no memset, so the call may be captured).
+ * All calls on one device share the array: calls that overlap in time on one device
+ * (other streams, other threads) race and must not be made.
+ */
+int kg_wgrad_noalloc(const void* A, const void* sa, const void* B, const void* sb, const void* C,
+                     void* D, const int32_t* ks, int G, int M, int N, int64_t K_total,
+                     int64_t scale_rows, int gran_k, int dtype, void* stream);
+
+/*
  * kg_wgrad_nt, kg_wgrad_nt_ws -- kg_wgrad and kg_wgrad_ws with K-major (NT)
  * operands: the token index is the contiguous one. The GitHub issue page
  * (qijiaxing, 2025-04-03) writes dw = dy^t x as a GEMM of dy^t [h_out, tokens] and
