@@ -87,8 +87,12 @@ struct Params {
 // SCALE_BYTES of scale tile per operand. PIPE: one 32-token MFMA step per stage, and
 // each wave reads stage kb+1's fragments into registers before it issues stage kb's
 // MFMAs (bf16 only).
+// SWZ (token-major fp8 only): LDS rows without padding; each row's 16-byte chunks are
+// XOR-permuted by the row's low three bits (logical chunk c of row r sits at c ^ (r & 7)),
+// so that the eight rows one transposing read touches still fall in distinct banks. The
+// LDS the padding took then holds a third stage.
 template <int BM_, int BN_, int WAVES_M_, int TK_, int NS_, int ELT_, int SCALE_BYTES_,
-          int THREADS_ = 512, bool PIPE_ = false, bool NT_ = false>
+          int THREADS_ = 512, bool PIPE_ = false, bool NT_ = false, bool SWZ_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, TK = TK_, NS = NS_, ELT = ELT_;
   static constexpr int THREADS = THREADS_, WAVES = THREADS_ / 64;
@@ -106,7 +110,8 @@ struct Cfg {
   // bytes); every pair of rows is followed by 16 bytes of padding, so that the 16
   // rows of a sub-tile, read at one byte offset, start in 16 distinct 4-bank groups.
   // The load layout's "row" is then a pair of channels (ROW = 272 bytes).
-  static constexpr int PAD = NT ? 16 : ELT == 2 ? 32 : 16;
+  static constexpr bool SWZ = SWZ_;
+  static constexpr int PAD = SWZ ? 0 : NT ? 16 : ELT == 2 ? 32 : 16;
   static constexpr int ROWA = NT ? 2 * TK * ELT + PAD : BM * ELT + PAD;
   static constexpr int ROWB = NT ? 2 * TK * ELT + PAD : BN * ELT + PAD;
   static constexpr int CHA = ROWA / 16, CHB = ROWB / 16;  // 16-byte chunks per row
@@ -129,8 +134,11 @@ struct Cfg {
   // SIMD one wave can run MFMAs while the other waits to issue loads (measured +2-6%
   // on the fp8 workloads; the load-bound bf16 half tiles lose 10% with half the
   // waves issuing loads)
-  static constexpr bool ALT = NS == 2 && WAVES == 8 && !PIPE && ELT == 1;
+  // (with three stages too: a wave then owns every other stage's loads)
+  static constexpr bool ALT = (NS == 2 || NS == 3) && WAVES == 8 && !PIPE && ELT == 1;
   static constexpr int SLOTS4 = (LOADS + 3) / 4;
+  // loads of a stage that wave w of the issuing half issues (ALT)
+  static __host__ __device__ constexpr int alt_loads(int w) { return (LOADS - (w & 3) + 3) / 4; }
   static constexpr int PER = LOADS / WAVES, HEAVY = LOADS % WAVES;
   static constexpr int OPA = RA * ROWA, OPB = RB * ROWB;
   static constexpr int SCALE_BYTES = SCALE_BYTES_;
@@ -152,6 +160,8 @@ struct Cfg {
   static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile must be whole sub-tile pairs");
   static_assert(RA * CHA % 64 == 0 && RB * CHB % 64 == 0, "stage must be whole wave loads");
   static_assert(!NT || (TK * ELT == 128 && !PIPE), "K-major rows: 128 bytes, plain stages");
+  static_assert(!SWZ || (!NT && !PIPE && ELT == 1 && BM * ELT >= 128 && BN * ELT >= 128),
+                "swizzled rows: token-major fp8, at least 8 chunks per row");
   static_assert(EPI_BYTES <= NS * STAGE, "epilogue must fit the stages");
   static_assert(NS >= 2, "at least two stages");
   static_assert(EPI_ROWS * EPI_CPR % THREADS == 0, "epilogue work must split evenly");
@@ -169,6 +179,10 @@ using CfgF8 = Cfg<256, 256, 4, 128, 2, 1, 1024>;
 // take; UE8M0 scales, folded into the widening, need no partials and use CfgF8: 17%
 // faster on 256 experts); two stages of 128
 using CfgF8h = Cfg<256, 128, 4, 128, 2, 1, 1024>;
+// CfgF8h with three stages in the LDS the row padding took (swizzled rows): two stages in
+// flight instead of one, for problems whose schedule leaves the LDS room (the kernel's
+// loads are bound by the bytes in flight per CU, not by bandwidth)
+using CfgF8h3 = Cfg<256, 128, 4, 128, 3, 1, 1024, 512, false, false, true>;
 // fp8 with fp32 scales per 32 tokens: the 256 x 128 tile of CfgF8h, four scale rows
 // per 128-token stage (4 KB of scale tile per operand)
 using CfgF8h32 = Cfg<256, 128, 4, 128, 2, 1, 4096>;
@@ -192,6 +206,7 @@ template <bool NT>
 struct Cfgs {
   using F8 = CfgF8;
   using F8h = CfgF8h;
+  using F8hD = CfgF8h3;  // CfgF8h with three stages (when the LDS holds them)
   using F8h32 = CfgF8h32;
   using B16 = CfgB16;
   using B16s = CfgB16s;
@@ -200,6 +215,7 @@ template <>
 struct Cfgs<true> {
   using F8 = CfgF8N;
   using F8h = CfgF8hN;
+  using F8hD = CfgF8hN;
   using F8h32 = CfgF8h32N;
   using B16 = CfgB16N;
   using B16s = CfgB16sN;
@@ -228,10 +244,13 @@ __device__ inline uint32_t load_off(const Params& p, int k, int lane) {
                         : kOobOffset;
   } else if (is_a) {
     const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
-    return ch < CF::DCA ? row * (uint32_t)(p.M * CF::ELT) + 16 * ch : kOobOffset;
+    // swizzled rows: LDS chunk ch of row `row` holds the row's chunk ch ^ (row & 7)
+    const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+    return ch < CF::DCA ? row * (uint32_t)(p.M * CF::ELT) + 16 * gch : kOobOffset;
   } else {
     const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
-    return ch < CF::DCB ? row * (uint32_t)(p.N * CF::ELT) + 16 * ch : kOobOffset;
+    const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+    return ch < CF::DCB ? row * (uint32_t)(p.N * CF::ELT) + 16 * gch : kOobOffset;
   }
 }
 
@@ -256,11 +275,13 @@ __device__ inline LoadOffsets<CF> load_offsets(const Params& p) {
     } else if (k < CF::LOADS_A) {
       const int idx = 64 * k + lane;
       const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
-      if (ch < CF::DCA) o.off[s] = row * eM + 16 * ch;
+      const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+      if (ch < CF::DCA) o.off[s] = row * eM + 16 * gch;
     } else if (k < CF::LOADS_A + CF::LOADS_B) {
       const int idx = 64 * (k - CF::LOADS_A) + lane;
       const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
-      if (ch < CF::DCB) o.off[s] = row * eN + 16 * ch;
+      const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+      if (ch < CF::DCB) o.off[s] = row * eN + 16 * gch;
     }
   }
   return o;
@@ -892,12 +913,34 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
                                       : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const float* sSa = (const float*)(st + CF::SA_OFF);
   const float* sSb = (const float*)(st + CF::SB_OFF);
+  // swizzled rows: the lane's rows all have r & 7 = (j >> 1) & 7, so each sub-tile's
+  // chunk moves by a fixed XOR; one base per sub-tile row (column), the token offsets
+  // stay immediates
+  const int sw = (j >> 1) & 7;
+  auto swz_a = [&](int i) __attribute__((always_inline)) {
+    return st + lrow * CF::ROWA + 16 * (((wm * CF::WM) / 16 + i) ^ sw) + 8 * (j & 1);
+  };
+  auto swz_b = [&](int jn) __attribute__((always_inline)) {
+    return st + CF::OPA + lrow * CF::ROWB + 16 * (((wn * CF::WN) / 16 + jn) ^ sw) + 8 * (j & 1);
+  };
+  auto rda = [&](int i, int kk) __attribute__((always_inline)) {
+    if constexpr (CF::SWZ)
+      return tr8(swz_a(i) + 32 * kk * CF::ROWA);
+    else
+      return rd8<CF, CF::ROWA>(aBase, i, kk);
+  };
+  auto rdb = [&](int jn, int kk) __attribute__((always_inline)) {
+    if constexpr (CF::SWZ)
+      return tr8(swz_b(jn) + 32 * kk * CF::ROWB);
+    else
+      return rd8<CF, CF::ROWB>(bBase, jn, kk);
+  };
   v8bf af[CF::NI][KK];
 #pragma unroll
   for (int i = 0; i < CF::NI; ++i)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      af[i][kk] = widen8(rd8<CF, CF::ROWA>(aBase, i, kk), 1.0f);
+      af[i][kk] = widen8(rda(i, kk), 1.0f);
   auto rescale = [&](int pi, int pj, const v4f& x) {
     const v4f sa = *(const v4f*)(sSa + wm * CF::WM + 16 * pi + 4 * q);
     const float sb = sSb[wn * CF::WN + 16 * pj + j];
@@ -910,7 +953,7 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
   // rescale runs between this column's first MFMAs.
   v2i rnext[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, 0, kk);
+  for (int kk = 0; kk < KK; ++kk) rnext[kk] = rdb(0, kk);
   v8bf bf[KK];
   v4f xprev[CF::NI];
 #pragma unroll
@@ -919,7 +962,7 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
     for (int kk = 0; kk < KK; ++kk) bf[kk] = widen8(rnext[kk], 1.0f);
     if (jn + 1 < CF::NJ) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) rnext[kk] = rd8<CF, CF::ROWB>(bBase, jn + 1, kk);
+      for (int kk = 0; kk < KK; ++kk) rnext[kk] = rdb(jn + 1, kk);
     }
     v4f x[CF::NI];
 #pragma unroll
@@ -1368,8 +1411,19 @@ __device__ __forceinline__ void item_gemm(const Params& p, const LoadOffsets<CF>
   }
   int buf = 0;  // j % NS
   for (int j = 0; j < n; ++j) {
-    const int ahead = min(CF::NS - 2, n - 1 - j);
-    wait_stages<CF>(ahead);
+    if constexpr (CF::ALT && CF::NS == 3) {
+      // a wave issued only every other stage: if the stage in flight after this one
+      // is its own, it may stay in flight (loads complete in issue order); else this
+      // wave's outstanding loads all belong to this stage
+      const int w = threadIdx.x >> 6;
+      if (j + 1 < n && (w >> 2) == ((kb0 + j + 1) & 1))
+        wait_vmcnt(CF::alt_loads(w));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+      const int ahead = min(CF::NS - 2, n - 1 - j);
+      wait_stages<CF>(ahead);
+    }
     __syncthreads();
     if constexpr (CF::NT) {
       if (kb0 + j == nk - 1 && (Kg * CF::ELT) % 16 != 0) {
@@ -1623,7 +1677,7 @@ static Launch launch_of() {
 
 // bf16 output (whole tiles only: stream-K is not taken with a bf16 D)
 template <bool NT>
-static Launch pick_outb(int kind, bool fast, bool small) {
+static Launch pick_outb(int kind, bool fast, bool small, bool deep) {
   using S = Cfgs<NT>;
   if (kind == F32S32)
     return fast ? launch_of<F32S32, true, typename S::F8h32, false, true>()
@@ -1632,16 +1686,17 @@ static Launch pick_outb(int kind, bool fast, bool small) {
     return small ? launch_of<BF16, false, typename S::B16s, false, true>()
                  : launch_of<BF16, false, typename S::B16, false, true>();
   if (kind == F32S)
-    return fast ? launch_of<F32S, true, typename S::F8, false, true>()
-                : launch_of<F32S, false, typename S::F8h, false, true>();
+    return fast   ? launch_of<F32S, true, typename S::F8, false, true>()
+           : deep ? launch_of<F32S, false, typename S::F8hD, false, true>()
+                  : launch_of<F32S, false, typename S::F8h, false, true>();
   return fast ? launch_of<E8M0, true, typename S::F8, false, true>()
               : launch_of<E8M0, false, typename S::F8, false, true>();
 }
 
 template <bool NT>
-static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb) {
+static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb, bool deep) {
   using S = Cfgs<NT>;
-  if (outb) return pick_outb<NT>(kind, fast, small);
+  if (outb) return pick_outb<NT>(kind, fast, small, deep);
   if (kind == F32S32)
     return fast ? (split ? launch_of<F32S32, true, typename S::F8h32, true>()
                          : launch_of<F32S32, true, typename S::F8h32>())
@@ -1650,8 +1705,9 @@ static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb) {
   if (split) {
     if (kind == BF16) return launch_of<BF16, false, typename S::B16, true>();
     if (kind == F32S)
-      return fast ? launch_of<F32S, true, typename S::F8, true>()
-                  : launch_of<F32S, false, typename S::F8h, true>();
+      return fast   ? launch_of<F32S, true, typename S::F8, true>()
+             : deep ? launch_of<F32S, false, typename S::F8hD, true>()
+                    : launch_of<F32S, false, typename S::F8h, true>();
     return fast ? launch_of<E8M0, true, typename S::F8, true>()
                 : launch_of<E8M0, false, typename S::F8, true>();
   }
@@ -1659,17 +1715,27 @@ static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb) {
     return small ? launch_of<BF16, false, typename S::B16s>()
                  : launch_of<BF16, false, typename S::B16>();
   if (kind == F32S)
-    return fast ? launch_of<F32S, true, typename S::F8>() : launch_of<F32S, false, typename S::F8h>();
+    return fast   ? launch_of<F32S, true, typename S::F8>()
+           : deep ? launch_of<F32S, false, typename S::F8hD>()
+                  : launch_of<F32S, false, typename S::F8h>();
   return fast ? launch_of<E8M0, true, typename S::F8>() : launch_of<E8M0, false, typename S::F8>();
 }
 
 // small: half tiles (bf16) for problems with few full tiles; split: stream-K over the
-// full-size tiles; outb: bf16 D; nt: K-major operands
+// full-size tiles; outb: bf16 D; nt: K-major operands; deep: the three-stage precise
+// fp32-scale tile (token-major) when its stages and the schedule fit the LDS
 static Launch pick(int kind, bool fast, bool small = false, bool split = false,
-                   bool outb = false, bool nt = false) {
-  return nt ? pick_t<true>(kind, fast, small, split, outb)
-            : pick_t<false>(kind, fast, small, split, outb);
+                   bool outb = false, bool nt = false, bool deep = false) {
+  return nt ? pick_t<true>(kind, fast, small, split, outb, deep)
+            : pick_t<false>(kind, fast, small, split, outb, deep);
 }
+
+// Dynamic LDS a workgroup may take on gfx950: 160 KB less 1 KB for the kernels' static
+// __shared__ arrays (at most about 0.6 KB: the scan's wave sums, stream-K's offsets).
+constexpr int kMaxLds = 159 * 1024;
+
+// The three-stage precise tile fits beside the schedule of G experts.
+static bool deep_fits(int G) { return CfgF8h3::NS * CfgF8h3::STAGE + sched_bytes(G) <= kMaxLds; }
 
 // Stream-K workspace: one int arrival counter per workgroup (the counter area is padded
 // to a multiple of 256 bytes), then two partial tiles per workgroup of the largest
@@ -1707,14 +1773,15 @@ static int device_setup(int dev) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     // every kernel the launches can pick: layouts x kinds x modes
     const int kinds[4] = {F32S, E8M0, BF16, F32S32};
-    for (int v = 0; v < 2 * 4 * 2 * 2 * 2 * 2; ++v) {
+    for (int v = 0; v < 2 * 4 * 2 * 2 * 2 * 2 * 2; ++v) {
       const bool nt = v & 1, fast = (v >> 3) & 1, small = (v >> 4) & 1;
-      const bool split = (v >> 5) & 1, outb = (v >> 6) & 1;
+      const bool split = (v >> 5) & 1, outb = (v >> 6) & 1, deep = (v >> 7) & 1;
       const int kind = kinds[(v >> 1) & 3];
       if ((fast && kind == BF16) || (split && outb)) continue;
-      const Launch l = pick(kind, fast, small, split, outb, nt);
+      const Launch l = pick(kind, fast, small, split, outb, nt, deep);
+      const int lds = l.stage_bytes + sched_bytes(kMaxGroups);
       e = hipFuncSetAttribute(l.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              l.stage_bytes + sched_bytes(kMaxGroups));
+                              lds < kMaxLds ? lds : kMaxLds);
       if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
     }
     void* sp = nullptr;
@@ -1856,7 +1923,7 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
   const bool split = workspace != nullptr && G <= kMaxSplitGroups && !out_bf16 &&
                      (size_t)workspace_bytes >= split_ws_bytes(cus) &&
                      (2 * T <= (int64_t)cus || 10 * T < 7 * rounds * (int64_t)cus);
-  const Launch L = pick(kind, fast, small && !split, split, out_bf16, nt);
+  const Launch L = pick(kind, fast, small && !split, split, out_bf16, nt, deep_fits(G));
   const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
   const int64_t total = (int64_t)G * tiles_m * tiles_n;
   if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;
