@@ -51,38 +51,80 @@ struct QParams {
   int gran;
 };
 
-// binary32 -> e4m3fn code: nearest value, ties to the even code, saturating at
-// +-448, sign kept, NaN -> 0x7F. Branch-free: with E the binary exponent of
-// min(|y|, 448) clamped to [-6, 8], the code is 8 * (E + 7) + rint(|y| * 2^(3 - E))
-// - 8 (exact: scaling by a power of two, then the round-to-nearest-even of
-// v_rndne_f32). E = -6 covers the subnormals (codes 0..8), and a mantissa that
-// rounds up to 16 carries into the exponent field by itself.
-__device__ inline uint32_t e4m3_rne(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const float a = __builtin_fminf(__builtin_fabsf(y), 448.0f);
-  int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
-  E = E < -6 ? -6 : E;
-  const int m = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - E));
-  const uint32_t code = (uint32_t)(8 * (E + 7) + m - 8);
-  return y != y ? 0x7Fu : (((u >> 24) & 0x80u) | code);
+// e4m3fn codes of four binary32 values, one per byte (a in the low byte): the
+// nearest e4m3fn value, ties to the even code, sign kept (also for zero). gfx950's
+// fp32 -> fp8 conversion instruction rounds this way; the values handed to it lie
+// within +-448 (1 + 2^-18), where no saturation is needed (448 rounds to itself up to
+// the midpoint 464), or are NaN, which it encodes as 0xFF and which is mapped to 0x7F
+// (a byte whose low seven bits are all ones carries into bit 7 when 1 is added).
+__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
+  uint32_t q = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  q = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)q, true);
+  const uint32_t nan = ((q & 0x7F7F7F7Fu) + 0x01010101u) & q & 0x80808080u;
+  return q ^ nan;
 }
 
-// e4m3_rne(x / s) for the binary32 quotient fl(x / s), without a division in the
-// common case: y' = x * inv (inv = fl(1 / s)) differs from fl(x / s) by less than
-// 2^-18 of the e4m3 step at |y'|, so both round the same way unless y' lies within
-// 2^-16 of a step midpoint; only lanes with such a value take the exact division.
-__device__ inline uint32_t e4m3_rne_quotient(float x, float s, float inv) {
-  const float y = x * inv;
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const float a = __builtin_fminf(__builtin_fabsf(y), 448.0f);
-  int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
-  E = E < -6 ? -6 : E;
-  const float r = __builtin_ldexpf(a, 3 - E);  // |y| in e4m3 steps (exact)
-  const float m = __builtin_rintf(r);
-  uint32_t q = y != y ? 0x7Fu : (((u >> 24) & 0x80u) | (uint32_t)(8 * (E + 7) + (int)m - 8));
-  if (__builtin_fabsf(__builtin_fabsf(r - m) - 0.5f) < 1.52587890625e-05f)  // 2^-16
-    q = e4m3_rne(x / s);
-  return q;
+// Magnitudes above 448 (here only infinities) saturate to +-448; NaN stays NaN.
+__device__ inline float e4m3_sat(float y) {
+  return __builtin_fabsf(y) > 448.0f ? __builtin_copysignf(448.0f, y) : y;
+}
+
+// Codes of four values of one row: e4m3(x_k / s_k) for fp32 scales, e4m3(x_k * m_k)
+// for UE8M0 (m_k = 2^(127 - e_k), an exact product).
+//
+// fp32 scales, common case (every s_k a normal number, so inv_k = fl(1 / s_k) = m_k
+// is one too): y_k = x_k * inv_k lies within 2^-22 (relative) of the binary32 quotient
+// fl(x_k / s_k). When y_k (1 - 2^-19) and y_k (1 + 2^-19) round to the same codes,
+// rounding being monotone, fl(x_k / s_k) between them rounds to those codes too;
+// otherwise (a value within about 2^-16 of a step of a rounding midpoint) the
+// quotients are divided out. (A y_k that is subnormal or zero rounds to a signed zero
+// code, as the quotient does.)
+//
+// EXACT (a column of the thread has a scale outside the normal range, or an infinite
+// maximum): the quotients or products themselves, infinities saturated.
+template <int SK, bool EXACT>
+__device__ __forceinline__ uint32_t e4m3x4_scaled(const float (&x)[4], const float (&s)[4],
+                                                  const float (&m)[4]) {
+  if constexpr (EXACT) {
+    float y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      y[k] = e4m3_sat(SK == KG_E4M3_F32SCALE ? x[k] / s[k] : x[k] * m[k]);
+    return e4m3x4(y[0], y[1], y[2], y[3]);
+  } else if constexpr (SK == KG_E4M3_F32SCALE) {
+    constexpr float lo = 1.0f - 0x1p-19f, hi = 1.0f + 0x1p-19f;
+    float y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = x[k] * m[k];
+    const uint32_t ql = e4m3x4(y[0] * lo, y[1] * lo, y[2] * lo, y[3] * lo);
+    const uint32_t qh = e4m3x4(y[0] * hi, y[1] * hi, y[2] * hi, y[3] * hi);
+    if (ql == qh) return ql;
+    return e4m3x4(x[0] / s[0], x[1] / s[1], x[2] / s[2], x[3] / s[3]);
+  } else {
+    return e4m3x4(x[0] * m[0], x[1] * m[1], x[2] * m[2], x[3] * m[3]);
+  }
+}
+
+// One thread's rows of codes: 8 channels (two 4-byte words) per row.
+template <int SK, bool EXACT, int ROWS, int RG>
+__device__ __forceinline__ void store_codes(const QParams& p, const float (&v)[ROWS][8],
+                                            const float (&sdiv)[8], const float (&mul)[8],
+                                            int rg, int rows, int64_t t0, int h0) {
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int r = rg + RG * i;
+    if (r < rows) {
+      uint32_t w4[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float xv[4] = {v[i][4 * h], v[i][4 * h + 1], v[i][4 * h + 2], v[i][4 * h + 3]};
+        const float sv[4] = {sdiv[4 * h], sdiv[4 * h + 1], sdiv[4 * h + 2], sdiv[4 * h + 3]};
+        const float mv[4] = {mul[4 * h], mul[4 * h + 1], mul[4 * h + 2], mul[4 * h + 3]};
+        w4[h] = e4m3x4_scaled<SK, EXACT>(xv, sv, mv);
+      }
+      *(uint2*)(p.Q + (t0 + r) * p.H + h0) = uint2{w4[0], w4[1]};
+    }
+  }
 }
 
 // E8M0 byte of the smallest power of two >= r (r = amax / 448 > 0), clamped to
@@ -225,37 +267,25 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
     float mul[8];   // UE8M0: 2^(127 - e); fp32 scales: 1 / s
     float sdiv[8];  // fp32 scales: s
     uint32_t eb[8];
+    bool exact = false;  // a scale outside the normal range or an infinite maximum
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if constexpr (SK == KG_E4M3_F32SCALE) {
         sdiv[c] = amax[c] == 0.0f ? 1.0f : amax[c] / 448.0f;
         mul[c] = 1.0f / sdiv[c];
+        exact |= !(sdiv[c] >= 0x1p-126f && sdiv[c] <= 0x1p126f);
       } else {
         const int e = amax[c] == 0.0f ? 127 : e8m0_ceil(amax[c] / 448.0f);
         eb[c] = (uint32_t)e;
         mul[c] = __builtin_ldexpf(1.0f, 127 - e);
+        sdiv[c] = 1.0f;  // unused
+        exact |= amax[c] > 3.40282347e38f;
       }
     }
-#pragma unroll
-    for (int i = 0; i < kMaxRows; ++i) {
-      const int r = rg + RG * i;
-      if (r < rows) {
-        uint32_t lo4 = 0, hi4 = 0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          uint32_t q;
-          if constexpr (SK == KG_E4M3_F32SCALE)
-            q = e4m3_rne_quotient(v[i][c], sdiv[c], mul[c]);
-          else
-            q = e4m3_rne(v[i][c] * mul[c]);  // exact: a power of two
-          if (c < 4)
-            lo4 |= q << (8 * c);
-          else
-            hi4 |= q << (8 * (c - 4));
-        }
-        *(uint2*)(p.Q + (t0 + r) * p.H + h0) = uint2{lo4, hi4};
-      }
-    }
+    if (exact)
+      store_codes<SK, true, kMaxRows, RG>(p, v, sdiv, mul, rg, rows, t0, h0);
+    else
+      store_codes<SK, false, kMaxRows, RG>(p, v, sdiv, mul, rg, rows, t0, h0);
     if (rg == 0 && h0 < p.H) {
       if constexpr (SK == KG_E4M3_F32SCALE) {
         float4* dst = (float4*)((float*)p.S + (int64_t)b * p.H + h0);

@@ -421,3 +421,74 @@ def dgrad_workload(name, device="cpu", seed=0):
         return make_dgrad_case(name, workload_ks("ue8m0_many", seed), 2048, 7168, seed=seed,
                                device=device)
     raise KeyError(name)
+
+
+def requant_edge_source(K, H, seed=0):
+    """Requantiser edge-case source: fp32 [K, H], every value exactly representable in
+    bf16. Column h follows pattern h % 16, each row-periodic so that any run of 8 or
+    more tokens holds the pattern's largest magnitude:
+      0  N(0,1) with +inf at every 32nd row
+      1  N(0,1) with -inf at every 32nd row and NaN at every 5th
+      2  all NaN
+      3  zeros, every other one negative
+      4  bf16 subnormals: +-j * 2^-133, j in 1..127
+      5  small normals +-(1 + j/128) * 2^-120 .. 2^-125 (amax / 448 is subnormal)
+      6-9  f * o * 2^k with f = 1, 3, 5, 7, o odd in 1..31, k in -12..3, and
+           +-448 f at every 8th row (so that x / (amax / 448) = o * 2^k exactly)
+      10 N(0,1) * 2^u, u uniform in -30..30
+      11-15 N(0,1), 1% of entries x 50
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((K, H)).astype(np.float32)
+    fam = np.arange(H) % 16
+    rows = np.arange(K)[:, None]
+    sign = np.where(rng.random((K, H)) < 0.5, -1.0, 1.0).astype(np.float32)
+    def put(mask_cols, vals):
+        x[:, mask_cols] = vals[:, mask_cols]
+    c = fam == 0
+    x[:, c] = np.where(rows % 32 == 0, np.float32(np.inf), x[:, c])
+    c = fam == 1
+    v = np.where(rows % 5 == 0, np.float32(np.nan), x[:, c])
+    x[:, c] = np.where(rows % 32 == 3, np.float32(-np.inf), v)
+    x[:, fam == 2] = np.nan
+    c = fam == 3
+    x[:, c] = np.where(rows % 2 == 0, np.float32(0.0), np.float32(-0.0))
+    j = rng.integers(1, 128, (K, H)).astype(np.float64)
+    put(fam == 4, (sign * np.ldexp(j, -133)).astype(np.float32))
+    e = rng.integers(-125, -119, (K, H))
+    put(fam == 5, (sign * np.ldexp(1.0 + j / 128.0, e)).astype(np.float32))
+    o = (2 * rng.integers(0, 16, (K, H)) + 1).astype(np.float64)
+    k = rng.integers(-12, 4, (K, H))
+    for f_id, f in zip((6, 7, 8, 9), (1.0, 3.0, 5.0, 7.0)):
+        c = fam == f_id
+        vals = (sign * f * np.ldexp(o, k)).astype(np.float32)
+        vals = np.where(rows % 8 == 0, (sign * np.float32(448.0 * f)).astype(np.float32), vals)
+        x[:, c] = vals[:, c]
+    u = rng.integers(-30, 31, (K, H))
+    put(fam == 10, np.ldexp(x.astype(np.float64), u).astype(np.float32))
+    c = fam >= 11
+    big = rng.random((K, H)) < 0.01
+    x[:, c] = np.where(big[:, c], x[:, c] * 50, x[:, c])
+    # every value to the nearest bf16 (the patterns above are exact already)
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def requant_edge_fp8_source(K, H, seed=0):
+    """Requantiser edge cases for the fp8 source with 1x128 per-token scales: e4m3fn
+    bytes [K, H] (uint8) of every code, NaN codes 0x7F and 0xFF included, and fp32
+    scales [K, H/128]: mostly 1e-4 .. 1e-2, with rows at 3e38 (products above 1
+    overflow to infinity), 1e-40 (subnormal products) and 0. The last 80 rows hold
+    codes of magnitude at most 224 with scales alternately 2^-149 (the smallest
+    subnormal) and 0, so that the largest magnitude of a run there is at most
+    224 * 2^-149."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, (K, H), dtype=np.uint8)
+    xs = (rng.random((K, H // 128)) * 0.01 + 1e-4).astype(np.float32)
+    xs[5::17] = np.float32(3e38)
+    xs[7::19] = np.float32(1e-40)
+    xs[11::23] = np.float32(0.0)
+    tail = codes[-80:]
+    codes[-80:] = np.where((tail & 0x7F) > 0x77, tail & 0xF7, tail)
+    xs[-80:] = np.float32(2.0 ** -149)
+    xs[-80::2] = np.float32(0.0)
+    return codes, xs

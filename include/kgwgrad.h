@@ -281,7 +281,11 @@ int kg_max_groups(void);
  *     KG_E4M3_UE8M0:    e = 127 + the smallest k with 2^k >= amax / 448, clamped to
  *                       [0, 254] (127 if amax == 0), q = e4m3(x * 2^(127 - e));
  *   e4m3() rounds to the nearest e4m3fn value, ties to the even code, saturating at
- *   +-448 and keeping the sign.
+ *   +-448 and keeping the sign; NaN becomes 0x7F. Special values: amax skips NaNs;
+ *   an infinite amax gives s = inf (finite x -> signed zero codes, infinite x -> NaN
+ *   0x7F) or the E8M0 byte 254 (infinite x -> +-448); a nonzero amax of at most
+ *   224 * 2^-149 makes amax / 448 = 0: s = 0 (x != 0 -> +-448, x == 0 -> 0x7F) or
+ *   the E8M0 byte 0.
  *
  *   scale_kind  KG_E4M3_F32SCALE or KG_E4M3_UE8M0; gran_k 32 or 128
  *   H           a multiple of 128; X, Q, S 16-byte aligned

@@ -454,8 +454,13 @@ uint8_t kgref_e4m3_encode(double v) {
 }
 
 /* Smallest power-of-two exponent k with 2^k >= r (r > 0, a normal or subnormal
- * binary32 value), as the E8M0 byte k + 127 clamped to [0, 254]. */
+ * binary32 value), as the E8M0 byte k + 127 clamped to [0, 254]. An infinite r (a
+ * block holding an infinity) has no such k: it takes the clamp's upper end, 254. A
+ * zero r (a nonzero amax whose quotient by 448 underflows) is met by every k: the
+ * clamp's lower end, 0. */
 static uint8_t e8m0_ceil(float r) {
+  if (isinf(r)) return 254;
+  if (r == 0.0f) return 0;
   int k;
   const double f = frexp((double)r, &k); /* r = f * 2^k, f in [0.5, 1) */
   if (f == 0.5) k -= 1;                   /* r is a power of two */
@@ -491,7 +496,8 @@ int kgref_requant(const void* X, const float* xs, const int32_t* ks, int G, int 
     for (int64_t t0 = t_first; t0 < t_first + ks[g]; t0 += gran_k, ++brow) {
       const int64_t t1 = t0 + gran_k < t_first + ks[g] ? t0 + gran_k : t_first + ks[g];
       for (int h = 0; h < H; ++h) {
-        /* the block's values of channel h, in fp32, and their largest magnitude */
+        /* the block's values of channel h, in fp32, and their largest magnitude
+         * (NaNs are skipped: the comparison below is false for them) */
         float amax = 0.0f;
         for (int64_t t = t0; t < t1; ++t) {
           float x;

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import fp8_grouped_gemm_tn_amd as kg
+from fp8_grouped_gemm_tn_amd import inputs
 from oracle import kgref
 
 pytestmark = pytest.mark.gpu
@@ -34,10 +35,16 @@ def make_source(src, K, H, seed):
 
 
 def run_case(src, kind, gran, ks, H, seed):
+    K = int(np.asarray(ks, np.int64).sum())
+    run_source(src, kind, gran, ks, H, *make_source(src, K, H, seed))
+
+
+def run_source(src, kind, gran, ks, H, X, xs, Xh, xsh):
+    """X, xs: the source as torch CPU tensors (bf16, or uint8 codes with fp32 scales);
+    Xh, xsh: the same as numpy arrays for the oracle."""
     ks = np.asarray(ks, np.int32)
     K = int(ks.sum())
     nblk = int(sum((int(k) + gran - 1) // gran for k in ks))
-    X, xs, Xh, xsh = make_source(src, K, H, seed)
     d = torch.device("cuda:0")
     Xd = X.to(d)
     xsd = None if xs is None else xs.to(d)
@@ -90,6 +97,35 @@ def test_requant_bit_exact_most_groups(kind, gran):
     say("requant 1024 groups", kind, gran)
     ks = [0 if i % 7 == 0 else (13 * i) % 41 for i in range(1024)]
     run_case(kg.KG_SRC_BF16, kind, gran, ks, 256, seed=12)
+
+
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("kind", [kg.KG_E4M3_F32SCALE, kg.KG_E4M3_UE8M0])
+def test_requant_bit_exact_edge_values(kind, gran):
+    """Infinities, NaNs, signed zeros, bf16 subnormals, block maxima whose scale is
+    subnormal (its reciprocal overflows), exact rounding ties x / s = o * 2^k for
+    s = 1, 3, 5, 7, and a wide dynamic range, on ragged experts."""
+    say("requant edge values bf16", kind, gran)
+    ks = [300, 0, 129, 1, 513, 64, 7]
+    K, H = sum(ks), 512
+    x32 = inputs.requant_edge_source(K, H, seed=gran + kind)
+    xb = torch.from_numpy(x32).to(torch.bfloat16)
+    run_source(kg.KG_SRC_BF16, kind, gran, ks, H, xb, None,
+               xb.view(torch.int16).numpy().view(np.uint16), None)
+
+
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("kind", [kg.KG_E4M3_F32SCALE, kg.KG_E4M3_UE8M0])
+def test_requant_bit_exact_edge_values_fp8_source(kind, gran):
+    """The fp8 source with every code (NaN codes included) and per-token scales whose
+    products overflow to infinity, are subnormal, or are zero (scale 0: the block's
+    fp32 scale amax / 448 can underflow to 0)."""
+    say("requant edge values fp8", kind, gran)
+    ks = [300, 0, 129, 1, 200]
+    K, H = sum(ks), 384
+    codes, xs = inputs.requant_edge_fp8_source(K, H, seed=gran + kind)
+    run_source(kg.KG_SRC_E4M3_1X128, kind, gran, ks, H, torch.from_numpy(codes),
+               torch.from_numpy(xs), codes, xs)
 
 
 def test_requant_ksum_mismatch_writes_nothing():

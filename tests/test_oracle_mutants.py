@@ -56,6 +56,12 @@ C_MUTANTS = {
     "fp32 scale amax / 447": [("const float s = amax == 0.0f ? 1.0f : amax / 448.0f;",
                                "const float s = amax == 0.0f ? 1.0f : amax / 447.0f;")],
     "ue8m0 exponent not exact at powers of two": [("if (f == 0.5) k -= 1;", "(void)f;")],
+    "ue8m0 infinite maximum not clamped": [("  if (isinf(r)) return 254;\n", "")],
+    "ue8m0 underflowed quotient not clamped": [("  if (r == 0.0f) return 0;\n", "")],
+    "requant amax takes NaNs": [("if (fabsf(x) > amax) amax = fabsf(x);",
+                                 "if (!(fabsf(x) <= amax)) amax = fabsf(x);")],
+    "e4m3 encode NaN keeps its sign": [("if (isnan(v)) return 0x7F;",
+                                        "if (isnan(v)) return signbit(v) ? 0xFF : 0x7F;")],
     "ue8m0 zero block exponent 0": [("const uint8_t e = amax == 0.0f ? 127 : e8m0_ceil(amax / 448.0f);",
                                      "const uint8_t e = amax == 0.0f ? 0 : e8m0_ceil(amax / 448.0f);")],
     "dgrad activation scales token-major": [

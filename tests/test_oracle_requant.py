@@ -74,11 +74,14 @@ def numpy_requant(x32, ks, gran, scale_kind):
         for b0 in range(t0, t0 + int(k), gran):
             b1 = min(b0 + gran, t0 + int(k))
             blk = x32[b0:b1]
-            amax = np.max(np.abs(blk), axis=0).astype(np.float32)
+            # largest magnitude with NaNs skipped (0 for an all-NaN column)
+            amax = np.fmax.reduce(np.abs(blk), axis=0).astype(np.float32)
+            amax = np.where(np.isnan(amax), np.float32(0), amax).astype(np.float32)
             if scale_kind == F32S:
                 s = np.where(amax == 0, np.float32(1.0), amax / np.float32(448.0)).astype(np.float32)
-                y = (blk / s[None, :]).astype(np.float32)
-                q = torch_enc(np.clip(y, -448, 448))
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    y = (blk / s[None, :]).astype(np.float32)
+                q = np.where(np.isnan(y), np.uint8(0x7F), torch_enc(np.clip(y, -448, 448)))
                 scales.append(s)
             else:
                 r = (amax / np.float32(448.0)).astype(np.float32)
@@ -89,12 +92,13 @@ def numpy_requant(x32, ks, gran, scale_kind):
                 ex = ((bits >> 23) & 0xFF).astype(np.int64)
                 mant = (bits & 0x7FFFFF)
                 k2 = np.where(ex > 0, ex - 127 + (mant != 0), 0)
-                sub = (ex == 0) & nz
+                sub = (ex == 0) & (mant != 0) & nz
                 if sub.any():  # subnormal quotients
                     k2[sub] = np.ceil(np.log2(r[sub].astype(np.float64))).astype(np.int64)
+                k2[nz & (r == 0)] = -1000  # amax / 448 underflowed: any k, clamped to 0
                 e[nz] = np.clip(k2[nz] + 127, 0, 254)
                 y = (blk.astype(np.float64) * np.exp2(127.0 - e)[None, :]).astype(np.float32)
-                q = torch_enc(np.clip(y, -448, 448))
+                q = np.where(np.isnan(y), np.uint8(0x7F), torch_enc(np.clip(y, -448, 448)))
                 scales.append(e.astype(np.uint8))
             rows_q[b0:b1] = q
         t0 += int(k)
@@ -206,3 +210,72 @@ def test_requant_validation():
     assert kgref.requant(x, None, [4], 128, 128, SBF, 7)[0] == kgref.ERR_DTYPE
     x8 = np.zeros((4, 96), np.uint8)
     assert kgref.requant(x8, np.zeros((4, 1), np.float32), [4], 96, 128, S8, F32S)[0] == kgref.ERR_SHAPE
+
+
+# ------------------------------------------------------------ special values
+
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("scale_kind", [F32S, UE8])
+def test_edge_values_match_independent_numpy(gran, scale_kind):
+    """Infinities, NaNs, signed zeros, bf16 subnormals, maxima whose scale is
+    subnormal, and exact rounding ties x / s = o * 2^k, against the numpy twin (NaNs
+    skipped by amax and encoded 0x7F; IEEE binary32 arithmetic for the rest)."""
+    from fp8_grouped_gemm_tn_amd import inputs
+    ks = [200, 0, 37, 64, 1]
+    K, H = sum(ks), 128
+    x32 = inputs.requant_edge_source(K, H, seed=gran + scale_kind)
+    xb = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    rc, Q, S = kgref.requant(xb, None, ks, H, gran, SBF, scale_kind)
+    assert rc == kgref.OK
+    Qn, Sn = numpy_requant(x32, ks, gran, scale_kind)
+    assert np.array_equal(Q, Qn)
+    assert np.array_equal(S.view(np.uint8), Sn.view(np.uint8))
+
+
+def test_edge_values_closed_forms():
+    """What IEEE arithmetic fixes for the special columns, block by block."""
+    from fp8_grouped_gemm_tn_amd import inputs
+    K, H = 128, 128
+    x32 = inputs.requant_edge_source(K, H, seed=3)
+    xb = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    _, Qf, Sf = kgref.requant(xb, None, [K], H, 128, SBF, F32S)
+    _, Qe, Se = kgref.requant(xb, None, [K], H, 128, SBF, UE8)
+    for h in range(H):
+        col, fam = x32[:, h], h % 16
+        fin = np.isfinite(col)
+        if fam == 0:   # +inf present: s = inf, finite values -> signed zeros, inf -> NaN
+            assert np.isinf(Sf[0, h]) and Se[0, h] == 254
+            assert (Qf[fin, h] & 0x7F == 0).all() and (Qf[~fin, h] == 0x7F).all()
+            assert (Qe[np.isposinf(col), h] == 0x7E).all()
+        if fam == 2:   # all NaN: amax 0, unit scale / byte 127, codes NaN
+            assert Sf[0, h] == 1.0 and Se[0, h] == 127 and (Qf[:, h] == 0x7F).all()
+        if fam == 3:   # zeros: sign kept
+            assert Sf[0, h] == 1.0 and Se[0, h] == 127
+            assert np.array_equal(Qf[:, h], np.where(np.signbit(col), 0x80, 0x00))
+        if fam == 6:   # amax 448: s = 1, e = 127, the codes are the values' own
+            assert Sf[0, h] == 1.0 and Se[0, h] == 127
+            assert np.array_equal(Qf[:, h], torch_enc(col)) and np.array_equal(Qe[:, h], Qf[:, h])
+        if fam in (7, 8, 9):  # amax 448 f: s = f exactly, x / s = o * 2^k exactly
+            f = (3.0, 5.0, 7.0)[fam - 7]
+            assert Sf[0, h] == f
+            assert np.array_equal(Qf[:, h], torch_enc((col / np.float32(f)).astype(np.float32)))
+
+
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("scale_kind", [F32S, UE8])
+def test_fp8_edge_source_matches_independent_numpy(gran, scale_kind):
+    """The fp8 source with NaN codes and per-token scales whose products overflow, are
+    subnormal or zero; runs whose fp32 scale amax / 448 underflows to 0."""
+    from fp8_grouped_gemm_tn_amd import inputs
+    ks = [300, 0, 129, 1, 200]
+    K, H = sum(ks), 256
+    X, xs = inputs.requant_edge_fp8_source(K, H, seed=gran + scale_kind)
+    rc, Q, S = kgref.requant(X, xs, ks, H, gran, S8, scale_kind)
+    assert rc == kgref.OK
+    with np.errstate(over="ignore", invalid="ignore"):
+        x32 = (dec(X).astype(np.float32) * np.repeat(xs, 128, axis=1)).astype(np.float32)
+    Qn, Sn = numpy_requant(x32, ks, gran, scale_kind)
+    assert np.array_equal(Q, Qn)
+    assert np.array_equal(S.view(np.uint8), Sn.view(np.uint8))
+    if scale_kind == F32S:
+        assert (S == 0).any() and np.isinf(S).any()
