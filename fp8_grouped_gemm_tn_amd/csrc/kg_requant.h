@@ -18,12 +18,16 @@
 // saturation at +-448 and the sign kept. Scale rows are packed per expert exactly
 // as kg_wgrad reads them.
 //
-// Design: HBM-bound, one pass. A work item is (scale row, 128-channel slice): 256
-// threads hold the block's values in registers (16 channel groups of 8 channels x 16
-// row groups), reduce the column maxima with lane shuffles and one LDS exchange, and
-// write 8-byte runs of fp8 codes. A persistent grid walks the items; each workgroup
-// scans ks once (the same scan as the GEMM) and finds an item's expert by binary
-// search over the scale-row offsets.
+// Design: HBM-bound, one pass. A work item is (scale row, channel tile); each wave
+// owns a 128-channel slab of the tile (16 lanes of 8 channels per row, 4 rows at a
+// time) and, with the other waves of its slab, the block's rows. The raw source
+// words stay in registers between a pass that takes the column maxima (lane shuffles,
+// then one LDS exchange when a slab spans several waves) and a pass that writes
+// 8-byte runs of fp8 codes. Loads and stores go through buffer resources over the
+// block's rows, whose range check turns rows past the block into zero reads and
+// dropped writes. A persistent grid walks the items; each workgroup scans ks once
+// (the same scan as the GEMM) and finds an item's expert by binary search over the
+// scale-row offsets.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,10 +38,18 @@
 
 namespace kg {
 
-constexpr int kQThreads = 256;
-constexpr int kQCols = 128;   // channels per item
-constexpr int kQColGroups = 16;  // threads per row: 8 channels each
-constexpr int kQRowGroups = kQThreads / kQColGroups;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kQCols = 128;      // channels per slab
+constexpr int kQColGroups = 16;  // lanes per row: 8 channels each
+
+// Slabs per item and waves per slab. gran_k 32: four one-wave slabs (8 rows per
+// lane). gran_k 128: bf16 sources two slabs of two waves (16 rows per lane); e4m3
+// sources four one-wave slabs (32 rows per lane, whose raw words take half the
+// registers of bf16 ones). Measured on MI355X among 1-8 slabs of 1-4 waves.
+constexpr int q_slabs(int src, int gran) { return gran == 32 ? 4 : src == KG_SRC_BF16 ? 2 : 4; }
+constexpr int q_wps(int src, int gran) { return gran == 32 ? 1 : src == KG_SRC_BF16 ? 2 : 1; }
 
 struct QParams {
   const unsigned char* X;  // bf16 or e4m3 [K_total, H]
@@ -106,23 +118,24 @@ __device__ __forceinline__ uint32_t e4m3x4_scaled(const float (&x)[4], const flo
 }
 
 // One thread's rows of codes: 8 channels (two 4-byte words) per row.
-template <int SK, bool EXACT, int ROWS, int RG>
-__device__ __forceinline__ void store_codes(const QParams& p, const float (&v)[ROWS][8],
-                                            const float (&sdiv)[8], const float (&mul)[8],
-                                            int rg, int rows, int64_t t0, int h0) {
+template <int SK, bool EXACT, int ROWS, int RG, class W>
+__device__ __forceinline__ void store_codes(__amdgpu_buffer_rsrc_t qr, int H, uint32_t qoff,
+                                            W widen, const float (&sdiv)[8],
+                                            const float (&mul)[8]) {
 #pragma unroll
   for (int i = 0; i < ROWS; ++i) {
-    const int r = rg + RG * i;
-    if (r < rows) {
+    {
+      float v[8];
+      widen(i, v);
       uint32_t w4[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float xv[4] = {v[i][4 * h], v[i][4 * h + 1], v[i][4 * h + 2], v[i][4 * h + 3]};
+        const float xv[4] = {v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
         const float sv[4] = {sdiv[4 * h], sdiv[4 * h + 1], sdiv[4 * h + 2], sdiv[4 * h + 3]};
         const float mv[4] = {mul[4 * h], mul[4 * h + 1], mul[4 * h + 2], mul[4 * h + 3]};
         w4[h] = e4m3x4_scaled<SK, EXACT>(xv, sv, mv);
       }
-      *(uint2*)(p.Q + (t0 + r) * p.H + h0) = uint2{w4[0], w4[1]};
+      __builtin_amdgcn_raw_buffer_store_b64(v2u{w4[0], w4[1]}, qr, (int)qoff, i * RG * H, 2 /* nt */);
     }
   }
 }
@@ -141,30 +154,31 @@ __device__ inline int e8m0_ceil(float r) {
   return e < 0 ? 0 : e > 254 ? 254 : e;
 }
 
-// Layout of an item (scale row, channel tile): 16 channel groups of 8 channels
-// each form a 128-channel slab. gran_k = 128: one slab, 16 row groups (rows rg + 16i,
-// four waves), column maxima through LDS. gran_k = 32: four slabs, one per wave, 4
-// row groups per wave (rows rg + 4i): the maxima need only lane shuffles.
+// Layout of an item (scale row, SLABS x 128 channels): wave w works on slab
+// w / WPS; its lanes hold channel group cg = lane % 16 (8 channels) of rows
+// rg + RG i, rg = 4 (w % WPS) + lane / 16, RG = 4 WPS.
 template <int SRC, int SK, int GRAN>
-__global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
+__global__ __launch_bounds__(q_slabs(SRC, GRAN) * q_wps(SRC, GRAN) * 64) void kg_requant_kernel(
+    QParams p) {
+  constexpr int SLABS = q_slabs(SRC, GRAN), WPS = q_wps(SRC, GRAN);
+  constexpr int NT = SLABS * WPS * 64;  // threads
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int64_t wsum_k[kMaxWaves];
   __shared__ int32_t wsum_b[kMaxWaves];
-  __shared__ float red[kQThreads / 64][kQCols];
+  __shared__ float red[NT / 64][kQCols];
   Sched s = sched_carve(smem, p.G);
   const int sched_rc =
-      sched_build<kQThreads>(p.ks, p.G, p.gran, p.K_total, s, wsum_k, wsum_b, false, p.s_rows);
+      sched_build<NT>(p.ks, p.G, p.gran, p.K_total, s, wsum_k, wsum_b, false, p.s_rows);
   if (sched_rc != KG_OK) {
     if (blockIdx.x == 0 && threadIdx.x == 0) kgwgrad_status_word = sched_rc;
     return;
   }
-  constexpr int SLABS = GRAN == 32 ? 4 : 1;
-  constexpr int RG = GRAN == 32 ? 4 : kQRowGroups;  // row groups per slab
-  constexpr int kMaxRows = GRAN / RG;                // rows per thread
+  constexpr int RG = 4 * WPS;          // row groups per slab
+  constexpr int kMaxRows = GRAN / RG;  // rows per thread
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cg = tid % kQColGroups;
-  const int rg = GRAN == 32 ? lane / kQColGroups : tid / kQColGroups;
-  const int slab = GRAN == 32 ? w : 0;
+  const int slab = w / WPS;
+  const int rg = (w % WPS) * 4 + lane / kQColGroups;
   const int ctiles = (p.H + kQCols * SLABS - 1) / (kQCols * SLABS);
   const int64_t nblk = s.boff[p.G];
   const int64_t total = nblk * ctiles;
@@ -183,72 +197,91 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
     const int g = lo;
     const int kb = b - s.boff[g];
     const int64_t t0 = s.off[g] + (int64_t)kb * p.gran;
-    const int h0 = (ct * SLABS + slab) * kQCols + cg * 8;
-    // rows of the block this thread's slab covers (none past the last channel)
-    const int rows = h0 < p.H ? (int)min((int64_t)GRAN, s.off[g + 1] - t0) : 0;
-    // this thread's rows (rg, rg + 16, ...) of its 8 channels: every load is issued
-    // before any is used, then the values are widened to binary32
+    const int hs = (ct * SLABS + slab) * kQCols;  // the wave's first channel
+    const int h0 = hs + cg * 8;
+    // rows of the block this wave's slab covers (none past the last channel)
+    const int rows = hs < p.H ? (int)min((int64_t)GRAN, s.off[g + 1] - t0) : 0;
+    // buffers over those rows from the slab's first channel: rows past them read as
+    // zeros and their codes are dropped by the range check (offsets below 2^32: H is
+    // at most 2^23)
+    constexpr int XB = SRC == KG_SRC_BF16 ? 2 : 1;  // source bytes per value
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.X + (t0 * p.H + hs) * XB), 0, (int)((uint32_t)rows * p.H * XB), kRsrcWord3);
+    const uint32_t xoff = (uint32_t)(rg * p.H + cg * 8) * XB;
     constexpr int RAW = SRC == KG_SRC_BF16 ? 4 : 2;  // 32-bit words per row
     uint32_t raw[kMaxRows][RAW];
     float xsc[kMaxRows];
+    const int HB = p.H / 128;
+    const float* xs_rows = SRC == KG_SRC_BF16 ? nullptr : p.xs + t0 * HB + hs / 128;
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)xs_rows, 0, SRC == KG_SRC_BF16 ? 0 : rows * HB * 4, kRsrcWord3);
+    // this thread's rows (rg, rg + RG, ...) of its 8 channels: every load is issued
+    // before any is used
 #pragma unroll
     for (int i = 0; i < kMaxRows; ++i) {
-      const int r = rg + RG * i;
-#pragma unroll
-      for (int k = 0; k < RAW; ++k) raw[i][k] = 0;
-      xsc[i] = 0.0f;
-      if (r < rows) {
-        const int64_t t = t0 + r;
-        if constexpr (SRC == KG_SRC_BF16) {
-          const v4i x = __builtin_nontemporal_load((const v4i*)(p.X + (t * p.H + h0) * 2));
-          raw[i][0] = (uint32_t)x.x;
-          raw[i][1] = (uint32_t)x.y;
-          raw[i][2] = (uint32_t)x.z;
-          raw[i][3] = (uint32_t)x.w;
-        } else {
-          const v2i x = __builtin_nontemporal_load((const v2i*)(p.X + t * p.H + h0));
-          raw[i][0] = (uint32_t)x.x;
-          raw[i][1] = (uint32_t)x.y;
-          xsc[i] = p.xs[t * (p.H / 128) + h0 / 128];
-        }
+      const int soff = i * RG * p.H * XB;
+      if constexpr (SRC == KG_SRC_BF16) {
+        const v4u x = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xoff, soff, 2 /* nt */);
+        raw[i][0] = x.x;
+        raw[i][1] = x.y;
+        raw[i][2] = x.z;
+        raw[i][3] = x.w;
+        xsc[i] = 0.0f;
+      } else {
+        const v2u x = __builtin_amdgcn_raw_buffer_load_b64(xr, (int)xoff, soff, 2 /* nt */);
+        raw[i][0] = x.x;
+        raw[i][1] = x.y;
+        xsc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               sr, rg * HB * 4, i * RG * HB * 4, 0));
       }
     }
-    float v[kMaxRows][8];
+    // binary32 values of row i (recomputed from the raw words in each pass, so that
+    // only the raw words stay live between the passes)
+    auto widen = [&](int i, float (&o)[8]) {
+      if constexpr (SRC == KG_SRC_BF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o[2 * k] = __builtin_bit_cast(float, raw[i][k] << 16);
+          o[2 * k + 1] = __builtin_bit_cast(float, raw[i][k] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const v2bf d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i][k], 1.0f, false);
+          const v2bf d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i][k], 1.0f, true);
+          o[4 * k + 0] = (float)d0[0] * xsc[i];
+          o[4 * k + 1] = (float)d0[1] * xsc[i];
+          o[4 * k + 2] = (float)d1[0] * xsc[i];
+          o[4 * k + 3] = (float)d1[1] * xsc[i];
+        }
+      }
+    };
     float amax[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) amax[c] = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxRows; ++i) {
-      if constexpr (SRC == KG_SRC_BF16) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[i][2 * k] = __builtin_bit_cast(float, raw[i][k] << 16);
-          v[i][2 * k + 1] = __builtin_bit_cast(float, raw[i][k] & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          // e4m3 decode (exact, through bf16), then one binary32 product per value
-          const v2bf d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i][k], 1.0f, false);
-          const v2bf d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i][k], 1.0f, true);
-          v[i][4 * k + 0] = (float)d0[0] * xsc[i];
-          v[i][4 * k + 1] = (float)d0[1] * xsc[i];
-          v[i][4 * k + 2] = (float)d1[0] * xsc[i];
-          v[i][4 * k + 3] = (float)d1[1] * xsc[i];
-        }
-      }
+      float o[8];
+      widen(i, o);
       // rows past the block are zeros here: they leave the maxima unchanged
 #pragma unroll
-      for (int c = 0; c < 8; ++c) amax[c] = __builtin_fmaxf(amax[c], __builtin_fabsf(v[i][c]));
+      for (int c = 0; c < 8; ++c) amax[c] = __builtin_fmaxf(amax[c], __builtin_fabsf(o[c]));
+    }
+    // the passes must not share their values (an empty asm that the compiler takes
+    // as rewriting the raw words: the values of the first pass die here)
+#pragma unroll
+    for (int i = 0; i < kMaxRows; ++i) {
+#pragma unroll
+      for (int k = 0; k < RAW; ++k) asm volatile("" : "+v"(raw[i][k]));
     }
     // column maxima: the 4 row groups of a wave share a channel group at lanes
-    // l, l + 16, l + 32, l + 48; at gran_k 128 then across the 4 waves through LDS
+    // l, l + 16, l + 32, l + 48; then across the slab's waves through LDS
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       amax[c] = __builtin_fmaxf(amax[c], __shfl_xor(amax[c], 16, 64));
       amax[c] = __builtin_fmaxf(amax[c], __shfl_xor(amax[c], 32, 64));
     }
-    if constexpr (GRAN == 128) {
+    if constexpr (WPS > 1) {
       if (lane < kQColGroups) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) red[w][cg * 8 + c] = amax[c];
@@ -256,9 +289,9 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
       __syncthreads();
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        float m = red[0][cg * 8 + c];
+        float m = red[slab * WPS][cg * 8 + c];
 #pragma unroll
-        for (int ww = 1; ww < kQThreads / 64; ++ww) m = __builtin_fmaxf(m, red[ww][cg * 8 + c]);
+        for (int ww = 1; ww < WPS; ++ww) m = __builtin_fmaxf(m, red[slab * WPS + ww][cg * 8 + c]);
         amax[c] = m;
       }
       __syncthreads();  // red is rewritten by the next item
@@ -282,10 +315,13 @@ __global__ __launch_bounds__(kQThreads) void kg_requant_kernel(QParams p) {
         exact |= amax[c] > 3.40282347e38f;
       }
     }
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.Q + t0 * p.H + hs), 0, rows * p.H, kRsrcWord3);
+    const uint32_t qoff = (uint32_t)(rg * p.H + cg * 8);
     if (exact)
-      store_codes<SK, true, kMaxRows, RG>(p, v, sdiv, mul, rg, rows, t0, h0);
+      store_codes<SK, true, kMaxRows, RG>(qr, p.H, qoff, widen, sdiv, mul);
     else
-      store_codes<SK, false, kMaxRows, RG>(p, v, sdiv, mul, rg, rows, t0, h0);
+      store_codes<SK, false, kMaxRows, RG>(qr, p.H, qoff, widen, sdiv, mul);
     if (rg == 0 && h0 < p.H) {
       if constexpr (SK == KG_E4M3_F32SCALE) {
         float4* dst = (float4*)((float*)p.S + (int64_t)b * p.H + h0);
@@ -317,7 +353,7 @@ extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int
   if (scale_kind != KG_E4M3_F32SCALE && scale_kind != KG_E4M3_UE8M0) return KG_ERR_DTYPE;
   if (G < 0 || H < 0 || K_total < 0) return KG_ERR_SHAPE;
   if (gran_k != 32 && gran_k != 128) return KG_ERR_GRAN;
-  if (G > kMaxGroups) return KG_ERR_UNSUPPORTED;
+  if (G > kMaxGroups || H > (1 << 23)) return KG_ERR_UNSUPPORTED;
   if (K_total > INT32_MAX || (int64_t)H * K_total > ((int64_t)1 << 46)) return KG_ERR_UNSUPPORTED;
   if (G == 0 || H == 0) return KG_OK;
   if (ks == nullptr) return KG_ERR_NULL;
@@ -362,10 +398,12 @@ extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int
   p.s_rows = s_rows;
   p.gran = gran_k;
   // items are not known on the host (they depend on ks): enough persistent
-  // workgroups for the largest case, eight per CU
-  const int tile = gran_k == 32 ? 512 : 128;  // channels per item
+  // workgroups for the largest case: 8192 threads per CU (more than stay resident;
+  // the rest start as resident ones finish)
+  const int slabs = q_slabs(src, gran_k), nt = slabs * q_wps(src, gran_k) * 64;
+  const int tile = kQCols * slabs;  // channels per item
   const int64_t max_items = ((K_total + (int64_t)G * (gran_k - 1)) / gran_k) * ((H + tile - 1) / tile);
-  const int64_t wgs = (int64_t)cus * 32;
+  const int64_t wgs = (int64_t)cus * 32 * 256 / nt;
   const int grid = (int)(max_items < wgs ? (max_items > 0 ? max_items : 1) : wgs);
   const void* fns[2][2][2] = {
       {{(const void*)kg_requant_kernel<KG_SRC_BF16, KG_E4M3_F32SCALE, 32>,
@@ -379,7 +417,7 @@ extern "C" int kg_requant(const void* X, const float* xs, const int32_t* ks, int
   const void* fn = fns[src == KG_SRC_BF16 ? 0 : 1][scale_kind == KG_E4M3_F32SCALE ? 0 : 1]
                       [gran_k == 32 ? 0 : 1];
   void* args[] = {&p};
-  e = hipLaunchKernel(fn, dim3(grid), dim3(kQThreads), args, sched_bytes(G), (hipStream_t)stream);
+  e = hipLaunchKernel(fn, dim3(grid), dim3(nt), args, sched_bytes(G), (hipStream_t)stream);
   if (e != hipSuccess) return KG_ERR_HIP;
   return KG_OK;
 }

@@ -293,7 +293,8 @@ int kg_max_groups(void);
  *
  * Errors (before any launch): KG_ERR_DTYPE, KG_ERR_SHAPE, KG_ERR_GRAN, KG_ERR_NULL,
  * KG_ERR_ALIGN, KG_ERR_ALIAS (outputs overlapping each other or an input),
- * KG_ERR_UNSUPPORTED (G > 1024), KG_ERR_SCALE_ROWS (s_rows < ceil(K_total / gran_k)),
+ * KG_ERR_UNSUPPORTED (G > 1024, H > 2^23, or H * K_total > 2^46), KG_ERR_SCALE_ROWS
+ * (s_rows < ceil(K_total / gran_k)),
  * KG_ERR_HIP. A ks that does not add up to K_total (KG_ERR_KSUM), or whose nblk
  * exceeds s_rows (KG_ERR_SCALE_ROWS), is reported by kg_status and nothing is
  * written. G == 0 or H == 0: KG_OK, no launch.

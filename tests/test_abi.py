@@ -161,6 +161,7 @@ def call_rq(X=FAKE, xs=None, ks=FAKE + (1 << 31), G=2, H=256, K=300, gran=128,
     (dict(H=-128), B.KG_ERR_SHAPE),
     (dict(gran=64), B.KG_ERR_GRAN),
     (dict(G=1025), B.KG_ERR_UNSUPPORTED),
+    (dict(H=(1 << 23) + 128, K=3), B.KG_ERR_UNSUPPORTED),  # 32-bit buffer offsets
     (dict(Q=None), B.KG_ERR_NULL),
     (dict(ks=None), B.KG_ERR_NULL),
     (dict(src=B.KG_SRC_E4M3_1X128), B.KG_ERR_NULL),      # 1x128 source without its scales
