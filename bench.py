@@ -78,13 +78,22 @@ for _m, _n, _k in ((4096, 2112, 7168), (4096, 24576, 1536), (4096, 32768, 512),
         f"fp8 e4m3 + fp32 scales per 128, no C")
 
 
-def kernel_source_hash():
-    """Hash of the kernel sources with comments and whitespace removed (a comment
+# The sources each kernel is built from (kgwgrad.hip includes the other two headers
+# at its end; the GEMM kernels do not use them).
+KERNEL_SOURCES = {
+    "kg_wgrad": ("kgwgrad.hip", "kg_device.h", "kg_sched.h"),
+    "kg_dgrad": ("kg_dgrad.h", "kgwgrad.hip", "kg_device.h", "kg_sched.h"),
+    "kg_requant": ("kg_requant.h", "kg_device.h", "kg_sched.h"),
+}
+
+
+def kernel_source_hash(kernel="kg_wgrad"):
+    """Hash of the kernel's sources with comments and whitespace removed (a comment
     edit does not change the kernels, so it does not invalidate stored counters)."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_grouped_gemm_tn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[kernel]):
         with open(os.path.join(csrc, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -101,7 +110,7 @@ def counters_for(workload, fast, bf16_out=False, kernel="kg_wgrad", nt=False):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source") != kernel_source_hash():
+    if rec.get("kernel_source") != kernel_source_hash(kernel):
         return None
     return rec.get("traffic_bytes")
 
@@ -149,7 +158,7 @@ def ingest_counters(fetch_csv, write_csv, name):
         per_launch = sorted(mine)[len(mine) // 2] * factor * 1024
         res[counter] = {"raw_kib_median": sorted(mine)[len(mine) // 2], "copy_kib": max(copy),
                         "scale": factor, "bytes_per_launch": per_launch}
-    rec = {"workload": name, "kernel_source": kernel_source_hash(),
+    rec = {"workload": name, "kernel_source": kernel_source_hash(kern),
            "traffic_bytes": int(res["FETCH_SIZE"]["bytes_per_launch"] +
                                 res["WRITE_SIZE"]["bytes_per_launch"]),
            "counters": res}
@@ -188,7 +197,7 @@ def ingest_mfma(csv_path, name, command):
     raw = {c: med(c) for c in MFMA_COUNTERS + ("duration_ns",)}
     busy = raw["SQ_VALU_MFMA_BUSY_CYCLES"] / (raw["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
     flops = (raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + raw["SQ_INSTS_VALU_MFMA_MOPS_F8"]) * 512
-    rec = {"workload": name, "kernel_source": kernel_source_hash(), "command": command,
+    rec = {"workload": name, "kernel_source": kernel_source_hash(kern), "command": command,
            "dispatches": len(mine),
            "mfma_busy_frac": round(busy, 4),
            "duration_ms_median": round(raw["duration_ns"] / 1e6, 4),
@@ -214,7 +223,7 @@ def mfma_counters_for(name, kernel="kg_wgrad"):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source") != kernel_source_hash():
+    if rec.get("kernel_source") != kernel_source_hash(kernel):
         return None
     return {"mfma_busy_frac": rec["mfma_busy_frac"],
             "mfma_flops_counted": rec["mfma_flops_counted"],

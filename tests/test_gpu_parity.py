@@ -588,6 +588,23 @@ def sampled_check(case, t, D, n=1500, seed=0, fast=False, tile=128):
             assert (D[g].view(torch.int32) == 0).all()
 
 
+@pytest.mark.parametrize("dtype,gran", [(F32, 128), (UE8, 32), (BF, 128)])
+def test_long_expert_random_data_within_accuracy_envelope(dtype, gran):
+    """An expert of 10^6 tokens of N(0, 1) data (the accuracy envelope's stated
+    length) beside a short one: sampled outputs within 1e-5 sum |ab| per element and
+    1e-5 in Frobenius norm of the oracle."""
+    say("long expert random data", dtype, gran)
+    ks = [1_000_000, 37]
+    case = inputs.make_case("long_random", ks, 64, 96, dtype, gran, with_c=True, seed=41,
+                            device="cuda")
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    torch.cuda.synchronize()
+    sampled_check(case, t, D, n=400, seed=5, tile=32)
+    del D, t, case
+    torch.cuda.empty_cache()
+
+
 # M or N at 2^24 (the largest accepted) and M x N at 2^29 (the largest expert output
 # whose byte offsets fit 32 bits): one stage's rows of a 2^24-wide operand span 2^31
 # bytes, and the epilogue's offsets in one expert's C reach 2^31.
