@@ -132,7 +132,7 @@ def _counter_rows(path):
     return out
 
 
-def ingest_counters(fetch_csv, write_csv, name):
+def ingest_counters(fetch_csv, write_csv, name, out_dir=None):
     """HBM bytes per launch of a kernel from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB plain copy
     recorded in the same CSV (run the profiled bench.py with --copy-calib). `name` is
@@ -162,7 +162,7 @@ def ingest_counters(fetch_csv, write_csv, name):
            "traffic_bytes": int(res["FETCH_SIZE"]["bytes_per_launch"] +
                                 res["WRITE_SIZE"]["bytes_per_launch"]),
            "counters": res}
-    path = os.path.join(ROOT, "profiles", f"{kern}_{name}_traffic.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern}_{name}_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -176,7 +176,7 @@ SIMDS = 4 * 256  # MI355X: 256 compute units of 4 SIMDs
 XCDS = 8  # GRBM counters come summed over the 8 XCDs' GRBMs
 
 
-def ingest_mfma(csv_path, name, command):
+def ingest_mfma(csv_path, name, command, out_dir=None):
     """MFMA utilisation of a kernel from one rocprofv3 --pmc pass over MFMA_COUNTERS
     (CSV): per dispatch (median over the kernel's dispatches) the MFMA-busy fraction
     SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDS x SIMDs) (rocprofv3's MfmaUtil,
@@ -210,7 +210,7 @@ def ingest_mfma(csv_path, name, command):
            "lds_bank_conflict_per_active": round(raw["SQ_LDS_BANK_CONFLICT"] /
                                                  max(raw["SQ_LDS_IDX_ACTIVE"], 1.0), 4),
            "counters_median": raw}
-    path = os.path.join(ROOT, "profiles", f"{kern}_{name}_mfma.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern}_{name}_mfma.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
