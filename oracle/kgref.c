@@ -173,7 +173,9 @@ static inline double scale_of(const problem_t* p, const void* s, int64_t r, int 
 }
 
 static inline int block_len(const problem_t* p) {
-  /* bf16 carries no scales: the whole group is one accumulation. */
+  /* Tokens per block partial. bf16 carries no scales (every scale is 1), so its runs
+   * of gran_k tokens only split the fp64 sum of exact products: the same sum up to
+   * fp64 rounding. */
   return p->gran_k;
 }
 
