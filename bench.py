@@ -384,22 +384,12 @@ def requant_main(args):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl, H, gran, kind, src, descr = REQUANT[args.requant]
+    assert inputs.REQUANT_WORKLOADS[args.requant] == (wl, H, gran, kind, src)
     dev = torch.device("cuda:0")
     copy_calibration(args, dev)
-    ks = inputs.workload_ks(wl, args.seed)
+    X, xs, ks = inputs.requant_source(args.requant, device=dev, seed=args.seed)
     K = int(ks.astype(np.int64).sum())
     nblk = int(sum((int(k) + gran - 1) // gran for k in ks))
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(args.seed)
-    x = torch.randn((K, H), generator=gen, device=dev)
-    if src == kg.KG_SRC_BF16:
-        X, xs = x.to(torch.bfloat16), None
-    else:  # the forward pass's copy: e4m3 with one fp32 scale per token per 128 channels
-        amax = x.abs().view(K, H // 128, 128).amax(dim=2).clamp_min(1e-30)
-        xs = (amax / 448.0).float()
-        X = (x.view(K, H // 128, 128) / xs[:, :, None]).view(K, H).to(torch.float8_e4m3fn)
-        X = X.view(torch.uint8)
-    del x
     ksd = torch.from_numpy(ks).to(dev)
     Q = torch.empty((K, H), dtype=torch.uint8, device=dev)
     S = torch.empty((nblk, H), dtype=torch.float32 if kind == kg.KG_E4M3_F32SCALE else torch.uint8,
@@ -441,17 +431,26 @@ def requant_main(args):
     }
     if not args.no_cpu:
         from oracle import kgref
-        # the oracle on the first expert's first blocks (all channels), ~10 s of CPU
-        g0 = int(np.argmax(ks > 0))
-        rows = min(int(ks[g0]), 4 * gran)
-        t0 = int(ks[:g0].astype(np.int64).sum())
+        # the oracle on the leading experts whose tokens fit in 32768 rows (all
+        # channels; at least the first expert's first 4 blocks): several seconds of CPU
+        ks64 = ks.astype(np.int64)
+        ne = 1
+        while ne < ks.size and ks64[:ne + 1].sum() <= 32768:
+            ne += 1
+        ks_sub = [int(k) for k in ks[:ne]]
+        g0 = 0
+        rows = int(sum(ks_sub))
+        if rows > 32768 or ne == 1:
+            rows = min(int(ks[0]), 32768)
+            ks_sub = [rows]
+        t0 = 0
         Xr = X[t0:t0 + rows]
         Xs = np.ascontiguousarray((Xr.view(torch.int16) if src == kg.KG_SRC_BF16 else Xr).cpu().numpy())
         if src == kg.KG_SRC_BF16:
             Xs = Xs.view(np.uint16)
         sub = lambda a: None if a is None else np.ascontiguousarray(a[t0:t0 + rows].cpu().numpy())
         tt = time.perf_counter()
-        rc, _, _ = kgref.requant(Xs, sub(xs), [rows], H, gran,
+        rc, _, _ = kgref.requant(Xs, sub(xs), ks_sub, H, gran,
                                  kgref.SRC_BF16 if src == kg.KG_SRC_BF16 else kgref.SRC_E4M3_1X128,
                                  kgref.SCALE_F32 if kind == kg.KG_E4M3_F32SCALE else kgref.SCALE_UE8M0)
         dt = time.perf_counter() - tt
@@ -459,8 +458,8 @@ def requant_main(args):
         sb = rows * H * (2 if src == kg.KG_SRC_BF16 else 1) + rows * H
         line["cpu_baseline"] = {"value": round(sb / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
                                 "kind": "oracle",
-                                "sample": f"expert {g0}, rows 0..{rows - 1}, all {H} channels: "
-                                          f"{sb / 1e6:.1f} MB in {dt:.2f} s"}
+                                "sample": f"experts 0..{len(ks_sub) - 1} (token rows 0..{rows - 1}), "
+                                          f"all {H} channels: {sb / 1e6:.1f} MB in {dt:.2f} s"}
     print(json.dumps(line), flush=True)
 
 

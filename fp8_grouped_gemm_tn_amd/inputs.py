@@ -492,3 +492,33 @@ def requant_edge_fp8_source(K, H, seed=0):
     xs[-80:] = np.float32(2.0 ** -149)
     xs[-80::2] = np.float32(0.0)
     return codes, xs
+
+
+# Requantiser workloads: (routing workload, H, gran_k, scale kind, source kind), the
+# kinds as in the C ABI (scale: 0 fp32, 1 UE8M0; source: 0 bf16, 1 e4m3 with 1x128
+# per-token scales)
+REQUANT_WORKLOADS = {
+    "local_share_A": ("local_share", 7168, 128, 0, 0),
+    "local_share_A_fp8": ("local_share", 7168, 128, 0, 1),
+    "ue8m0_many_B": ("ue8m0_many", 7168, 32, 1, 0),
+}
+
+
+def requant_source(name, device="cpu", seed=0):
+    """The requantiser's source for a named workload: (X, xs, ks). X is N(0, 1) values
+    [tokens, H] as bf16, or (source kind 1) as the forward pass's e4m3 copy with one
+    fp32 scale per token per 128 channels (amax / 448, amax floored at 1e-30), xs
+    [tokens, H / 128]; ks the workload's routing (numpy int32)."""
+    wl, H, gran, kind, src = REQUANT_WORKLOADS[name]
+    ks = workload_ks(wl, seed)
+    K = int(ks.astype(np.int64).sum())
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    x = torch.randn((K, H), generator=gen, device=dev)
+    if src == 0:
+        return x.to(torch.bfloat16), None, ks
+    amax = x.abs().view(K, H // 128, 128).amax(dim=2).clamp_min(1e-30)
+    xs = (amax / FP8_MAX).float()
+    X = (x.view(K, H // 128, 128) / xs[:, :, None]).view(K, H).to(torch.float8_e4m3fn)
+    return X.view(torch.uint8), xs, ks

@@ -190,3 +190,49 @@ def test_requant_feeds_wgrad():
     for gi in (0, 2):
         rel = (D[gi].cpu() - ref[gi]).norm() / ref[gi].norm()
         assert rel < 0.1, float(rel)
+
+
+@pytest.mark.parametrize("name", list(inputs.REQUANT_WORKLOADS))
+def test_requant_full_size_sampled_blocks(name):
+    """The bench workloads at full size, in the launch configuration bench.py times:
+    16 random blocks (scale rows) plus the first and last block of three experts are
+    compared bit for bit (codes and scales, all channels) with the oracle run on just
+    those blocks' token rows."""
+    say("requant full size", name)
+    wl, H, gran, kind, src = inputs.REQUANT_WORKLOADS[name]
+    d = torch.device("cuda:0")
+    X, xs, ks = inputs.requant_source(name, device=d, seed=0)
+    K = int(ks.astype(np.int64).sum())
+    nblk = int(sum((int(k) + gran - 1) // gran for k in ks))
+    Q = torch.empty((K, H), dtype=torch.uint8, device=d)
+    S = torch.empty((nblk, H), dtype=torch.float32 if kind == kg.KG_E4M3_F32SCALE else torch.uint8,
+                    device=d)
+    rc = kg.kg_requant_raw(X, xs, torch.from_numpy(ks).to(d), ks.size, H, K, gran, src, kind, Q, S)
+    assert rc == kg.KG_OK
+    assert kg.kg_status() == kg.KG_OK
+    # blocks: (scale row, first token, tokens)
+    off = np.concatenate([[0], np.cumsum(ks.astype(np.int64))])
+    blocks = []
+    for g in range(ks.size):
+        for kb in range((int(ks[g]) + gran - 1) // gran):
+            t0 = int(off[g]) + kb * gran
+            blocks.append((len(blocks), t0, min(gran, int(off[g + 1]) - t0)))
+    rng = np.random.default_rng(11)
+    pick = set(rng.choice(len(blocks), 16, replace=False).tolist())
+    live = np.nonzero(ks > 0)[0]
+    for g in live[[0, live.size // 2, -1]]:
+        first = int(sum((int(k) + gran - 1) // gran for k in ks[:g]))
+        pick |= {first, first + (int(ks[g]) + gran - 1) // gran - 1}
+    for b in sorted(pick):
+        row, t0, n = blocks[b]
+        Xh = X[t0:t0 + n].cpu()
+        Xh = (Xh.view(torch.int16).numpy().view(np.uint16) if src == kg.KG_SRC_BF16
+              else Xh.numpy())
+        xsh = None if xs is None else np.ascontiguousarray(xs[t0:t0 + n].cpu().numpy())
+        rc, Qr, Sr = kgref.requant(Xh, xsh, [n], H, gran, SRC[src], KIND[kind])
+        assert rc == kgref.OK
+        assert np.array_equal(Q[t0:t0 + n].cpu().numpy(), Qr), f"block {b}: codes differ"
+        assert np.array_equal(S[row].cpu().numpy().view(np.uint8), Sr[0].view(np.uint8)), \
+            f"block {b}: scales differ"
+    del X, xs, Q, S
+    torch.cuda.empty_cache()
