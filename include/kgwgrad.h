@@ -236,7 +236,7 @@ int64_t kg_wgrad_workspace_flag_bytes(void);
  * kg_status recorded (KG_ERR_KSUM, KG_ERR_SCALE_ROWS, KG_ERR_SCALE_RANGE). The how-to
  * page ("Dispatch and Tensor-Map Handling") has the host check the per-expert counts
  * against the operands before any work; with the counts in device memory that check
- * runs in the kernel, which writes nothing on a mismatch and leaves the verdict here.
+ * runs in the kernel, which writes nothing on a mismatch and leaves its result here.
  * Returns KG_ERR_HIP if the stream reports an error.
  */
 int kg_status(void* stream);
