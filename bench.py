@@ -768,8 +768,31 @@ def worked_shape_timing(kg, inputs, calls=400):
         singles.append(a.elapsed_time(b))
     assert kg.kg_status() == kg.KG_OK
     singles.sort()
+    # 20 calls captured in a HIP graph and replayed: the device-side time per call
+    # without the Python binding's per-call work
+    per_graph, replays = 20, 25
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    b.record(stream)
+    b.synchronize()
+    us_graph = a.elapsed_time(b) * 1e3 / (replays * per_graph)
+    assert kg.kg_status() == kg.KG_OK
     return {"workload": DESCR["worked"], "us_per_call_back_to_back": round(ms * 1e3, 2),
             "us_single_call_events": round(singles[len(singles) // 2] * 1e3, 2),
+            "us_per_call_graph_replay": round(us_graph, 2),
             "flops": c.flops, "bound": "launch latency"}
 
 
