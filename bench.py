@@ -209,6 +209,10 @@ def ingest_mfma(csv_path, name, command, out_dir=None):
            "mfma_flops_f8": raw["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512,
            "lds_bank_conflict_per_active": round(raw["SQ_LDS_BANK_CONFLICT"] /
                                                  max(raw["SQ_LDS_IDX_ACTIVE"], 1.0), 4),
+           # SQ_ACTIVE_INST_VALU counts, summed over waves, the 4-cycle units in which a
+           # wave issues VALU instructions (MFMA issue included): per SIMD cycle
+           "valu_issue_frac": round(4 * raw["SQ_ACTIVE_INST_VALU"] /
+                                    (raw["GRBM_GUI_ACTIVE"] / XCDS * SIMDS), 4),
            "counters_median": raw}
     path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern}_{name}_mfma.json")
     with open(path, "w") as f:
