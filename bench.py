@@ -233,6 +233,7 @@ def mfma_counters_for(name, kernel="kg_wgrad"):
             "mfma_flops_counted": rec["mfma_flops_counted"],
             "shader_clock_ghz": rec["shader_clock_ghz"],
             "lds_bank_conflict_per_active": rec["lds_bank_conflict_per_active"],
+            "valu_issue_frac": rec.get("valu_issue_frac"),
             "source": os.path.relpath(path, ROOT)}
 
 
