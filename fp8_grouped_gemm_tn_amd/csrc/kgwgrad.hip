@@ -949,8 +949,11 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
   };
   // One column jn of sub-tiles at a time: its NI partial sums are NI independent MFMA
   // chains advanced together (step kk of every chain before step kk + 1 of any), so
-  // no MFMA waits for the result of the one before it; the previous column's
-  // rescale runs between this column's first MFMAs.
+  // no MFMA waits for the result of the one before it. With at most four columns per
+  // wave the previous column's rescale runs between this column's first MFMAs; with
+  // more, each column is rescaled right after its MFMAs, which frees the registers
+  // of the deferred partial sums (the 64 x 128 wave tile would spill otherwise).
+  constexpr bool DEFER = CF::NJ <= 4;
   v2i rnext[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) rnext[kk] = rdb(0, kk);
@@ -970,7 +973,7 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
 #pragma unroll
       for (int i = 0; i < CF::NI; ++i)
         x[i] = mfma_bf16(af[i][kk], bf[kk], kk == 0 ? part[i][jn] : x[i]);
-      if (PROMOTE && kk == 0 && jn > 0) {
+      if (DEFER && PROMOTE && kk == 0 && jn > 0) {
 #pragma unroll
         for (int i = 0; i < CF::NI; ++i) rescale(i, jn - 1, xprev[i]);
       }
@@ -978,14 +981,17 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
 #pragma unroll
     for (int i = 0; i < CF::NI; ++i) {
       if constexpr (PROMOTE) {
-        xprev[i] = x[i];
+        if constexpr (DEFER)
+          xprev[i] = x[i];
+        else
+          rescale(i, jn, x[i]);
         part[i][jn] = v4f{0.f, 0.f, 0.f, 0.f};
       } else {
         part[i][jn] = x[i];
       }
     }
   }
-  if constexpr (PROMOTE) {
+  if constexpr (PROMOTE && DEFER) {
 #pragma unroll
     for (int i = 0; i < CF::NI; ++i) rescale(i, CF::NJ - 1, xprev[i]);
   }
@@ -1694,9 +1700,13 @@ static Launch pick_outb(int kind, bool fast, bool small, bool deep) {
 }
 
 template <bool NT>
-static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb, bool deep) {
+static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb, bool deep,
+                     bool wide) {
   using S = Cfgs<NT>;
   if (outb) return pick_outb<NT>(kind, fast, small, deep);
+  if constexpr (!NT) {
+    if (wide && kind == F32S && !fast && !split) return launch_of<F32S, false, typename S::F8>();
+  }
   if (kind == F32S32)
     return fast ? (split ? launch_of<F32S32, true, typename S::F8h32, true>()
                          : launch_of<F32S32, true, typename S::F8h32>())
@@ -1725,9 +1735,9 @@ static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb, boo
 // full-size tiles; outb: bf16 D; nt: K-major operands; deep: the three-stage precise
 // fp32-scale tile (token-major) when its stages and the schedule fit the LDS
 static Launch pick(int kind, bool fast, bool small = false, bool split = false,
-                   bool outb = false, bool nt = false, bool deep = false) {
-  return nt ? pick_t<true>(kind, fast, small, split, outb, deep)
-            : pick_t<false>(kind, fast, small, split, outb, deep);
+                   bool outb = false, bool nt = false, bool deep = false, bool wide = false) {
+  return nt ? pick_t<true>(kind, fast, small, split, outb, deep, wide)
+            : pick_t<false>(kind, fast, small, split, outb, deep, wide);
 }
 
 // Dynamic LDS a workgroup may take on gfx950: 160 KB less 1 KB for the kernels' static
@@ -1773,12 +1783,13 @@ static int device_setup(int dev) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     // every kernel the launches can pick: layouts x kinds x modes
     const int kinds[4] = {F32S, E8M0, BF16, F32S32};
-    for (int v = 0; v < 2 * 4 * 2 * 2 * 2 * 2 * 2; ++v) {
+    for (int v = 0; v < 2 * 4 * 2 * 2 * 2 * 2 * 2 * 2; ++v) {
       const bool nt = v & 1, fast = (v >> 3) & 1, small = (v >> 4) & 1;
       const bool split = (v >> 5) & 1, outb = (v >> 6) & 1, deep = (v >> 7) & 1;
+      const bool wide = (v >> 8) & 1;
       const int kind = kinds[(v >> 1) & 3];
       if ((fast && kind == BF16) || (split && outb)) continue;
-      const Launch l = pick(kind, fast, small, split, outb, nt, deep);
+      const Launch l = pick(kind, fast, small, split, outb, nt, deep, wide);
       const int lds = l.stage_bytes + sched_bytes(kMaxGroups);
       e = hipFuncSetAttribute(l.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                               lds < kMaxLds ? lds : kMaxLds);
@@ -1923,7 +1934,13 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
   const bool split = workspace != nullptr && G <= kMaxSplitGroups && !out_bf16 &&
                      (size_t)workspace_bytes >= split_ws_bytes(cus) &&
                      (2 * T <= (int64_t)cus || 10 * T < 7 * rounds * (int64_t)cus);
-  const Launch L = pick(kind, fast, small && !split, split, out_bf16, nt, deep_fits(G));
+  // precise fp32 scales, long experts (on average at least 4096 tokens): 256 x 256
+  // tiles, which widen fewer fp8 values per MFMA; shorter experts (and their C) keep
+  // the 256 x 128 tile, whose smaller work items balance better
+  const bool wide = kind == F32S && !fast && !split && !out_bf16 && !nt &&
+                    K_total >= (int64_t)4096 * G &&
+                    CfgF8::NS * CfgF8::STAGE + sched_bytes(G) <= kMaxLds;
+  const Launch L = pick(kind, fast, small && !split, split, out_bf16, nt, deep_fits(G), wide);
   const int tiles_m = (M + L.bm - 1) / L.bm, tiles_n = (N + L.bn - 1) / L.bn;
   const int64_t total = (int64_t)G * tiles_m * tiles_n;
   if (total > INT32_MAX) return KG_ERR_UNSUPPORTED;

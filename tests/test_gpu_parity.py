@@ -588,6 +588,23 @@ def sampled_check(case, t, D, n=1500, seed=0, fast=False, tile=128):
             assert (D[g].view(torch.int32) == 0).all()
 
 
+@pytest.mark.parametrize("with_c", [True, False])
+def test_wide_precise_tile_for_long_experts(with_c):
+    """fp32 scales per 128 tokens, precise mode, experts of 4096+ tokens on average:
+    the 256 x 256 tile (KG_PRINT_CONFIG names it), with partial tiles in M and N, an
+    empty and a one-token expert, against the full oracle."""
+    say("wide precise tile", with_c)
+    case = small_case(F32, 128, [9000, 0, 8200, 1], 320, 272, with_c=with_c, seed=17)
+    t = to_dev(case)
+    D = run_gpu(case, t)
+    D_ref, bound = oracle_full(case)
+    check_close(D, D_ref, bound, "wide precise tile")
+    if case.C is not None:
+        assert torch.equal(D[1].view(torch.int32), t["C"][1].view(torch.int32))
+    else:
+        assert (D[1].view(torch.int32) == 0).all()
+
+
 @pytest.mark.parametrize("dtype,gran", [(F32, 128), (UE8, 32), (BF, 128)])
 def test_long_expert_random_data_within_accuracy_envelope(dtype, gran):
     """An expert of 10^6 tokens of N(0, 1) data (the accuracy envelope's stated
@@ -792,12 +809,18 @@ def test_print_config_switch():
         "c = inputs.workload('worked', device='cuda')\n"
         "D = torch.empty((c.G, c.M, c.N), device='cuda')\n"
         "kg.kg_wgrad(c.A, c.sa, c.B, c.sb, None, D, torch.from_numpy(c.ks).cuda(), 128, c.dtype)\n"
+        "assert kg.kg_status() == kg.KG_OK\n"
+        "w = inputs.make_case('long', [4096], 64, 128, c.dtype, 128, with_c=False, device='cuda')\n"
+        "Dw = torch.empty((1, 64, 128), device='cuda')\n"
+        "kg.kg_wgrad(w.A, w.sa, w.B, w.sb, None, Dw, torch.from_numpy(w.ks).cuda(), 128, w.dtype)\n"
         "assert kg.kg_status() == kg.KG_OK\n")
     env = dict(os.environ, KG_PRINT_CONFIG="1", PYTHONPATH=root)
     res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          timeout=300, cwd=root)
     assert res.returncode == 0, res.stderr[-2000:]
     lines = [l for l in res.stderr.splitlines() if l.startswith("kgwgrad:")]
-    assert len(lines) == 1, res.stderr[-2000:]
+    assert len(lines) == 2, res.stderr[-2000:]
     assert "token-major e4m3+f32 gran 128 precise G 3 M 64 N 128 K_total 104" in lines[0]
     assert "whole tiles" in lines[0] and "tile 256x128" in lines[0]
+    # 4096 tokens per expert: the wide precise tile
+    assert "precise G 1 M 64 N 128 K_total 4096" in lines[1] and "tile 256x256" in lines[1]
