@@ -1704,9 +1704,7 @@ static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb, boo
                      bool wide) {
   using S = Cfgs<NT>;
   if (outb) return pick_outb<NT>(kind, fast, small, deep);
-  if constexpr (!NT) {
-    if (wide && kind == F32S && !fast && !split) return launch_of<F32S, false, typename S::F8>();
-  }
+  if (wide && kind == F32S && !fast && !split) return launch_of<F32S, false, typename S::F8>();
   if (kind == F32S32)
     return fast ? (split ? launch_of<F32S32, true, typename S::F8h32, true>()
                          : launch_of<F32S32, true, typename S::F8h32>())
@@ -1935,9 +1933,9 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
                      (size_t)workspace_bytes >= split_ws_bytes(cus) &&
                      (2 * T <= (int64_t)cus || 10 * T < 7 * rounds * (int64_t)cus);
   // precise fp32 scales, long experts (on average at least 4096 tokens): 256 x 256
-  // tiles, which widen fewer fp8 values per MFMA; shorter experts (and their C) keep
-  // the 256 x 128 tile, whose smaller work items balance better
-  const bool wide = kind == F32S && !fast && !split && !out_bf16 && !nt &&
+  // tiles, which widen fewer fp8 values per MFMA (either layout); shorter experts (and
+  // their C) keep the 256 x 128 tile, whose smaller work items balance better
+  const bool wide = kind == F32S && !fast && !split && !out_bf16 &&
                     K_total >= (int64_t)4096 * G &&
                     CfgF8::NS * CfgF8::STAGE + sched_bytes(G) <= kMaxLds;
   const Launch L = pick(kind, fast, small && !split, split, out_bf16, nt, deep_fits(G), wide);

@@ -86,6 +86,26 @@ def test_nt_ragged_matches_oracle_and_token_major(dtype, gran, flags):
         assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
 
 
+def test_nt_wide_precise_tile_for_long_experts():
+    """fp32 scales, precise mode, experts of 4096+ tokens on average (the 256 x 256
+    tile) with K-major operands, unaligned expert starts and partial tiles: the oracle,
+    and the token-major kernel's bits."""
+    say("nt wide precise tile")
+    ks = [9001, 0, 8200, 3]
+    case = small_case(F32, 128, ks, 320, 272, with_c=True, seed=23)
+    t = to_dev(case)
+    At, Bt = nt_dev(case, t)
+    D = run_nt(case, t, At, Bt, 0)
+    D_ref, bound = nt_oracle(case, At, Bt)
+    check_close(D, D_ref, bound, "nt wide")
+    assert torch.equal(D[1].cpu().view(torch.int32), case.C[1].view(torch.int32))
+    if same_order(F32, 128, 0):
+        D_tn = torch.full_like(D, float("nan"))
+        kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], t["C"], D_tn, t["ks"], 128, F32)
+        torch.cuda.synchronize()
+        assert torch.equal(D.view(torch.int32), D_tn.view(torch.int32))
+
+
 @pytest.mark.parametrize("dtype,gran,flags", [(F32, 128, 0), (UE8, 32, FAST), (BF, 128, 0)])
 def test_nt_every_tail_length(dtype, gran, flags):
     # one expert per tail length 1..16 (mod 16) after an unaligned start, no C
@@ -162,7 +182,7 @@ def test_nt_ksum_mismatch_is_reported_and_writes_nothing():
     assert torch.isnan(D).all()
 
 
-@pytest.mark.parametrize("name", ["bf16", "zipf_fp8", "ue8m0_many"])
+@pytest.mark.parametrize("name", ["bf16", "zipf_fp8", "ue8m0_many", "local_share"])
 def test_nt_full_size_sampled(name):
     """Full-size workloads with K-major operands (the layout transposed on the GPU),
     in the configuration bench.py --nt times, sampled against the oracle on the
