@@ -1683,8 +1683,9 @@ static Launch launch_of() {
 
 // bf16 output (whole tiles only: stream-K is not taken with a bf16 D)
 template <bool NT>
-static Launch pick_outb(int kind, bool fast, bool small, bool deep) {
+static Launch pick_outb(int kind, bool fast, bool small, bool deep, bool wide) {
   using S = Cfgs<NT>;
+  if (wide && kind == F32S && !fast) return launch_of<F32S, false, typename S::F8, false, true>();
   if (kind == F32S32)
     return fast ? launch_of<F32S32, true, typename S::F8h32, false, true>()
                 : launch_of<F32S32, false, typename S::F8h32, false, true>();
@@ -1703,7 +1704,7 @@ template <bool NT>
 static Launch pick_t(int kind, bool fast, bool small, bool split, bool outb, bool deep,
                      bool wide) {
   using S = Cfgs<NT>;
-  if (outb) return pick_outb<NT>(kind, fast, small, deep);
+  if (outb) return pick_outb<NT>(kind, fast, small, deep, wide);
   if (wide && kind == F32S && !fast && !split) return launch_of<F32S, false, typename S::F8>();
   if (kind == F32S32)
     return fast ? (split ? launch_of<F32S32, true, typename S::F8h32, true>()
@@ -1935,7 +1936,7 @@ static int wgrad_run(bool nt, const void* A, int64_t lda, const void* sa, const 
   // precise fp32 scales, long experts (on average at least 4096 tokens): 256 x 256
   // tiles, which widen fewer fp8 values per MFMA (either layout); shorter experts (and
   // their C) keep the 256 x 128 tile, whose smaller work items balance better
-  const bool wide = kind == F32S && !fast && !split && !out_bf16 &&
+  const bool wide = kind == F32S && !fast && !split &&
                     K_total >= (int64_t)4096 * G &&
                     CfgF8::NS * CfgF8::STAGE + sched_bytes(G) <= kMaxLds;
   const Launch L = pick(kind, fast, small && !split, split, out_bf16, nt, deep_fits(G), wide);

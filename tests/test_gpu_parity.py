@@ -605,6 +605,22 @@ def test_wide_precise_tile_for_long_experts(with_c):
         assert (D[1].view(torch.int32) == 0).all()
 
 
+def test_wide_precise_tile_bf16_output():
+    """The wide precise tile with bf16 C and D: every output within its rounding
+    interval of the oracle; the empty expert passes C through bit for bit."""
+    say("wide precise tile, bf16 output")
+    case = small_case(F32, 128, [9000, 0, 8200, 1], 320, 272, with_c=True, seed=18)
+    t = to_dev(case)
+    Cb = t["C"].to(torch.bfloat16)
+    D = torch.full((case.G, case.M, case.N), float("nan"), dtype=torch.bfloat16, device=dev())
+    kg.kg_wgrad(t["A"], t["sa"], t["B"], t["sb"], Cb, D, t["ks"], 128, F32, K_total=case.K_total)
+    assert kg.kg_status() == kg.KG_OK
+    torch.cuda.synchronize()
+    D_ref, bound = oracle_full(case, C=Cb.float().cpu().numpy().astype(np.float32))
+    check_bf16_out(D, D_ref, bound, "wide bf16 out")
+    assert torch.equal(D[1].view(torch.int16), Cb[1].view(torch.int16))
+
+
 @pytest.mark.parametrize("dtype,gran", [(F32, 128), (UE8, 32), (BF, 128)])
 def test_long_expert_random_data_within_accuracy_envelope(dtype, gran):
     """An expert of 10^6 tokens of N(0, 1) data (the accuracy envelope's stated
