@@ -72,3 +72,33 @@ def test_random_configuration(seed):
         # the workspace's arrival counters are back at zero after the call
         nflag = kg.kg_wgrad_workspace_flag_bytes()
         assert (ws[:nflag] == 0).all()
+
+
+@pytest.mark.parametrize("seed", range(100, 124))
+def test_random_configuration_k_major(seed):
+    """The same random draws through kg_wgrad_nt: K-major copies of A and B in rows
+    padded (by a seeded amount) with NaN codes, so that a read past an expert's tokens
+    or into the padding shows, against the oracle's K-major entry."""
+    from tests.test_gpu_nt import nt_oracle, run_nt
+    cfg = draw(seed)
+    say("random k-major config", seed, {k: v for k, v in cfg.items() if k != "ks"}, "G",
+        len(cfg["ks"]), "tokens", sum(cfg["ks"]))
+    case = inputs.make_case("random", cfg["ks"], cfg["M"], cfg["N"], cfg["dtype"], cfg["gran"],
+                            with_c=cfg["with_c"], seed=seed)
+    t = to_dev(case)
+    rng = np.random.default_rng(seed)
+    At = inputs.k_major(t["A"], int(rng.integers(0, 40)))
+    Bt = inputs.k_major(t["B"], int(rng.integers(0, 40)))
+    flags = FAST if cfg["fast"] else 0
+    ws = kg.new_workspace(dev()) if cfg["use_ws"] else None
+    out = torch.bfloat16 if cfg["bf16_out"] else torch.float32
+    D = run_nt(case, t, At, Bt, flags, out=out, workspace=ws)
+    if cfg["bf16_out"]:
+        Ch = None if case.C is None else t["C"].to(torch.bfloat16).float().cpu().numpy()
+        D_ref, bound = nt_oracle(case, At, Bt, C=Ch)
+        check_bf16_out(D, D_ref, bound, f"random k-major {seed}", fast=cfg["fast"])
+    else:
+        D_ref, bound = nt_oracle(case, At, Bt)
+        check_close(D, D_ref, bound, f"random k-major {seed}", fast=cfg["fast"])
+    if ws is not None:
+        assert (ws[:kg.kg_wgrad_workspace_flag_bytes()] == 0).all()
