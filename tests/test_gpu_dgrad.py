@@ -190,3 +190,37 @@ def test_dgrad_size_limits_sampled(ms, N, K, flags, out):
     sampled(c, t, flags, out, n=60, seed=N ^ K)
     del t, c
     torch.cuda.empty_cache()
+
+
+def draw_dgrad(seed):
+    """A seeded random dgrad configuration: expert count, rows per expert (long, short
+    with empty and one-row experts, or heavy-tailed), N and K (multiples of 128), mode
+    and output type."""
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.integers(1, 65))
+    style = rng.integers(0, 3)
+    if style == 0:
+        ms = rng.integers(0, 700, G)
+    elif style == 1:
+        ms = rng.choice([0, 1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257], G)
+    else:
+        ms = np.minimum((rng.pareto(1.2, G) * 50).astype(np.int64), 2000)
+    ms[rng.random(G) < 0.15] = 0
+    N = 128 * int(rng.integers(1, 7))
+    K = 128 * int(rng.integers(1, 9))
+    flags = FAST if rng.random() < 0.4 else 0
+    out = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    return [int(m) for m in ms], N, K, flags, out
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_dgrad_random_configuration(seed):
+    ms, N, K, flags, out = draw_dgrad(seed)
+    say("dgrad random", seed, "G", len(ms), "rows", sum(ms), N, K, flags, out)
+    c = inputs.make_dgrad_case("t", ms, N, K, seed=seed)
+    t = to_dev(c)
+    D = run(c, t, flags, out)
+    h = c.host()
+    rc, ref, bound = kgref.dgrad(h["A"], h["sa"], h["W"], h["sw"], h["ms"], c.N, c.K)
+    assert rc == kgref.OK
+    check(D, ref, bound, fast=bool(flags), what=f"dgrad random {seed}")
