@@ -236,3 +236,26 @@ def test_requant_full_size_sampled_blocks(name):
             f"block {b}: scales differ"
     del X, xs, Q, S
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_requant_random_configuration(seed):
+    """Seeded random requantiser configurations, bit-exact against the oracle: source,
+    scale kind, block size, expert count and token counts (long, short with empty and
+    one-token experts, or heavy-tailed) and channel count."""
+    rng = np.random.default_rng(3000 + seed)
+    src = [kg.KG_SRC_BF16, kg.KG_SRC_E4M3_1X128][seed % 2]
+    kind = [kg.KG_E4M3_F32SCALE, kg.KG_E4M3_UE8M0][(seed // 2) % 2]
+    gran = [32, 128][(seed // 4) % 2]
+    G = int(rng.integers(1, 65))
+    style = rng.integers(0, 3)
+    if style == 0:
+        ks = rng.integers(0, 600, G)
+    elif style == 1:
+        ks = rng.choice([0, 1, 2, 31, 32, 33, 127, 128, 129], G)
+    else:
+        ks = np.minimum((rng.pareto(1.2, G) * 40).astype(np.int64), 2000)
+    ks[rng.random(G) < 0.15] = 0
+    H = 128 * int(rng.integers(1, 9))
+    say("requant random", seed, src, kind, gran, "G", G, "tokens", int(ks.sum()), "H", H)
+    run_case(src, kind, gran, [int(k) for k in ks], H, seed)
