@@ -177,7 +177,8 @@ using CfgF8 = Cfg<256, 256, 4, 128, 2, 1, 1024>;
 // fp8 widened to bf16 with fp32 scales: 256 x 128 per workgroup, 64 x 64 per wave (the
 // widened fragments and the block partials need the registers a wider wave tile would
 // take; UE8M0 scales, folded into the widening, need no partials and use CfgF8: 17%
-// faster on 256 experts); two stages of 128
+// faster on 256 experts); two stages of 128. Long experts take CfgF8 instead, each
+// column of sub-tiles rescaled right after its MFMAs (fewer conversions per MFMA).
 using CfgF8h = Cfg<256, 128, 4, 128, 2, 1, 1024>;
 // CfgF8h with three stages in the LDS the row padding took (swizzled rows): two stages in
 // flight instead of one, for problems whose schedule leaves the LDS room (the kernel's
