@@ -1495,11 +1495,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
   }
   // Workgroup b runs on XCD b % 8. With several rounds of items, each XCD takes a
   // contiguous run of every round (neighbouring tiles that share operand rows in
-  // its L2), the runs of odd rounds in reverse XCD order. When all items fit in one
-  // round, XCD x takes the x-th eighth of the GEMM tiles (a contiguous run: mostly one
-  // expert, sharing operand rows in its L2) and the x-th eighth of the fill tiles, so
-  // that every L2 serves GEMM tiles; if an XCD's share would not fit its workgroups,
-  // items are dealt round-robin.
+  // its L2), mostly the runs of odd rounds in reverse XCD order (see below). When all
+  // items fit in one round, XCD x takes the x-th eighth of the GEMM tiles (a
+  // contiguous run: mostly one expert, sharing operand rows in its L2) and the x-th
+  // eighth of the fill tiles, so that every L2 serves GEMM tiles; if an XCD's share
+  // would not fit its workgroups, items are dealt round-robin.
   const int b = blockIdx.x;
   int slot = b;
   if (grid % 8 == 0 && !one_round) {
@@ -1524,8 +1524,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void kg_wgrad_kernel(Params p) {
     const int total = p.G * T;
     for (int base = 0; base < total; base += grid) {
       // odd rounds dealt in reverse (XCD x takes run 7 - x): the items come longest
-      // first, and this evens out the work of the XCDs' and workgroups' shares
-      const int idx = base + (((base / grid) & 1) ? grid - 1 - slot : slot);
+      // first, and this evens out the work of the XCDs' and workgroups' shares. Not in
+      // the fp8-MFMA mode with fp32 scales, whose load-bound long experts gain more
+      // from each XCD keeping its panel position from round to round (measured).
+      constexpr bool kReverse = !(FAST && KIND == F32S);
+      const int idx = base + ((kReverse && ((base / grid) & 1)) ? grid - 1 - slot : slot);
       if (idx >= total) break;
       const Item it = decode_item(idx, T, p.tiles_m, p.tiles_n, s.order);
       const int g = it.g;
