@@ -1311,6 +1311,8 @@ __device__ __forceinline__ void compute_stage(const unsigned char* st, int gran,
                                               int srows, int mlim, int nlim,
                                               v4f (&acc)[CF::NI][CF::NJ],
                                               v4f (&part)[CF::NI][CF::NJ]) {
+  static_assert(!CF::SWZ || (KIND == F32S && !FAST),
+                "swizzled stages: only the precise fp32-scale compute reads them");
   if constexpr (KIND == BF16) {
     compute_bf16<CF>(st, acc);
   } else if constexpr (KIND == F32S32) {
