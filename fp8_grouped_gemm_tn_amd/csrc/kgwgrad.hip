@@ -969,6 +969,12 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
       for (int kk = 0; kk < KK; ++kk) rnext[kk] = rdb(jn + 1, kk);
     }
     v4f x[CF::NI];
+    // K-major 64 x 128 wave tiles: the wave issues a column's MFMAs at raised priority,
+    // so that the SIMD's other wave fills the MFMAs' cycles with its VALU work
+    // (measured 6-7% on long K-major experts; the token-major kernels gained 1-3% or
+    // lost as much depending on the variant, and keep the default priority)
+    constexpr bool kPrio = !DEFER && CF::NT;
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -979,6 +985,7 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
         for (int i = 0; i < CF::NI; ++i) rescale(i, jn - 1, xprev[i]);
       }
     }
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < CF::NI; ++i) {
       if constexpr (PROMOTE) {
