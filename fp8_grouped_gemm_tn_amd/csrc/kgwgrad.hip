@@ -759,10 +759,11 @@ __device__ inline v8bf widen8(v2i x, float scale) {
 // of the transposing read; K-major, its channel row of the wave's first sub-tile
 // plus its first token byte (the K-major offsets below are then immediates). Both
 // layouts give a lane the same tokens, so the MFMAs see the same operands, except in
-// two K-major paths that read whole 16-byte runs instead (the split runs of the
-// token-major order conflicted in the LDS banks): bf16 (compute_bf16) and fp32
-// scales in the fp8-MFMA mode (rdf8n); the MFMA sums those orders with different
-// roundings.
+// the K-major paths that read whole 16-byte runs instead (the split runs of the
+// token-major order conflicted in the LDS banks, also when the compiler merged two
+// steps' reads into one ds_read2_b64): bf16 (compute_bf16) and fp32 scales per 128
+// tokens in both modes (rdf8n; compute_precise_f32s); the MFMA sums those orders with
+// different roundings.
 // fp8, tokens 32kk + 8q .. +7 of sub-tile row (column) i (K-major base: + 8q):
 template <class CF, int ROW>
 __device__ inline v2i rd8(const unsigned char* base, int i, int kk) {
@@ -907,13 +908,19 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
   const int q = lane >> 4, j = lane & 15;
   const int wm = w % CF::WAVES_M, wn = w / CF::WAVES_M;
   const int lrow = 8 * q + (j >> 1);
-  const int lbyte = 8 * q;  // K-major: first token byte
+  const int lbyte = 16 * q;  // K-major: first token byte of the lane's 16-byte runs
   const unsigned char* aBase = CF::NT ? st + CF::nt_row(wm * CF::WM + j) + lbyte
                                       : st + lrow * CF::ROWA + 8 * (j & 1) + wm * CF::WM;
   const unsigned char* bBase = CF::NT ? st + CF::OPA + CF::nt_row(wn * CF::WN + j) + lbyte
                                       : st + CF::OPA + lrow * CF::ROWB + 8 * (j & 1) + wn * CF::WN;
   const float* sSa = (const float*)(st + CF::SA_OFF);
   const float* sSb = (const float*)(st + CF::SB_OFF);
+  // K-major: step kk takes the lane's tokens 64(kk/2) + 16q + 8(kk%2) .. +7, so that
+  // steps 2m and 2m+1 read one 16-byte run per lane
+  auto rdn = [&](const unsigned char* base, int i, int kk) __attribute__((always_inline)) {
+    const v4i r = *(const v4i*)(base + i * CF::NT_SUB + 64 * (kk >> 1));
+    return (kk & 1) ? v2i{r.z, r.w} : v2i{r.x, r.y};
+  };
   // swizzled rows: the lane's rows all have r & 7 = (j >> 1) & 7, so each sub-tile's
   // chunk moves by a fixed XOR; one base per sub-tile row (column), the token offsets
   // stay immediates
@@ -927,12 +934,16 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
   auto rda = [&](int i, int kk) __attribute__((always_inline)) {
     if constexpr (CF::SWZ)
       return tr8(swz_a(i) + 32 * kk * CF::ROWA);
+    else if constexpr (CF::NT)
+      return rdn(aBase, i, kk);
     else
       return rd8<CF, CF::ROWA>(aBase, i, kk);
   };
   auto rdb = [&](int jn, int kk) __attribute__((always_inline)) {
     if constexpr (CF::SWZ)
       return tr8(swz_b(jn) + 32 * kk * CF::ROWB);
+    else if constexpr (CF::NT)
+      return rdn(bBase, jn, kk);
     else
       return rd8<CF, CF::ROWB>(bBase, jn, kk);
   };
