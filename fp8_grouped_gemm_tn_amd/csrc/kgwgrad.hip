@@ -88,9 +88,9 @@ struct Params {
 // each wave reads stage kb+1's fragments into registers before it issues stage kb's
 // MFMAs (bf16 only).
 // SWZ (token-major fp8 only): LDS rows without padding; each row's 16-byte chunks are
-// XOR-permuted by the row's low three bits (logical chunk c of row r sits at c ^ (r & 7)),
-// so that the eight rows one transposing read touches still fall in distinct banks. The
-// LDS the padding took then holds a third stage.
+// XOR-permuted by a key of the row index (logical chunk c of row r sits at
+// c ^ swz_key(r)), so that the rows the transposing reads of a half-wave touch still
+// fall in distinct banks. The LDS the padding took then holds a third stage.
 template <int BM_, int BN_, int WAVES_M_, int TK_, int NS_, int ELT_, int SCALE_BYTES_,
           int THREADS_ = 512, bool PIPE_ = false, bool NT_ = false, bool SWZ_ = false>
 struct Cfg {
@@ -120,6 +120,14 @@ struct Cfg {
   static constexpr int RA = NT ? BM / 2 : TK, RB = NT ? BN / 2 : TK;  // LDS rows per operand
   // K-major: byte offset of channel row r within its operand, and of 16 channels
   static __host__ __device__ constexpr int nt_row(int r) { return (r >> 1) * ROWA + (r & 1) * TK * ELT; }
+  // Swizzled rows (SWZ): LDS chunk ch of row r holds the row's 16-byte chunk
+  // ch ^ swz_key(r). The 16 rows that a half-wave's transposing reads name then fall
+  // in distinct bank groups: a row of 256 bytes spans all 64 banks (key r mod 16),
+  // rows of 128 bytes alternate between the two bank halves (key r / 2 mod 8).
+  // Measured with an LDS probe: the key r mod 8 left these reads 2-way conflicted.
+  static __host__ __device__ constexpr int swz_key(int r, int row_bytes) {
+    return row_bytes >= 256 ? (r & 15) : ((r >> 1) & 7);
+  }
   static constexpr int NT_SUB = 8 * ROWA;
   // A stage is LOADS wave loads of 1 KB: LOADS_A of A rows, LOADS_B of B rows and,
   // with scales, one scale tile per operand. Load k of a stage is issued by wave
@@ -160,8 +168,9 @@ struct Cfg {
   static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile must be whole sub-tile pairs");
   static_assert(RA * CHA % 64 == 0 && RB * CHB % 64 == 0, "stage must be whole wave loads");
   static_assert(!NT || (TK * ELT == 128 && !PIPE), "K-major rows: 128 bytes, plain stages");
-  static_assert(!SWZ || (!NT && !PIPE && ELT == 1 && BM * ELT >= 128 && BN * ELT >= 128),
-                "swizzled rows: token-major fp8, at least 8 chunks per row");
+  static_assert(!SWZ || (!NT && !PIPE && ELT == 1 && (BM * ELT == 128 || BM * ELT == 256) &&
+                          (BN * ELT == 128 || BN * ELT == 256)),
+                "swizzled rows: token-major fp8, rows of 128 or 256 bytes");
   static_assert(EPI_BYTES <= NS * STAGE, "epilogue must fit the stages");
   static_assert(NS >= 2, "at least two stages");
   static_assert(EPI_ROWS * EPI_CPR % THREADS == 0, "epilogue work must split evenly");
@@ -245,12 +254,12 @@ __device__ inline uint32_t load_off(const Params& p, int k, int lane) {
                         : kOobOffset;
   } else if (is_a) {
     const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
-    // swizzled rows: LDS chunk ch of row `row` holds the row's chunk ch ^ (row & 7)
-    const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+    // swizzled rows: LDS chunk ch of row `row` holds the row's chunk ch ^ swz_key(row)
+    const int gch = CF::SWZ ? ch ^ CF::swz_key(row, CF::ROWA) : ch;
     return ch < CF::DCA ? row * (uint32_t)(p.M * CF::ELT) + 16 * gch : kOobOffset;
   } else {
     const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
-    const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+    const int gch = CF::SWZ ? ch ^ CF::swz_key(row, CF::ROWB) : ch;
     return ch < CF::DCB ? row * (uint32_t)(p.N * CF::ELT) + 16 * gch : kOobOffset;
   }
 }
@@ -276,12 +285,12 @@ __device__ inline LoadOffsets<CF> load_offsets(const Params& p) {
     } else if (k < CF::LOADS_A) {
       const int idx = 64 * k + lane;
       const int row = idx / CF::CHA, ch = idx - row * CF::CHA;
-      const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+      const int gch = CF::SWZ ? ch ^ CF::swz_key(row, CF::ROWA) : ch;
       if (ch < CF::DCA) o.off[s] = row * eM + 16 * gch;
     } else if (k < CF::LOADS_A + CF::LOADS_B) {
       const int idx = 64 * (k - CF::LOADS_A) + lane;
       const int row = idx / CF::CHB, ch = idx - row * CF::CHB;
-      const int gch = CF::SWZ ? ch ^ (row & 7) : ch;
+      const int gch = CF::SWZ ? ch ^ CF::swz_key(row, CF::ROWB) : ch;
       if (ch < CF::DCB) o.off[s] = row * eN + 16 * gch;
     }
   }
@@ -921,15 +930,15 @@ __device__ __forceinline__ void compute_precise_f32s(const unsigned char* st, v4
     const v4i r = *(const v4i*)(base + i * CF::NT_SUB + 64 * (kk >> 1));
     return (kk & 1) ? v2i{r.z, r.w} : v2i{r.x, r.y};
   };
-  // swizzled rows: the lane's rows all have r & 7 = (j >> 1) & 7, so each sub-tile's
-  // chunk moves by a fixed XOR; one base per sub-tile row (column), the token offsets
-  // stay immediates
-  const int sw = (j >> 1) & 7;
+  // swizzled rows: the lane's rows lrow + 32 kk all have the key of lrow, so each
+  // sub-tile's chunk moves by a fixed XOR; one base per sub-tile row (column), the
+  // token offsets stay immediates
+  const int swa = CF::swz_key(lrow, CF::ROWA), swb = CF::swz_key(lrow, CF::ROWB);
   auto swz_a = [&](int i) __attribute__((always_inline)) {
-    return st + lrow * CF::ROWA + 16 * (((wm * CF::WM) / 16 + i) ^ sw) + 8 * (j & 1);
+    return st + lrow * CF::ROWA + 16 * (((wm * CF::WM) / 16 + i) ^ swa) + 8 * (j & 1);
   };
   auto swz_b = [&](int jn) __attribute__((always_inline)) {
-    return st + CF::OPA + lrow * CF::ROWB + 16 * (((wn * CF::WN) / 16 + jn) ^ sw) + 8 * (j & 1);
+    return st + CF::OPA + lrow * CF::ROWB + 16 * (((wn * CF::WN) / 16 + jn) ^ swb) + 8 * (j & 1);
   };
   auto rda = [&](int i, int kk) __attribute__((always_inline)) {
     if constexpr (CF::SWZ)
